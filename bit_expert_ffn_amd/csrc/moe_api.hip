@@ -1,0 +1,247 @@
+// C ABI of libmoe_ffn: argument validation, workspace layout and launches.
+// The operations are defined in include/moe_ffn.h with their sources.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe_ffn.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+static thread_local char g_err[512] = "";
+
+static moe_status fail(moe_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Bump {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    }
+};
+
+SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype) {
+    SmallLayout L{};
+    Bump b;
+    const size_t n = (size_t)T * k;
+    L.ids = b.take(n * 4);
+    L.w = b.take(n * 4);
+    L.meta = b.take(sizeof(SmallMeta));
+    L.pair_tok = b.take(n * 4);
+    L.pair_slot = b.take(n * 4);
+    L.pair_exp = b.take(n * 4);
+    L.slot_pair = b.take(n * 4);
+    L.group_first = b.take(n * 4);
+    L.group_n = b.take(n * 4);
+    L.active = b.take(n * 4);
+    L.a_hi = b.take(n * FF * 2);
+    L.a_lo = b.take(n * FF * 2);
+    L.as_hi = b.take((size_t)T * FFs * 2);
+    L.as_lo = b.take((size_t)T * FFs * 2);
+    L.d = b.take(n * H * 4);
+    L.ds = b.take((size_t)T * H * 4);
+    const GemvShape g = gemv_shape(H, FF, FFs, qtype, 0.f);
+    L.tile_cnt = b.take((size_t)g.tiles_dn * 4);
+    L.total = b.off;
+    return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+static moe_status check_expert(const moe_expert_desc* d, const char* what) {
+    if (!d) return fail(MOE_ERR_INVALID_ARG, "%s: descriptor is NULL", what);
+    const int qk = codes_per_block(d->qtype);
+    if (qk == 0) return fail(MOE_ERR_INVALID_ARG, "%s: unknown qtype %d", what, d->qtype);
+    if (d->hidden <= 0 || d->ff <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: hidden and ff must be > 0", what);
+    if (d->hidden % qk || d->ff % qk)
+        return fail(MOE_ERR_INVALID_ARG, "%s: hidden (%d) and ff (%d) must be multiples of %d", what, d->hidden,
+                    d->ff, qk);
+    if (d->act != MOE_ACT_SWIGLU) return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d not supported", what, d->act);
+    if (!isfinite(d->zero_point)) return fail(MOE_ERR_INVALID_ARG, "%s: zero_point is not finite", what);
+    if (d->hidden / qk > kMaxBlocksPerRow || d->ff / qk > kMaxBlocksPerRow)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: more than %d blocks per row", what, kMaxBlocksPerRow);
+    return MOE_OK;
+}
+
+static moe_status check_layer(const moe_layer_desc* d) {
+    if (!d) return fail(MOE_ERR_INVALID_ARG, "layer descriptor is NULL");
+    moe_status s = check_expert(&d->expert, "layer");
+    if (s != MOE_OK) return s;
+    if (d->n_experts < 1 || d->n_experts > kMaxE)
+        return fail(MOE_ERR_UNSUPPORTED, "n_experts %d outside [1, %d]", d->n_experts, kMaxE);
+    if (d->top_k < 1 || d->top_k > d->n_experts)
+        return fail(MOE_ERR_INVALID_ARG, "top_k %d outside [1, n_experts=%d]", d->top_k, d->n_experts);
+    if (d->top_k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "top_k %d above %d", d->top_k, kMaxK);
+    if (d->renormalize != 0 && d->renormalize != 1) return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1");
+    const int qk = codes_per_block(d->expert.qtype);
+    if (d->shared_ff < 0 || d->shared_ff % qk)
+        return fail(MOE_ERR_INVALID_ARG, "shared_ff %d must be >= 0 and a multiple of %d", d->shared_ff, qk);
+    if (d->shared_ff / qk > kMaxBlocksPerRow) return fail(MOE_ERR_UNSUPPORTED, "shared_ff too large");
+    return MOE_OK;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    }
+    return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_expert_blob_bytes(const moe_expert_desc* d) {
+    if (check_expert(d, "blob") != MOE_OK) return 0;
+    const int qk = codes_per_block(d->qtype);
+    return (size_t)3 * ((size_t)d->hidden * d->ff / qk) * kBlockBytes;
+}
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc* d, int32_t T) {
+    if (check_layer(d) != MOE_OK || T < 0) return 0;
+    if (T <= kSmallT)
+        return small_layout(T, d->top_k, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype).total;
+    return large_layout(T, d->top_k, d->n_experts, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype)
+        .total;
+}
+
+size_t moe_expert_workspace_bytes(const moe_expert_desc* d, int32_t T) {
+    if (check_expert(d, "expert") != MOE_OK || T < 0) return 0;
+    if (T <= kSmallT) return small_layout(T, 1, d->hidden, d->ff, 0, d->qtype).total;
+    return large_layout(T, 1, 1, d->hidden, d->ff, 0, d->qtype).total;
+}
+
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize, int32_t* ids,
+                          float* weights, void* stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+    if (E < 1 || E > kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E %d outside [1, %d]", E, kMaxE);
+    if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "k %d outside [1, E=%d]", k, E);
+    if (k > kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k %d above %d", k, kMaxK);
+    if (renormalize != 0 && renormalize != 1) return fail(MOE_ERR_INVALID_ARG, "renormalize must be 0 or 1");
+    if (T == 0) return MOE_OK;
+    if (!logits || !ids || !weights) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4))
+        return fail(MOE_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+    hipError_t e = launch_route_topk(logits, T, E, k, renormalize, ids, weights, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "route launch: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_desc& ed, int FFs,
+                            const void* const* table, const void* single, const void* shared, const void* x,
+                            int x_dtype, const float* logits, float* y, int32_t* ids_out, float* w_out, void* ws,
+                            size_t ws_bytes, hipStream_t s, bool identity) {
+    char* wsb = (char*)ws;
+    if (T <= kSmallT) {
+        const SmallLayout L = small_layout(T, k, ed.hidden, ed.ff, FFs, ed.qtype);
+        if (ws_bytes < L.total)
+            return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+        const GemvShape g = gemv_shape(ed.hidden, ed.ff, FFs, ed.qtype, ed.zero_point);
+        int* ids = ids_out ? ids_out : (int*)(wsb + L.ids);
+        float* w = w_out ? w_out : (float*)(wsb + L.w);
+        hipError_t e = launch_route_bucket_small(logits, T, E, k, renorm, identity ? 1 : 0, ids, w, L, wsb,
+                                                 g.tiles_dn, s);
+        if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "route launch: %s", hipGetErrorString(e));
+        int max_groups = T * k;
+        if (max_groups > E * ((T + kGroup - 1) / kGroup)) max_groups = E * ((T + kGroup - 1) / kGroup);
+        e = launch_gemv_layer(g, table, single, shared, x, x_dtype, T, k, max_groups, ids, w, L, wsb, y, s);
+        if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "GEMV launch: %s", hipGetErrorString(e));
+        return MOE_OK;
+    }
+    return fail(MOE_ERR_UNSUPPORTED, "T = %d above %d: matrix-core path not built", T, kSmallT);
+}
+
+moe_status moe_expert_ffn(const moe_expert_desc* desc, const void* blob, const void* x, int32_t x_dtype, int32_t T,
+                          float* y, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_expert(desc, "moe_expert_ffn");
+    if (st != MOE_OK) return st;
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown x_dtype %d", x_dtype);
+    if (T == 0) return MOE_OK;
+    if (!blob || !x || !y || !ws) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(blob, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256))
+        return fail(MOE_ERR_INVALID_ARG, "blob, x and y must be 16-byte aligned and ws 256-byte aligned");
+    const size_t need = moe_expert_workspace_bytes(desc, T);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    return run_layer(T, 1, 1, 1, *desc, 0, nullptr, blob, nullptr, x, x_dtype, nullptr, y, nullptr, nullptr, ws,
+                     ws_bytes, (hipStream_t)stream, true);
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expert_table, const void* shared_blob,
+                             const void* x, int32_t x_dtype, const float* logits, int32_t T, float* y,
+                             int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_layer(desc);
+    if (st != MOE_OK) return st;
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown x_dtype %d", x_dtype);
+    if ((desc->shared_ff > 0) != (shared_blob != nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "shared_blob must be non-NULL exactly when shared_ff > 0");
+    if (T == 0) return MOE_OK;
+    if (!expert_table || !x || !logits || !y || !ws) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, 256) ||
+        !aligned(expert_table, 8) || (shared_blob && !aligned(shared_blob, 16)) || (ids_out && !aligned(ids_out, 4)) ||
+        (w_out && !aligned(w_out, 4)))
+        return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (x, y, blobs: 16 B; ws: 256 B)");
+    const size_t need = moe_layer_workspace_bytes(desc, T);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    return run_layer(T, desc->n_experts, desc->top_k, desc->renormalize, desc->expert, desc->shared_ff, expert_table,
+                     nullptr, shared_blob, x, x_dtype, logits, y, ids_out, w_out, ws, ws_bytes, (hipStream_t)stream,
+                     false);
+}
+
+moe_status moe_dequant_matrix(const moe_expert_desc* desc, const void* blob, int32_t m, float* out, void* stream) {
+    moe_status st = check_expert(desc, "moe_dequant_matrix");
+    if (st != MOE_OK) return st;
+    if (m < 0 || m > 2) return fail(MOE_ERR_INVALID_ARG, "matrix index %d outside [0, 2]", m);
+    if (!blob || !out) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(blob, 16) || !aligned(out, 4)) return fail(MOE_ERR_INVALID_ARG, "misaligned pointer");
+    const int qk = codes_per_block(desc->qtype);
+    const int H = desc->hidden, FF = desc->ff;
+    const int rows = m == 2 ? H : FF, cols = m == 2 ? FF : H;
+    const size_t mat_bytes = (size_t)FF * (H / qk) * kBlockBytes;   // gate and up are the same size
+    hipError_t e = launch_dequant(blob, desc->qtype, desc->zero_point, rows, cols, (size_t)m * mat_bytes, out,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "dequant launch: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+moe_status moe_validate_table(const void* const* expert_table, int32_t E, void* stream) {
+    if (!expert_table || E < 1) return fail(MOE_ERR_INVALID_ARG, "NULL table or E < 1");
+    void** host = (void**)malloc(sizeof(void*) * (size_t)E);
+    if (!host) return fail(MOE_ERR_DEVICE, "host allocation failed");
+    hipError_t e = hipMemcpyAsync(host, expert_table, sizeof(void*) * (size_t)E, hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) {
+        free(host);
+        return fail(MOE_ERR_DEVICE, "table copy: %s", hipGetErrorString(e));
+    }
+    for (int i = 0; i < E; ++i)
+        if (!host[i]) {
+            free(host);
+            return fail(MOE_ERR_INVALID_ARG, "expert_table[%d] is NULL", i);
+        }
+    free(host);
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+/*
+ * moe_ffn.h -- C ABI of the routed low-bit expert FFN library for MI355X (gfx950).
+ *
+ * One routed mixture-of-experts FFN layer per call: top-k routing over the
+ * router logits, the selected experts' block-quantized gate/up/down weights
+ * dequantized inside the kernels, SwiGLU, and the router-weighted combine plus
+ * an optional shared expert.
+ *
+ * Sources of what is computed (page titles; section names in quotes):
+ *   Krasis white paper, 5.3 "Per-token routed expert execution": route, select
+ *     top-k ids and weights, look experts up in a flat device pointer table,
+ *     run the expert projections, apply the activation, reduce the weighted
+ *     expert outputs.  7.1: the layer output is the router-weighted sum.
+ *   "Strata in the source: one verify window, three workers and a cache that
+ *     learns", "The byte budget, in code": 64 weights per fp16 scale in 16
+ *     bytes of 2-bit codes; gate, up and down per expert.  "The CPU kernels":
+ *     the code bit order.  "The plan: three destinations per expert": a verify
+ *     window's routed ids are de-duplicated so an expert chosen by several
+ *     tokens is read once.
+ *   kairos-engine README, "The MoE forward": top-k over the logits, experts
+ *     processed expert-major over buckets of tokens, shared expert summed with
+ *     the routed ones.  "Prefill and decode are different machines": fused
+ *     dequant GEMV for a few tokens, dequant then matrix-core GEMM for many.
+ *
+ * Conventions for every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     keeps no reference after the call returns and allocates no device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); all
+ *     work is enqueued on it and the call returns without synchronising.
+ *   - Shapes and pointers are checked on the host before anything is enqueued;
+ *     on failure a non-OK status is returned, nothing is launched and
+ *     moe_last_error() describes the problem.  A launch failure returns
+ *     MOE_ERR_DEVICE.  Faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Results are deterministic: the same inputs give bitwise identical outputs
+ *     from run to run (no atomics on any value path).  On the decode/verify path
+ *     (T <= 8) a token's output is also bitwise independent of the other tokens
+ *     in the batch.
+ *   - Calls with distinct workspaces may run concurrently on distinct streams.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, k out of range, ... */
+    MOE_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels cover */
+    MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than the *_workspace_bytes size */
+    MOE_ERR_DEVICE = 4         /* a HIP call or kernel launch failed */
+} moe_status;
+
+/* Block formats.  Every block is 16 bytes of codes followed (in the scales
+ * plane) by one IEEE fp16 scale; weight = scale * (code - zero_point).
+ *   MOE_Q2_64: 64 two-bit codes; code i in byte i/4 at bit 2*(i%4)
+ *              (Strata "The byte budget, in code" and "The CPU kernels").
+ *   MOE_Q4_32: 32 four-bit codes; code i in byte i/2, low nibble for even i. */
+typedef enum { MOE_Q2_64 = 1, MOE_Q4_32 = 2 } moe_qtype;
+
+/* Activation dtypes: fp32, or bfloat16 stored as raw 16-bit words. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Gated activation of an expert: SwiGLU, a = silu(gate x) * (up x). */
+typedef enum { MOE_ACT_SWIGLU = 0 } moe_act;
+
+typedef struct {
+    int32_t hidden;      /* H: model width = input and output length */
+    int32_t ff;          /* FF: expert intermediate width */
+    int32_t qtype;       /* moe_qtype */
+    float zero_point;    /* z: 1.5 (2-bit) / 7.5 (4-bit) in the measured shapes; 1.0 is the Strata mapping */
+    int32_t act;         /* moe_act */
+} moe_expert_desc;
+
+typedef struct {
+    moe_expert_desc expert;  /* shape and format of every routed expert (and of the shared one, but ff) */
+    int32_t n_experts;       /* E */
+    int32_t top_k;           /* k, 1 <= k <= min(E, 32) */
+    int32_t renormalize;     /* 1: softmax over the k selected logits; 0: full softmax over E, read at the selected */
+    int32_t shared_ff;       /* FF of the always-on shared expert; 0 = none */
+} moe_layer_desc;
+
+/*
+ * Expert blob layout (bytes).  gate [FF][H], up [FF][H], down [H][FF], in this
+ * order; each matrix is quantized in blocks along its input dimension and
+ * stored as a codes plane [rows][nblk][16] followed by a scales plane
+ * [rows][nblk] of little-endian fp16.  Total = 3 * H * FF / qk * 18 bytes
+ * (1,382,400 for H=2560, FF=640, 2-bit: "The byte budget, in code").
+ * H and FF must be multiples of qk (64 for MOE_Q2_64, 32 for MOE_Q4_32).
+ * Blobs should be 16-byte aligned; the planes then are too.
+ */
+size_t moe_expert_blob_bytes(const moe_expert_desc* desc);   /* 0 if desc is invalid */
+
+/* Device workspace the calls below need for T tokens (bytes, 256-aligned
+ * sub-buffers).  0 if the descriptor is invalid. */
+size_t moe_expert_workspace_bytes(const moe_expert_desc* desc, int32_t T);
+size_t moe_layer_workspace_bytes(const moe_layer_desc* desc, int32_t T);
+
+/*
+ * Top-k routing (Krasis 5.3; kairos "The MoE forward").
+ *   logits  : [T][E] fp32, row-major.
+ *   ids     : [T][k] int32 out -- the k largest logits of each token in rank
+ *             order: logit descending, expert index ascending on ties
+ *             (-0 and +0 are equal; a NaN logit ranks below every number).
+ *   weights : [T][k] fp32 out -- renormalize=1: exp(l_j - l_0) / sum_{i<k}
+ *             exp(l_i - l_0) (sums to 1); renormalize=0: the full softmax over
+ *             all E logits at the selected experts.  An all -inf selection
+ *             gets equal weights.
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 32), T >= 0 (T = 0 is a no-op).
+ */
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, int32_t renormalize,
+                          int32_t* ids, float* weights, void* stream);
+
+/*
+ * One expert's SwiGLU FFN on T tokens: y[t] = W_down (silu(W_gate x[t]) * (W_up x[t])).
+ *   blob : one expert blob (layout above).
+ *   x    : [T][H] activations, dtype x_dtype (moe_dtype).
+ *   y    : [T][H] fp32 out.
+ *   ws   : device workspace of at least moe_expert_workspace_bytes(desc, T) bytes.
+ * T <= 8 runs the dequant-fused GEMV path; larger T the matrix-core path.
+ */
+moe_status moe_expert_ffn(const moe_expert_desc* desc, const void* blob, const void* x, int32_t x_dtype,
+                          int32_t T, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One routed MoE FFN layer on T tokens.
+ *   expert_table : device array of E device pointers, entry e = expert e's blob
+ *                  (Krasis 5.3: a flat device pointer table lets captured graphs
+ *                  follow changing expert addresses).  Entries are not checked
+ *                  on the hot path; a null entry that gets selected is undefined
+ *                  behaviour (use moe_validate_table to check a table).
+ *   shared_blob  : the shared expert (ff = desc->shared_ff), NULL iff shared_ff == 0.
+ *   x            : [T][H] activations (x_dtype); logits : [T][E] fp32.
+ *   y            : [T][H] fp32 out: y[t] = shared(x[t]) + sum_j w[t][j] * expert_{ids[t][j]}(x[t]),
+ *                  accumulated in that fixed order (shared first, then rank order).
+ *   ids_out, w_out : optional [T][k] copies of the routing (NULL to skip).
+ *   ws           : device workspace of at least moe_layer_workspace_bytes(desc, T) bytes.
+ * T <= 8 (decode, verify windows) runs the GEMV path: routing, expert-major
+ * de-duplicated buckets, dequant-fused gate/up + SwiGLU, down, combine.
+ * Larger T (prefill) sorts token slots by expert and runs grouped matrix-core
+ * GEMMs over ragged per-expert token counts.
+ */
+moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expert_table, const void* shared_blob,
+                             const void* x, int32_t x_dtype, const float* logits, int32_t T, float* y,
+                             int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Debug: dequantize matrix m (0 gate [FF][H], 1 up [FF][H], 2 down [H][FF]) of
+ * a blob to fp32 (exact: an fp16 scale times a small integer offset), row-major.
+ */
+moe_status moe_dequant_matrix(const moe_expert_desc* desc, const void* blob, int32_t m, float* out, void* stream);
+
+/*
+ * Debug: copy the device table to the host and check that its first E entries
+ * are non-null.  Synchronises `stream`.  Returns MOE_ERR_INVALID_ARG naming the
+ * first null entry.
+ */
+moe_status moe_validate_table(const void* const* expert_table, int32_t E, void* stream);
+
+const char* moe_status_str(moe_status s);
+/* Detail of the last non-OK status returned on the calling thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle on the
+same seeded inputs.  Expert ids must match exactly, routing weights within
+1e-6, layer outputs within max|err| <= 2e-3 * rms(oracle output)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_expert_ffn_amd as moe
+import oracle
+import synth
+from helpers import f16_bits_array, max_err_over_rms, random_expert
+from synth import workloads as wl
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+DEV = "cuda"
+
+
+def _bf16_tensor(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _x_tensor(x):
+    return _bf16_tensor(x) if x.dtype == np.uint16 else torch.from_numpy(x).to(DEV)
+
+
+# --- routing ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k", [(1, 512, 10), (8, 512, 10), (5, 128, 8), (64, 256, 8), (3, 8, 2), (2, 1024, 32),
+                                   (4, 64, 64 // 2), (7, 33, 33 // 2), (1, 1, 1), (3, 16, 16)])
+def test_route_topk_matches_oracle(T, E, k):
+    rng = np.random.default_rng(T * 1000 + E)
+    l = rng.integers(-3, 4, size=(T, E)).astype(np.float32) * np.float32(0.5)   # many ties
+    l[0] = rng.normal(size=E).astype(np.float32)
+    for renorm in (True, False):
+        ids_ref, w_ref = oracle.route_topk(l, k, renorm)
+        ids, w = moe.route_topk(torch.from_numpy(l).to(DEV), k, renorm)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6
+
+
+def test_route_topk_special_values():
+    l = np.array([[-0.0, 0.0, -1.0, np.nan, -np.inf, 2.0],
+                  [np.nan, np.nan, -np.inf, -np.inf, np.nan, -np.inf],
+                  [0.0, -0.0, 0.0, -0.0, 0.0, -0.0],
+                  [-np.inf] * 6], dtype=np.float32)
+    for k in (1, 3, 6):
+        ids_ref, w_ref = oracle.route_topk(l, k)
+        ids, w = moe.route_topk(torch.from_numpy(l).to(DEV), k)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+        wg = w.cpu().numpy()
+        finite = np.isfinite(w_ref)
+        assert np.array_equal(np.isfinite(wg), finite)
+        assert np.max(np.abs(wg[finite] - w_ref[finite])) <= 1e-6
+
+
+def test_route_topk_zipf_logits():
+    for s, E, k in [(1.0, 512, 10), (0.8, 128, 8), (0.6, 256, 8)]:
+        l = synth.logits(0, 3, 0, 300, E, s)
+        ids_ref, w_ref = oracle.route_topk(l, k)
+        ids, w = moe.route_topk(torch.from_numpy(l).to(DEV), k)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6
+
+
+# --- block decoding ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("qtype,H,FF", [(1, 256, 128), (2, 96, 64), (1, 2560, 640)])
+def test_dequant_matches_oracle_exactly(qtype, H, FF):
+    z = 1.5 if qtype == 1 else 7.5
+    blob = synth.expert_blob(5, 0, 1, 64 if qtype == 1 else 32, H, FF, 0.05)
+    # plant special scales: zero, the smallest subnormal, a mid subnormal, the largest finite
+    nb = FF * (H // (64 if qtype == 1 else 32))
+    sc = blob[nb * 16: nb * 18].view('<u2')
+    sc[:4] = [0x0000, 0x0001, 0x0155, 0x7BFF]
+    d = moe.expert_desc(H, FF, qtype, z)
+    dev = torch.from_numpy(blob).to(DEV)
+    for m in range(3):
+        got = moe.dequant_matrix(d, dev, m).cpu().numpy().astype(np.float64)
+        np.testing.assert_array_equal(got, oracle.dequant_matrix(blob, qtype, z, H, FF, m))
+
+
+# --- one expert --------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("qtype,H,FF", [(1, 256, 128), (2, 256, 128), (1, 2560, 640), (2, 2816, 704),
+                                        (2, 2816, 2112), (1, 192, 320), (2, 7168, 2048)])
+@pytest.mark.parametrize("T", [1, 2, 3, 8])
+@pytest.mark.parametrize("xd", ["bf16", "f32"])
+def test_expert_ffn_matches_oracle(qtype, H, FF, T, xd):
+    z = 1.5 if qtype == 1 else 7.5
+    qk = 64 if qtype == 1 else 32
+    blob = synth.expert_blob(7, 1, T, qk, H, FF, 0.05 if qtype == 1 else 0.02)
+    x = synth.activations(7, 1, T, T, H, xd)
+    d = moe.expert_desc(H, FF, qtype, z)
+    y = moe.expert_ffn(d, torch.from_numpy(blob).to(DEV), _x_tensor(x)).cpu().numpy()
+    ref = oracle.expert_ffn(blob, qtype, z, H, FF, x)
+    assert max_err_over_rms(y, ref) <= TOL
+
+
+def test_expert_ffn_page_mapping_z1():
+    """The Strata page's own code mapping (z = 1) and a one-hot closed form."""
+    rng = np.random.default_rng(2)
+    H, FF = 128, 64
+    blob, _, _ = random_expert(rng, 1, H, FF, 0.05)
+    x = rng.normal(size=(2, H)).astype(np.float32)
+    d = moe.expert_desc(H, FF, 1, 1.0)
+    y = moe.expert_ffn(d, torch.from_numpy(blob).to(DEV), torch.from_numpy(x).to(DEV)).cpu().numpy()
+    assert max_err_over_rms(y, oracle.expert_ffn(blob, 1, 1.0, H, FF, x)) <= TOL
+
+
+# --- layers ------------------------------------------------------------------------------------
+
+def _layer_parity(w, layers, steps, tokens=None, arena=None):
+    arena = arena or wl.DeviceArena(w, device=DEV, layers=layers)
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k, shared_ff=w.shared_ff)
+    T = w.tokens if tokens is None else tokens
+    for l in layers:
+        host_blobs = None
+        for step in steps:
+            x, logits = wl.device_inputs(w, l, step, device=DEV, tokens=T)
+            ids = torch.empty((T, w.top_k), dtype=torch.int32, device=DEV)
+            wt = torch.empty((T, w.top_k), dtype=torch.float32, device=DEV)
+            y = moe.layer_forward(desc, arena.tables[l], x, logits, shared=arena.shared_blob(l), ids=ids,
+                                  weights=wt)
+            hx, hl = wl.host_inputs(w, l, step, tokens=T)
+            ids_ref, w_ref = oracle.route_topk(hl, w.top_k)
+            np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+            assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
+            needed = sorted(set(ids_ref.reshape(-1).tolist()))
+            if host_blobs is None:
+                host_blobs = {}
+            for e in needed:
+                if e not in host_blobs:
+                    host_blobs[e] = synth.expert_blob(w.seed, l, e, w.qk, w.hidden, w.ff, w.sigma)
+            # experts never selected are never read: an all-zero stand-in keeps the oracle's table complete
+            zero = np.zeros(w.blob_bytes, dtype=np.uint8)
+            table = [host_blobs.get(e, zero) for e in range(w.experts)]
+            y_ref, ids2, _ = oracle.layer_forward(table, w.top_k, w.qtype, w.zero_point, w.hidden, w.ff, hx, hl,
+                                                  shared=wl.host_shared_blob(w, l), shared_ff=w.shared_ff)
+            np.testing.assert_array_equal(ids2, ids_ref)
+            err = max_err_over_rms(y.cpu().numpy(), y_ref)
+            assert err <= TOL, f"{w.name} layer {l} step {step}: max|err|/rms {err:.3e}"
+    return arena
+
+
+def test_layer_tiny():
+    _layer_parity(wl.WORKLOADS["tiny"], [0], [0, 1, 2])
+
+
+def test_layer_strata_decode_two_layers():
+    _layer_parity(wl.WORKLOADS["strata_decode"], [0, 47], [0, 1])
+
+
+def test_layer_gemma_decode_two_layers():
+    _layer_parity(wl.WORKLOADS["gemma_decode"], [0, 29], [0, 1])
+
+
+@pytest.mark.parametrize("name", ["verify_t4", "verify_t8"])
+def test_layer_verify_windows(name):
+    _layer_parity(wl.WORKLOADS[name], [3], [0, 1])
+
+
+@pytest.mark.parametrize("T", [2, 3, 5, 6, 7])
+def test_layer_ragged_windows(T):
+    _layer_parity(wl.WORKLOADS["verify_t8"], [1], [4], tokens=T)
+
+
+# --- invariants of the GEMV path ----------------------------------------------------------------
+
+def test_batch_invariance_and_determinism():
+    """Token t's output is bitwise the same alone (T=1) and inside a window of 8,
+    and identical from run to run."""
+    w = wl.WORKLOADS["verify_t8"]
+    arena = wl.DeviceArena(w, device=DEV, layers=[2])
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k)
+    x, logits = wl.device_inputs(w, 2, 0, device=DEV)
+    y8 = moe.layer_forward(desc, arena.tables[2], x, logits)
+    y8b = moe.layer_forward(desc, arena.tables[2], x, logits)
+    assert torch.equal(y8, y8b)
+    for t in range(8):
+        y1 = moe.layer_forward(desc, arena.tables[2], x[t:t + 1].contiguous(), logits[t:t + 1].contiguous())
+        assert torch.equal(y1[0], y8[t]), f"token {t} differs between T=1 and T=8"
+    for T in (2, 3, 4, 5):
+        yT = moe.layer_forward(desc, arena.tables[2], x[:T].contiguous(), logits[:T].contiguous())
+        assert torch.equal(yT, y8[:T])
+
+
+def test_identical_experts_ignore_routing():
+    w = wl.WORKLOADS["strata_decode"]
+    blob = torch.from_numpy(synth.expert_blob(0, 0, 0, w.qk, w.hidden, w.ff, w.sigma)).to(DEV)
+    table = torch.full((w.experts,), blob.data_ptr(), dtype=torch.int64, device=DEV)
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k)
+    ed = moe.expert_desc(w.hidden, w.ff, w.qtype, w.zero_point)
+    x, logits = wl.device_inputs(w, 0, 0, device=DEV, tokens=4)
+    y_one = moe.expert_ffn(ed, blob, x).cpu().numpy()
+    for s in range(3):
+        lg = torch.randn((4, w.experts), device=DEV, generator=torch.Generator(device=DEV).manual_seed(s))
+        y = moe.layer_forward(desc, table, x, lg).cpu().numpy()
+        assert max_err_over_rms(y, y_one) <= 1e-5
+
+
+def test_permutation_equivariance():
+    w = wl.WORKLOADS["strata_decode"]
+    arena = wl.DeviceArena(w, device=DEV, layers=[1])
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k)
+    x, logits = wl.device_inputs(w, 1, 0, device=DEV)
+    ids = torch.empty((1, w.top_k), dtype=torch.int32, device=DEV)
+    y = moe.layer_forward(desc, arena.tables[1], x, logits, ids=ids)
+    perm = torch.randperm(w.experts, generator=torch.Generator().manual_seed(0)).to(DEV)
+    ids2 = torch.empty_like(ids)
+    y2 = moe.layer_forward(desc, arena.tables[1][perm].contiguous(), x, logits[:, perm].contiguous(), ids=ids2)
+    assert torch.equal(perm[ids2.long()].int(), ids)
+    assert torch.equal(y, y2)
+
+
+def test_doubling_down_scales_doubles_output():
+    w = wl.WORKLOADS["gemma_decode"]
+    H, FF = w.hidden, w.ff
+    blob = synth.expert_blob(0, 0, 3, w.qk, H, FF, w.sigma)
+    off = 2 * FF * (H // 32) * 18 + H * (FF // 32) * 16
+    b2 = blob.copy()
+    sc = b2[off: off + 2 * H * (FF // 32)].view('<u2')
+    e = (sc >> 10) & 31
+    sc[:] = np.where(e == 0, (sc & 0x8000) | ((sc & 0x3FF) << 1), sc + 0x400)
+    d = moe.expert_desc(H, FF, w.qtype, w.zero_point)
+    x, _ = wl.device_inputs(w, 0, 0, device=DEV, tokens=3)
+    y1 = moe.expert_ffn(d, torch.from_numpy(blob).to(DEV), x)
+    y2 = moe.expert_ffn(d, torch.from_numpy(b2).to(DEV), x)
+    assert torch.equal(y2, 2 * y1)
+
+
+def test_k_equals_e_and_single_expert():
+    rng = np.random.default_rng(8)
+    H, FF, E = 128, 64, 4
+    blobs = [random_expert(rng, 2, H, FF, 0.02)[0] for _ in range(E)]
+    dev = [torch.from_numpy(b).to(DEV) for b in blobs]
+    table = torch.tensor([t.data_ptr() for t in dev], dtype=torch.int64, device=DEV)
+    x = rng.normal(size=(3, H)).astype(np.float32)
+    for k in (1, E):
+        logits = rng.normal(size=(3, E)).astype(np.float32)
+        desc = moe.layer_desc(H, FF, 2, 7.5, E, k)
+        y = moe.layer_forward(desc, table, torch.from_numpy(x).to(DEV), torch.from_numpy(logits).to(DEV))
+        y_ref, _, _ = oracle.layer_forward(blobs, k, 2, 7.5, H, FF, x, logits)
+        assert max_err_over_rms(y.cpu().numpy(), y_ref) <= TOL
+    desc = moe.layer_desc(H, FF, 2, 7.5, 1, 1)
+    y = moe.layer_forward(desc, table[:1].contiguous(), torch.from_numpy(x).to(DEV),
+                          torch.zeros((3, 1), device=DEV))
+    assert max_err_over_rms(y.cpu().numpy(), oracle.expert_ffn(blobs[0], 2, 7.5, H, FF, x)) <= TOL
