@@ -1,0 +1,231 @@
+"""Benchmark of the routed low-bit expert FFN hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: for every layer of the
+workload, routing + bucketing, dequant-fused gate/up + SwiGLU, down and the
+weighted combine, layer after layer on one stream (no cross-layer lookahead:
+layer l+1's call is enqueued after layer l's and reads its own fresh inputs).
+All experts of all layers are resident in HBM and every step's activations and
+logits are generated and uploaded before the timed region.  The timed region
+replays a HIP graph holding the K steps.
+
+Prints one JSON line (rank 0).  Default workload: the 48-layer x 512-expert
+2-bit decode stack, one token per step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE decode tokens/s (expert stack) + achieved HBM GB/s as % of 8 TB/s"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_per_layer(w, ids_np):
+    """Bytes the method must move for one layer call: each distinct selected
+    expert's blob once, the shared expert, activations in, logits in, fp32
+    outputs out."""
+    uniq = len(np.unique(ids_np))
+    return (uniq * w.blob_bytes + w.shared_blob_bytes + w.tokens * w.hidden * (2 if w.x_dtype == "bf16" else 4)
+            + w.tokens * w.experts * 4 + w.tokens * w.hidden * 4), uniq
+
+
+def cpu_baseline(w, x_host, l_host, budget_s=12.0):
+    """The float64 oracle, single-threaded, on a bounded sample: whole decode
+    steps (all layers, all tokens of the step) until the budget is spent."""
+    import oracle
+    import synth
+    from synth import workloads as wl
+    t_total = 0.0
+    steps = 0
+    ref = None
+    while t_total < budget_s:
+        for l in range(w.layers):
+            ids_ref, _ = oracle.route_topk(l_host[steps][l], w.top_k)
+            need = sorted(set(ids_ref.reshape(-1).tolist()))
+            zero = np.zeros(w.blob_bytes, dtype=np.uint8)
+            blobs = {e: synth.expert_blob(w.seed, l, e, w.qk, w.hidden, w.ff, w.sigma) for e in need}
+            table = [blobs.get(e, zero) for e in range(w.experts)]
+            shared = wl.host_shared_blob(w, l)
+            t0 = time.perf_counter()
+            y, _, _ = oracle.layer_forward(table, w.top_k, w.qtype, w.zero_point, w.hidden, w.ff,
+                                           x_host[steps][l], l_host[steps][l], shared=shared, shared_ff=w.shared_ff)
+            t_total += time.perf_counter() - t0
+            if steps == 0 and l == w.layers - 1:
+                ref = y
+        steps += 1
+        if steps >= len(x_host):
+            break
+    tok = steps * w.tokens
+    return {"value": tok / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full step(s) x {w.layers} layers x {w.tokens} token(s) of the same workload, "
+                      f"float64 oracle single-threaded, {t_total:.1f} s"}, ref
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="strata_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism is a design note "
+              "only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_expert_ffn_amd as moe
+    from synth import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    if w.tokens > 8:
+        raise SystemExit("prefill workloads are measured by bench_prefill (matrix-core path)")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+    nsteps = K + W
+
+    t0 = time.time()
+    arena = wl.DeviceArena(w, device=dev, progress=lambda l: log(f"arena layer {l + 1}/{w.layers}")
+                           if (l + 1) % 12 == 0 else None)
+    log(f"arena ready: {w.layers} x {w.experts} x {w.blob_bytes} B in {time.time() - t0:.1f} s")
+
+    # Fresh activations and logits for every (step, layer), resident before timing.
+    x_host, l_host = [], []
+    xs = torch.empty((nsteps, w.layers, w.tokens, w.hidden),
+                     dtype=torch.bfloat16 if w.x_dtype == "bf16" else torch.float32, device=dev)
+    lg = torch.empty((nsteps, w.layers, w.tokens, w.experts), dtype=torch.float32, device=dev)
+    for s in range(nsteps):
+        xr, lr = [], []
+        for l in range(w.layers):
+            xh, lh = wl.host_inputs(w, l, s)
+            xr.append(xh)
+            lr.append(lh)
+            xs[s, l].copy_(torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16) if w.x_dtype == "bf16"
+                           else torch.from_numpy(xh))
+            lg[s, l].copy_(torch.from_numpy(lh))
+        x_host.append(xr)
+        l_host.append(lr)
+
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k, shared_ff=w.shared_ff)
+    ws = moe.workspace(moe.layer_workspace_bytes(desc, w.tokens), dev)
+    y = torch.empty((nsteps, w.layers, w.tokens, w.hidden), dtype=torch.float32, device=dev)
+    ids = torch.empty((nsteps, w.layers, w.tokens, w.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((nsteps, w.layers, w.tokens, w.top_k), dtype=torch.float32, device=dev)
+
+    def run_steps(s0, s1, stream):
+        for s in range(s0, s1):
+            for l in range(w.layers):
+                moe.layer_forward(desc, arena.tables[l], xs[s, l], lg[s, l], shared=arena.shared_blob(l),
+                                  y=y[s, l], ids=ids[s, l], weights=wts[s, l], ws=ws, stream=stream)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    if args.no_graph:
+        def replay_warm():
+            run_steps(0, W, stream)
+
+        def replay_timed():
+            run_steps(W, nsteps, stream)
+    else:
+        g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            # one eager pass first (library initialisation outside capture)
+            run_steps(0, 1, stream)
+            stream.synchronize()
+            with torch.cuda.graph(g_warm, stream=stream):
+                run_steps(0, W, stream)
+            with torch.cuda.graph(g_timed, stream=stream):
+                run_steps(W, nsteps, stream)
+
+        def replay_warm():
+            with torch.cuda.stream(stream):
+                g_warm.replay()
+
+        def replay_timed():
+            with torch.cuda.stream(stream):
+                g_timed.replay()
+
+    replay_warm()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    replay_timed()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / K
+    tok_s = K * w.tokens / (ms_total / 1e3)
+
+    # Algorithmic bytes of the timed steps, from the routing the GPU produced.
+    ids_np = ids.cpu().numpy()
+    bytes_steps, uniq_tot = 0, 0
+    for s in range(W, nsteps):
+        for l in range(w.layers):
+            b, u = algorithmic_bytes_per_layer(w, ids_np[s, l])
+            bytes_steps += b
+            uniq_tot += u
+    gbps = bytes_steps / (ms_total / 1e3) / 1e9
+
+    # Per-layer-call duration, measured live with HIP events on the launch stream
+    # (eager launches, one event pair per layer call).
+    n_ev = min(w.layers, 48)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    durs = []
+    for rep in range(3):
+        s = W + (rep % K)
+        with torch.cuda.stream(stream):
+            for l in range(n_ev):
+                evs[l][0].record(stream)
+                moe.layer_forward(desc, arena.tables[l], xs[s, l], lg[s, l], shared=arena.shared_blob(l),
+                                  y=y[s, l], ids=ids[s, l], weights=wts[s, l], ws=ws, stream=stream)
+                evs[l][1].record(stream)
+        torch.cuda.synchronize()
+        durs += [a.elapsed_time(b) for a, b in evs]
+    layer_ms = float(np.mean(durs))
+    bytes_layer = bytes_steps / (K * w.layers)
+    achieved = bytes_layer / (layer_ms / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "experts": w.experts, "hidden": w.hidden, "ff": w.ff,
+                   "top_k": w.top_k, "tokens_per_step": w.tokens,
+                   "format": "2-bit/64 + fp16 scale" if w.qtype == 1 else "4-bit/32 + fp16 scale",
+                   "shared_ff": w.shared_ff, "graph": not args.no_graph},
+        "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": int(bytes_steps / K), "distinct_experts_per_layer": round(uniq_tot / (K * w.layers), 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "moe_layer_forward (one layer call)", "launch_ms": round(layer_ms, 5)},
+        "wall_s": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        base, ref = cpu_baseline(w, x_host, l_host)
+        result["cpu_baseline"] = base
+        got = y[0, w.layers - 1].cpu().numpy()
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        result["parity_max_err_over_rms"] = float(np.max(np.abs(got - ref)) / rms)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

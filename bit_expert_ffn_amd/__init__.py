@@ -105,6 +105,11 @@ def expert_workspace_bytes(desc, T):
     return int(lib().moe_expert_workspace_bytes(ctypes.byref(desc), T))
 
 
+def workspace(nbytes, device):
+    """A workspace buffer: zeroed once, as the library requires of its first 256 bytes."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -147,7 +152,7 @@ def expert_ffn(desc, blob, x, y=None, ws=None, stream=None):
         y = torch.empty((T, desc.hidden), dtype=torch.float32, device=x.device)
     need = expert_workspace_bytes(desc, T)
     if ws is None:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+        ws = workspace(need, x.device)
     _check(lib().moe_expert_ffn(ctypes.byref(desc), _ptr(blob), _ptr(x), _xdtype(x), T, _ptr(y), _ptr(ws),
                                 ws.numel(), _stream(stream)))
     return y
@@ -160,7 +165,7 @@ def layer_forward(desc, table, x, logits, shared=None, y=None, ids=None, weights
     if y is None:
         y = torch.empty((T, desc.expert.hidden), dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = torch.empty(max(layer_workspace_bytes(desc, T), 256), dtype=torch.uint8, device=x.device)
+        ws = workspace(layer_workspace_bytes(desc, T), x.device)
     _check(lib().moe_layer_forward(ctypes.byref(desc), _ptr(table), _ptr(shared), _ptr(x), _xdtype(x),
                                    _ptr(logits), T, _ptr(y), _ptr(ids), _ptr(weights), _ptr(ws), ws.numel(),
                                    _stream(stream)))

@@ -31,28 +31,15 @@ struct Bump {
     }
 };
 
-SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype) {
+SmallLayout small_layout(int T, int k, int FF, int FFs) {
     SmallLayout L{};
     Bump b;
     const size_t n = (size_t)T * k;
+    L.sync = b.take(decode_sync_bytes(T * k + T));
     L.ids = b.take(n * 4);
     L.w = b.take(n * 4);
-    L.meta = b.take(sizeof(SmallMeta));
-    L.pair_tok = b.take(n * 4);
-    L.pair_slot = b.take(n * 4);
-    L.pair_exp = b.take(n * 4);
-    L.slot_pair = b.take(n * 4);
-    L.group_first = b.take(n * 4);
-    L.group_n = b.take(n * 4);
-    L.active = b.take(n * 4);
-    L.a_hi = b.take(n * FF * 2);
-    L.a_lo = b.take(n * FF * 2);
-    L.as_hi = b.take((size_t)T * FFs * 2);
-    L.as_lo = b.take((size_t)T * FFs * 2);
-    L.d = b.take(n * H * 4);
-    L.ds = b.take((size_t)T * H * 4);
-    const GemvShape g = gemv_shape(H, FF, FFs, qtype, 0.f);
-    L.tile_cnt = b.take((size_t)g.tiles_dn * 4);
+    L.a = b.take(n * FF * 4);
+    L.as = b.take((size_t)T * FFs * 4);
     L.total = b.off;
     return L;
 }
@@ -119,14 +106,14 @@ size_t moe_expert_blob_bytes(const moe_expert_desc* d) {
 size_t moe_layer_workspace_bytes(const moe_layer_desc* d, int32_t T) {
     if (check_layer(d) != MOE_OK || T < 0) return 0;
     if (T <= kSmallT)
-        return small_layout(T, d->top_k, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype).total;
+        return small_layout(T, d->top_k, d->expert.ff, d->shared_ff).total;
     return large_layout(T, d->top_k, d->n_experts, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype)
         .total;
 }
 
 size_t moe_expert_workspace_bytes(const moe_expert_desc* d, int32_t T) {
     if (check_expert(d, "expert") != MOE_OK || T < 0) return 0;
-    if (T <= kSmallT) return small_layout(T, 1, d->hidden, d->ff, 0, d->qtype).total;
+    if (T <= kSmallT) return small_layout(T, 1, d->ff, 0).total;
     return large_layout(T, 1, 1, d->hidden, d->ff, 0, d->qtype).total;
 }
 
@@ -152,19 +139,15 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
                             size_t ws_bytes, hipStream_t s, bool identity) {
     char* wsb = (char*)ws;
     if (T <= kSmallT) {
-        const SmallLayout L = small_layout(T, k, ed.hidden, ed.ff, FFs, ed.qtype);
+        const SmallLayout L = small_layout(T, k, ed.ff, FFs);
         if (ws_bytes < L.total)
             return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
-        const GemvShape g = gemv_shape(ed.hidden, ed.ff, FFs, ed.qtype, ed.zero_point);
-        int* ids = ids_out ? ids_out : (int*)(wsb + L.ids);
-        float* w = w_out ? w_out : (float*)(wsb + L.w);
-        hipError_t e = launch_route_bucket_small(logits, T, E, k, renorm, identity ? 1 : 0, ids, w, L, wsb,
-                                                 g.tiles_dn, s);
-        if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "route launch: %s", hipGetErrorString(e));
-        int max_groups = T * k;
-        if (max_groups > E * ((T + kGroup - 1) / kGroup)) max_groups = E * ((T + kGroup - 1) / kGroup);
-        e = launch_gemv_layer(g, table, single, shared, x, x_dtype, T, k, max_groups, ids, w, L, wsb, y, s);
-        if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "GEMV launch: %s", hipGetErrorString(e));
+        const GemvShape g = gemv_shape(ed.hidden, ed.ff, FFs, ed.qtype, ed.zero_point, T, k);
+        if (g.lds_bytes > 128 * 1024)
+            return fail(MOE_ERR_UNSUPPORTED, "decode tile needs %zu bytes of LDS", g.lds_bytes);
+        hipError_t e = launch_decode_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm,
+                                           identity ? 1 : 0, ids_out, w_out, L, wsb, y, s);
+        if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
         return MOE_OK;
     }
     return fail(MOE_ERR_UNSUPPORTED, "T = %d above %d: matrix-core path not built", T, kSmallT);

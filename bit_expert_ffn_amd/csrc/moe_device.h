@@ -1,0 +1,220 @@
+// Device helpers shared by the HIP kernels of libmoe_ffn: orderable routing
+// keys, DPP wavefront reductions and the one-wave top-k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Routing order (Krasis white paper 5.3: the k highest-scoring experts; ties
+// toward the lower index).  A 32-bit key orders floats like `>` with
+// -0 == +0; NaN maps to 1, below every number (-inf maps to 0x007FFFFF), and 0
+// marks an empty or already-selected slot.
+__device__ __forceinline__ uint32_t order_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (f != f) return 1u;
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_order_bits(uint32_t k) {
+    if (k <= 1u) return __uint_as_float(0x7FC00000u);
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    const uint32_t o = dpp_u32<CTRL>(v);
+    return o > v ? o : v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) {
+    const uint32_t o = dpp_u32<CTRL>(v);
+    return o < v ? o : v;
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Maximum / minimum over the 64 lanes of a wave (every lane active); uniform
+// result.  Four DPP steps give each row of 16 lanes its extremum; the four
+// rows combine on the scalar unit.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max_u32<kDppXor1>(v);
+    v = dpp_max_u32<kDppXor2>(v);
+    v = dpp_max_u32<kDppHalfMirror>(v);
+    v = dpp_max_u32<kDppMirror>(v);
+    const uint32_t a = max(readlane_u32(v, 0), readlane_u32(v, 16));
+    const uint32_t b = max(readlane_u32(v, 32), readlane_u32(v, 48));
+    return max(a, b);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = dpp_min_u32<kDppXor1>(v);
+    v = dpp_min_u32<kDppXor2>(v);
+    v = dpp_min_u32<kDppHalfMirror>(v);
+    v = dpp_min_u32<kDppMirror>(v);
+    const uint32_t a = min(readlane_u32(v, 0), readlane_u32(v, 16));
+    const uint32_t b = min(readlane_u32(v, 32), readlane_u32(v, 48));
+    return min(a, b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_f32(float v) {
+    return v + __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// Sum over the 64 lanes of a wave in a fixed order (deterministic); uniform result.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v = dpp_add_f32<kDppXor1>(v);
+    v = dpp_add_f32<kDppXor2>(v);
+    v = dpp_add_f32<kDppHalfMirror>(v);
+    v = dpp_add_f32<kDppMirror>(v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Sum over aligned groups of 8 lanes (every lane active); each lane gets its group's sum.
+__device__ __forceinline__ float group8_sum_f32(float v) {
+    v = dpp_add_f32<kDppXor1>(v);
+    v = dpp_add_f32<kDppXor2>(v);
+    v = dpp_add_f32<kDppHalfMirror>(v);
+    return v;
+}
+
+// One wave: top-k of one token's E <= 64 * KPL logits (every lane active).
+// Lane l holds logits l, l + 64, ... (KPL slots) and first sorts them by
+// (key descending, index ascending) with a sorting network.  Each round takes the wave maximum of the lanes' heads; the owner
+// is the single lane holding it, or on an exact tie the one whose head has the
+// lowest expert index; the owner then shifts its list by one.  Lane j < k
+// returns the j-th selected expert and its routing weight: softmax over the k
+// selected logits (renorm) or the full softmax over E read at the selected
+// experts; an all -inf selection gets equal weights.
+// Batcher odd-even merge sort networks (compare-exchange index pairs) for
+// 2, 4, 8 and 16 keys, listed as constants so every index is static.
+template <int KPL> struct SortNet;
+template <> struct SortNet<2> {
+    static constexpr int N = 1;
+    static constexpr int P[1][2] = {{0, 1}};
+};
+template <> struct SortNet<4> {
+    static constexpr int N = 5;
+    static constexpr int P[5][2] = {{0, 1}, {2, 3}, {0, 2}, {1, 3}, {1, 2}};
+};
+template <> struct SortNet<8> {
+    static constexpr int N = 19;
+    static constexpr int P[19][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {0, 2}, {1, 3}, {4, 6}, {5, 7}, {1, 2}, {5, 6}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {2, 4}, {3, 5}, {1, 2}, {3, 4}, {5, 6}};
+};
+template <> struct SortNet<16> {
+    static constexpr int N = 63;
+    static constexpr int P[63][2] = {{0, 1}, {2, 3}, {4, 5}, {6, 7}, {8, 9}, {10, 11}, {12, 13}, {14, 15}, {0, 2}, {1, 3}, {4, 6}, {5, 7}, {8, 10}, {9, 11}, {12, 14}, {13, 15}, {1, 2}, {5, 6}, {9, 10}, {13, 14}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {8, 12}, {9, 13}, {10, 14}, {11, 15}, {2, 4}, {3, 5}, {10, 12}, {11, 13}, {1, 2}, {3, 4}, {5, 6}, {9, 10}, {11, 12}, {13, 14}, {0, 8}, {1, 9}, {2, 10}, {3, 11}, {4, 12}, {5, 13}, {6, 14}, {7, 15}, {4, 8}, {5, 9}, {6, 10}, {7, 11}, {2, 4}, {3, 5}, {6, 8}, {7, 9}, {10, 12}, {11, 13}, {1, 2}, {3, 4}, {5, 6}, {7, 8}, {9, 10}, {11, 12}, {13, 14}};
+};
+
+// Sort a lane's packed keys descending: key64 = order_bits(logit) << 32 | ~index,
+// so that a larger key64 ranks first (higher logit, then lower index).  Each
+// compare-exchange is one 64-bit compare and two selects, with no branches.
+template <int KPL>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[KPL]) {
+#pragma unroll
+    for (int c = 0; c < SortNet<KPL>::N; ++c) {
+        const int i = SortNet<KPL>::P[c][0], j = SortNet<KPL>::P[c][1];
+        const uint64_t a = key[i], b = key[j];
+        const bool sw = b > a;
+        key[i] = sw ? b : a;
+        key[j] = sw ? a : b;
+    }
+}
+
+template <int KPL>
+__device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int E, int k, int renorm, int lane,
+                                              int* out_id, float* out_w) {
+    uint64_t key[KPL];
+    float lv[KPL];
+    // Every load is unconditional (clamped address) so that all of them are in
+    // flight together; out-of-range slots are masked afterwards, branch-free.
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int e = lane + 64 * i;
+        lv[i] = row[e < E ? e : E - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const uint32_t e = (uint32_t)(lane + 64 * i);
+        const uint64_t valid = 0ull - (uint64_t)(e < (uint32_t)E);
+        key[i] = (((uint64_t)order_bits(lv[i]) << 32) | (uint64_t)(0xFFFFFFFFu - e)) & valid;
+    }
+    sort_desc<KPL>(key);
+
+    int my_id = -1;
+    uint32_t my_key = 0, top_key = 0;
+    for (int r = 0; r < k; ++r) {
+        const uint32_t head = (uint32_t)(key[0] >> 32);
+        const uint32_t m = wave_max_u32(head);
+        const uint64_t cand = __ballot(head == m);
+        int owner;
+        if (__popcll(cand) == 1) {
+            owner = __ffsll((unsigned long long)cand) - 1;
+        } else {   // exact tie: the lowest expert index among the candidates
+            const uint32_t ix = 0xFFFFFFFFu - (uint32_t)key[0];
+            owner = (int)(wave_min_u32(head == m ? ix : 0xFFFFFFFFu) & 63u);
+        }
+        const int id = (int)(0xFFFFFFFFu - (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[0], owner));
+        if (lane == r) {
+            my_id = id;
+            my_key = m;
+        }
+        if (r == 0) top_key = m;
+        if (lane == owner) {
+#pragma unroll
+            for (int i = 0; i + 1 < KPL; ++i) key[i] = key[i + 1];
+            key[KPL - 1] = 0ull;
+        }
+    }
+    const float top = from_order_bits(top_key);
+    const float my_logit = from_order_bits(my_key);
+    const bool all_neg_inf = (top == -INFINITY);
+    float e_sel = 0.f;
+    if (lane < k) e_sel = all_neg_inf ? 1.f : expf(my_logit - top);
+    float denom;
+    if (renorm) {
+        denom = wave_sum_f32(e_sel);
+    } else {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E) part += all_neg_inf ? 1.f : expf(lv[i] - top);
+        }
+        denom = wave_sum_f32(part);
+    }
+    *out_id = my_id;
+    *out_w = e_sel / denom;
+}
+
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm, int lane,
+                                          int* out_id, float* out_w) {
+    if (E <= 128) wave_topk_kpl<2>(row, E, k, renorm, lane, out_id, out_w);
+    else if (E <= 256) wave_topk_kpl<4>(row, E, k, renorm, lane, out_id, out_w);
+    else if (E <= 512) wave_topk_kpl<8>(row, E, k, renorm, lane, out_id, out_w);
+    else wave_topk_kpl<16>(row, E, k, renorm, lane, out_id, out_w);
+}
+
+}  // namespace moe

@@ -34,6 +34,7 @@
 // 4-bit codes use q = 0 only (one shift per code pair).  fp32 activations
 // (and the SwiGLU output feeding the down projection) are split into two bf16
 // terms hi + lo (relative error <= 2^-17) that share the accumulators.
+#include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -53,7 +54,27 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 constexpr uint32_t kMagic = 0x43004300u;   // bf16 pair (128.0, 128.0)
+
+// (d & mask) | magic in one v_and_or_b32.  gfx9 VOP3 encodings take no literal
+// constant and one scalar operand, so the mask goes in an SGPR and the magic
+// in a VGPR (left to itself the compiler emits an AND and an OR).
+__device__ __forceinline__ uint32_t and_or(uint32_t d, uint32_t mask, uint32_t magic_v) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(d), "s"(mask), "v"(magic_v));
+    return r;
+}
+
+__device__ __forceinline__ uint32_t magic_vgpr() {
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(m) : "i"(kMagic));
+    return m;
+}
+
+// Bytes 0-1 of a and of b -> (a.lo16, b.lo16); bytes 2-3 -> (a.hi16, b.hi16).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 constexpr uint32_t kOnes = 0x3F803F80u;    // bf16 pair (1.0, 1.0)
+constexpr int kMaxPass = 8;    // gate/up passes per tile (tile rows = P * passes)
 
 template <int QT>
 struct QTraits;
@@ -94,7 +115,7 @@ __device__ __forceinline__ void arrange_pairs(const uint32_t* nat, uint32_t* pr)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 uint32_t a = nat[8 * d + i / 2], b = nat[8 * d + 4 + i / 2];
-                pr[8 * d + i] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+                pr[8 * d + i] = (i & 1) ? pair_hi(a, b) : pair_lo(a, b);
             }
     } else {
         // dword d: pair i = (v[8d + i], v[8d + i + 4])
@@ -103,7 +124,7 @@ __device__ __forceinline__ void arrange_pairs(const uint32_t* nat, uint32_t* pr)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t a = nat[4 * d + i / 2], b = nat[4 * d + 2 + i / 2];
-                pr[4 * d + i] = (i & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+                pr[4 * d + i] = (i & 1) ? pair_hi(a, b) : pair_lo(a, b);
             }
     }
 }
@@ -176,6 +197,34 @@ __device__ __forceinline__ void load_slice_f32(XSlice<QT, 2>& s, const float* sr
     finish_slice<QT, 2>(s, z);
 }
 
+// A slice stored as packed words pk[j] = bf16 hi(v_j) | bf16 lo(v_j) << 16 (the
+// SwiGLU output as the gate/up stage publishes it): de-interleave into the two
+// terms' dot pairs.
+template <int QT>
+__device__ __forceinline__ void load_slice_packed(XSlice<QT, 2>& s, const uint32_t* pk, float z) {
+    constexpr int QK = QTraits<QT>::QK;
+    constexpr int HALF = QT == 1 ? 8 : 4;   // pair (v, v + HALF) within a dword's codes
+    constexpr int PER = QT == 1 ? 16 : 8;   // values per code dword
+    uint32_t w[QK];
+#pragma unroll
+    for (int v = 0; v < QK / 4; ++v) {
+        const uint4 u = reinterpret_cast<const uint4*>(pk)[v];
+        w[4 * v + 0] = u.x;
+        w[4 * v + 1] = u.y;
+        w[4 * v + 2] = u.z;
+        w[4 * v + 3] = u.w;
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) {
+            const uint32_t a = w[PER * d + i], b = w[PER * d + i + HALF];
+            s.pr[0][HALF * d + i] = pair_lo(a, b);
+            s.pr[1][HALF * d + i] = pair_hi(a, b);
+        }
+    finish_slice<QT, 2>(s, z);
+}
+
 // sum_i s * (c_i - z) x_i of one block for NT tokens (ntok valid).
 template <int QT, int NTERM, int NT>
 __device__ __forceinline__ void block_dot(const uint4 codes, float scale, const XSlice<QT, NTERM> (&xs)[NT],
@@ -187,20 +236,21 @@ __device__ __forceinline__ void block_dot(const uint4 codes, float scale, const 
 #pragma unroll
         for (int q = 0; q < NQ; ++q) acc[t][q] = xs[t].neg_c[q];
     const uint32_t dw[4] = {codes.x, codes.y, codes.z, codes.w};
+    const uint32_t mg = magic_vgpr();
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t D = dw[d];
         if constexpr (QT == 1) {
             uint32_t p[8];
             const uint32_t D6 = D >> 6, D12 = D >> 12;
-            p[0] = (D & 0x00030003u) | kMagic;
-            p[1] = (D & 0x000C000Cu) | kMagic;
-            p[2] = (D & 0x00300030u) | kMagic;
-            p[3] = (D6 & 0x00030003u) | kMagic;
-            p[4] = (D6 & 0x000C000Cu) | kMagic;
-            p[5] = (D6 & 0x00300030u) | kMagic;
-            p[6] = (D12 & 0x00030003u) | kMagic;
-            p[7] = (D12 & 0x000C000Cu) | kMagic;
+            p[0] = and_or(D, 0x00030003u, mg);
+            p[1] = and_or(D, 0x000C000Cu, mg);
+            p[2] = and_or(D, 0x00300030u, mg);
+            p[3] = and_or(D6, 0x00030003u, mg);
+            p[4] = and_or(D6, 0x000C000Cu, mg);
+            p[5] = and_or(D6, 0x00300030u, mg);
+            p[6] = and_or(D12, 0x00030003u, mg);
+            p[7] = and_or(D12, 0x000C000Cu, mg);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if (t < ntok) {
@@ -213,10 +263,10 @@ __device__ __forceinline__ void block_dot(const uint4 codes, float scale, const 
             }
         } else {
             uint32_t p[4];
-            p[0] = (D & 0x000F000Fu) | kMagic;
-            p[1] = ((D >> 4) & 0x000F000Fu) | kMagic;
-            p[2] = ((D >> 8) & 0x000F000Fu) | kMagic;
-            p[3] = ((D >> 12) & 0x000F000Fu) | kMagic;
+            p[0] = and_or(D, 0x000F000Fu, mg);
+            p[1] = and_or(D >> 4, 0x000F000Fu, mg);
+            p[2] = and_or(D >> 8, 0x000F000Fu, mg);
+            p[3] = and_or(D >> 12, 0x000F000Fu, mg);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if (t < ntok) {
@@ -242,89 +292,224 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Gate/up + SwiGLU.
+// Fused decode / verify layer: one kernel per layer.
+//
+// Every workgroup first recomputes the routing and the expert-major buckets of
+// the <= 8 tokens from the logits (a few KB, served from L2).  Workgroups
+// [0, n_gu) run gate/up + SwiGLU tiles and publish their rows of `a` with
+// agent-coherent stores; each tile then bumps its group's counter, and the
+// last tile of a group bumps `groups_done`.  Workgroups [n_gu, grid) own a
+// tile of H output rows: they issue the loads of their down-projection weights
+// for every selected expert at once, wait until every group is done, read
+// `a`, and finish the down projection and the weighted combine for their rows
+// (no second pass).  Workgroups are dispatched in index order on each XCD, so
+// every gate/up workgroup is running or done before any down workgroup on the
+// same XCD starts waiting; the wait is bounded anyway and flags an error if
+// the bound is ever reached.  The last down workgroup to leave returns every
+// counter to zero for the next call.  Same-address atomics serialise (about
+// 12 ns each), so counters are per group, on separate 64-byte lines, and the
+// exit count is two-level.
 // ---------------------------------------------------------------------------------------------
-struct GateUpParams {
+constexpr int kMaxPairs = kSmallT * kMaxK;   // 256
+constexpr size_t kDecodeLdsBudget = 112 * 1024;   // dynamic LDS of the fused decode kernel
+constexpr int kMaxRowsDn = 12;               // H rows per down workgroup
+constexpr int kRowsPerThread = 6;            // down rows one thread prefetches
+constexpr long kSpinLimit = 1l << 22;
+constexpr int kExitFan = 16;                 // first-level exit counters
+
+struct DecodeParams {
     const void* const* table;
-    const uint8_t* single;     // used instead of table[e] when table == nullptr
+    const uint8_t* single;       // one expert's blob when table == nullptr (moe_expert_ffn)
     const uint8_t* shared;
-    const void* x;             // [T][H]
-    int H, FF, FFs, T;
+    const void* x;               // [T][H] bf16 or fp32
+    const float* logits;         // [T][E]
+    int T, E, k, renorm, identity;
+    int H, FF, FFs;
     float z;
-    const SmallMeta* meta;
-    const int* pair_tok;
-    const int* pair_exp;
-    const int* group_first;
-    const int* group_n;
-    uint16_t *a_hi, *a_lo;     // [pairs][FF]
-    uint16_t *as_hi, *as_lo;   // [T][FFs]
-    int passes;                // M: passes per tile (tile rows = P * M)
-    int tiles, tiles_s, max_groups;
+    int* ids_out;                // [T][k] or null
+    float* w_out;                // [T][k] or null
+    uint32_t* a;                 // [T*k][FF] packed bf16 hi | lo << 16, agent-coherent
+    uint32_t* as;                // [T][FFs] the same for the shared expert
+    float* y;                    // [T][H]
+    int* sync;                   // DecodeSync words, see sync_* below
+    int gu_passes, tiles_gu, tiles_gu_s, max_groups, shared_groups, n_gu;
+    int dn_rows, tiles_dn;
 };
 
-constexpr int kMaxPass = 8;
+// Word offsets inside the synchronisation area (ints; 16 ints = one 64-byte line).
+__device__ __forceinline__ int* sync_group(int* s, int g) { return s + 16 * (4 + g); }
+__device__ __forceinline__ int* sync_groups_done(int* s) { return s; }
+__device__ __forceinline__ int* sync_error(int* s) { return s + 16; }
+__device__ __forceinline__ int* sync_exit_top(int* s) { return s + 32; }
+__device__ __forceinline__ int* sync_exit(int* s, int i, int max_groups) { return s + 16 * (4 + max_groups + i); }
+
+struct RouteLDS {
+    int id[kMaxPairs];
+    float w[kMaxPairs];
+    int pair_tok[kMaxPairs], pair_exp[kMaxPairs], slot_pair[kMaxPairs];
+    int group_first[kMaxPairs], group_n[kMaxPairs], group_of_pair[kMaxPairs];
+    int rank[kMaxPairs], pos[kMaxPairs], cnt[kMaxPairs];
+    int slot_src[kMaxPairs];   // slot (t, j) -> group * NT + token-in-group of its pair
+    int n_groups;
+    int flag;
+};
+
+// Routing of the T tokens (wave w takes tokens w, w + 4) and the buckets: pairs
+// (token, slot) sorted by (expert, token); runs of <= NT pairs of one expert
+// form a group.
+template <int NT>
+__device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int k = p.k, T = p.T;
+    if (T == 1) {
+        // One token: the pairs are its k slots, sorted by expert; each is its own group.
+        if (wv == 0) {
+            int id = 0;
+            float wt = 1.f;
+            if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, &id, &wt);
+            int rank = 0;
+            for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(id, i) < id;
+            if (lane < k) {
+                R.id[lane] = id;
+                R.w[lane] = wt;
+                R.slot_pair[lane] = rank;
+                R.pair_tok[rank] = 0;
+                R.pair_exp[rank] = id;
+                R.group_first[rank] = rank;
+                R.group_n[rank] = 1;
+                R.group_of_pair[rank] = rank;
+                R.slot_src[lane] = rank * NT;
+            }
+            if (lane == 0) R.n_groups = k;
+        }
+        __syncthreads();
+        return;
+    }
+    for (int t = wv; t < T; t += kGemvThreads / 64) {
+        int id = 0;
+        float wt = 1.f;
+        if (!p.identity) wave_topk(p.logits + (size_t)t * p.E, p.E, k, p.renorm, lane, &id, &wt);
+        if (lane < k) {
+            R.id[t * k + lane] = id;
+            R.w[t * k + lane] = wt;
+        }
+    }
+    __syncthreads();
+    const int n = T * k;
+    for (int q = tid; q < n; q += kGemvThreads) {
+        const int e = R.id[q], t = q / k;
+        int rank = 0, pos = 0, cnt = 0;
+        for (int t2 = 0; t2 < T; ++t2) {
+#pragma unroll 4
+            for (int j2 = 0; j2 < k; ++j2) {
+                const int er = R.id[t2 * k + j2];
+                rank += (er < e) || (er == e && t2 < t);
+                pos += (er == e && t2 < t);
+                cnt += (er == e);
+            }
+        }
+        R.rank[q] = rank;
+        R.pos[q] = pos;
+        R.cnt[q] = cnt;
+        R.pair_tok[rank] = t;
+        R.pair_exp[rank] = e;
+        R.slot_pair[q] = rank;
+    }
+    __syncthreads();
+    for (int q = tid; q < n; q += kGemvThreads) {
+        const int pos = R.pos[q], rq = R.rank[q];
+        int g = -1;   // groups start at pairs with pos % NT == 0; count those up to this pair
+#pragma unroll 4
+        for (int r = 0; r < n; ++r) g += (R.pos[r] % NT == 0) && (R.rank[r] <= rq);
+        R.group_of_pair[rq] = g;
+        if (pos % NT == 0) {
+            R.group_first[g] = rq;
+            R.group_n[g] = min(NT, R.cnt[q] - pos);
+        }
+    }
+    if (tid == 0) {
+        int ng = 0;
+        for (int r = 0; r < n; ++r) ng += (R.pos[r] % NT == 0);
+        R.n_groups = ng;
+    }
+    __syncthreads();
+    for (int q = tid; q < n; q += kGemvThreads) {
+        const int pr = R.slot_pair[q];
+        const int gg = R.group_of_pair[pr];
+        R.slot_src[q] = gg * NT + (pr - R.group_first[gg]);
+    }
+    __syncthreads();
+}
+
+// Sum of `count` LDS partials part[base + i * stride] by 8 lanes: lane s adds
+// i = s, s + 8, ... in order, then the 8 lanes combine by DPP.  Called by every
+// lane of the wave; lanes with valid == false contribute 0.
+__device__ __forceinline__ float lds_sum8(const float* part, int base, int stride, int count, bool valid, int s) {
+    float v = 0.f;
+    if (valid)
+        for (int i = s; i < count; i += 8) v += part[base + i * stride];
+    return group8_sum_f32(v);
+}
 
 template <int QT, int NT, int NTERM>
-__global__ void __launch_bounds__(kGemvThreads) gateup_kernel(GateUpParams p) {
+__device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float* lds) {
     constexpr int QK = QTraits<QT>::QK;
-    extern __shared__ float lds[];
     const int tid = threadIdx.x;
-    int idx = blockIdx.x;
-
     const uint8_t* blob;
-    int rows, tile, ntok, toks[NT], outrow[NT];
-    uint16_t *ohi, *olo;
-    if (idx < p.max_groups * p.tiles) {
-        const int g = idx / p.tiles;
-        tile = idx - g * p.tiles;
-        if (g >= p.meta->n_groups) return;
-        const int first = p.group_first[g];
-        ntok = p.group_n[g];
-        const int e = p.pair_exp[first];
-        blob = p.table ? (const uint8_t*)p.table[e] : p.single;
+    int rows, tile, ntok, grp, toks[NT], outrow[NT];
+    uint32_t* out;
+    if (item < p.max_groups * p.tiles_gu) {
+        const int g = item / p.tiles_gu;
+        tile = item - g * p.tiles_gu;
+        if (g >= R.n_groups) return;
+        grp = g;
+        const int first = R.group_first[g];
+        ntok = R.group_n[g];
+        blob = p.table ? (const uint8_t*)p.table[R.pair_exp[first]] : p.single;
         rows = p.FF;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            toks[t] = t < ntok ? p.pair_tok[first + t] : 0;
+            toks[t] = R.pair_tok[first + (t < ntok ? t : 0)];
             outrow[t] = first + t;
         }
-        ohi = p.a_hi;
-        olo = p.a_lo;
+        out = p.a;
     } else {
-        idx -= p.max_groups * p.tiles;
-        const int sg = idx / p.tiles_s;
-        tile = idx - sg * p.tiles_s;
+        const int i2 = item - p.max_groups * p.tiles_gu;
+        const int sg = i2 / p.tiles_gu_s;
+        tile = i2 - sg * p.tiles_gu_s;
+        grp = p.max_groups + sg;
         blob = p.shared;
         rows = p.FFs;
         ntok = min(NT, p.T - sg * NT);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            toks[t] = t < ntok ? sg * NT + t : 0;
+            toks[t] = sg * NT + (t < ntok ? t : 0);
             outrow[t] = sg * NT + t;
         }
-        ohi = p.as_hi;
-        olo = p.as_lo;
+        out = p.as;
     }
 
     const int nblk = p.H / QK;
     const int P = kGemvThreads / nblk;
     const bool active = tid < P * nblk;
-    const int rp = tid / nblk, b = tid - (tid / nblk) * nblk;
-    const int R = P * p.passes;
-    const int f0 = tile * R;
-    const size_t plane = (size_t)rows * nblk;        // blocks per matrix
+    const int rp = active ? tid / nblk : 0, b = active ? tid - (tid / nblk) * nblk : 0;
+    const int Rr = P * p.gu_passes;
+    const int f0 = tile * Rr;
+    const size_t plane = (size_t)rows * nblk;
     const uint8_t* gcode = blob;
     const uint8_t* gscale = blob + plane * 16;
     const uint8_t* ucode = blob + plane * 18;
     const uint8_t* uscale = ucode + plane * 16;
 
-    // Issue every code and scale load of the tile first.
+    // Loads of every pass first, from clamped rows (the last tile's overhang
+    // re-reads its last row), so that all of them are in flight at once; the
+    // pass count is uniform across the workgroup.
     uint4 cg[kMaxPass], cu[kMaxPass];
     uint16_t sg_[kMaxPass], su_[kMaxPass];
 #pragma unroll
     for (int m = 0; m < kMaxPass; ++m) {
-        const int f = f0 + m * P + rp;
-        if (m < p.passes && active && f < rows) {
+        if (m < p.gu_passes) {
+            const int f = min(f0 + m * P + rp, rows - 1);
             const size_t blk = (size_t)f * nblk + b;
             cg[m] = *reinterpret_cast<const uint4*>(gcode + blk * 16);
             cu[m] = *reinterpret_cast<const uint4*>(ucode + blk * 16);
@@ -332,211 +517,249 @@ __global__ void __launch_bounds__(kGemvThreads) gateup_kernel(GateUpParams p) {
             su_[m] = *reinterpret_cast<const uint16_t*>(uscale + blk * 2);
         }
     }
-
     XSlice<QT, NTERM> xs[NT];
-    if (active) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < ntok) {
-                if constexpr (NTERM == 1) {
-                    const uint16_t* src = (const uint16_t*)p.x + (size_t)toks[t] * p.H + b * QK;
-                    load_slice_bf16<QT, 1>(xs[t], src, nullptr, p.z);
-                } else {
-                    const float* src = (const float*)p.x + (size_t)toks[t] * p.H + b * QK;
-                    load_slice_f32<QT>(xs[t], src, p.z);
-                }
-            }
-        }
+    for (int t = 0; t < NT; ++t) {
+        if constexpr (NTERM == 1)
+            load_slice_bf16<QT, 1>(xs[t], (const uint16_t*)p.x + (size_t)toks[t] * p.H + b * QK, nullptr, p.z);
+        else
+            load_slice_f32<QT>(xs[t], (const float*)p.x + (size_t)toks[t] * p.H + b * QK, p.z);
     }
-
-    // part[mat][row][b][t]
-    float* part = lds;
+    // part[(mat * Rr + rr) * nblk + b][t]
 #pragma unroll
     for (int m = 0; m < kMaxPass; ++m) {
         const int f = f0 + m * P + rp;
-        if (m < p.passes && active && f < rows) {
+        if (m < p.gu_passes && active && f < rows) {
             float og[NT], ou[NT];
             block_dot<QT, NTERM, NT>(cg[m], half_bits_to_f32(sg_[m]), xs, ntok, og);
             block_dot<QT, NTERM, NT>(cu[m], half_bits_to_f32(su_[m]), xs, ntok, ou);
             const int rr = m * P + rp;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                part[((0 * R + rr) * nblk + b) * NT + t] = og[t];
-                part[((1 * R + rr) * nblk + b) * NT + t] = ou[t];
+                lds[((0 * Rr + rr) * nblk + b) * NT + t] = og[t];
+                lds[((1 * Rr + rr) * nblk + b) * NT + t] = ou[t];
             }
         }
     }
     __syncthreads();
-
-    for (int i = tid; i < R * NT; i += kGemvThreads) {
-        const int rr = i / NT, t = i - (i / NT) * NT;
+    // Row sums: item (mat, rr, t) by 8 lanes; results to red[(mat * Rr + rr) * NT + t].
+    float* red = lds + 2 * Rr * nblk * NT;
+    const int n_items = 2 * Rr * NT;
+    for (int it0 = 0; it0 < n_items; it0 += kGemvThreads / 8) {
+        const int it = it0 + tid / 8, s = tid & 7;
+        const bool valid = it < n_items;
+        const int mat = valid ? it / (Rr * NT) : 0;
+        const int rr = valid ? (it / NT) % Rr : 0;
+        const int t = valid ? it % NT : 0;
+        const float v = lds_sum8(lds, ((mat * Rr + rr) * nblk) * NT + t, NT, nblk, valid, s);
+        if (valid && s == 0) red[(mat * Rr + rr) * NT + t] = v;
+    }
+    __syncthreads();
+    for (int i = tid; i < Rr * NT; i += kGemvThreads) {
+        const int rr = i / NT, t = i - rr * NT;
         const int f = f0 + rr;
         if (f >= rows || t >= ntok) continue;
-        float g = 0.f, u = 0.f;
-        for (int bb = 0; bb < nblk; ++bb) {
-            g += part[((0 * R + rr) * nblk + bb) * NT + t];
-            u += part[((1 * R + rr) * nblk + bb) * NT + t];
-        }
+        const float g = red[(0 * Rr + rr) * NT + t];
+        const float u = red[(1 * Rr + rr) * NT + t];
         const float a = g / (1.f + expf(-g)) * u;
+        // two bf16 terms hi + lo (relative error <= 2^-17), split once here
         const uint32_t hi = bf16_rne(a);
         const uint32_t lo = bf16_rne(a - bf16_to_f32(hi));
-        const size_t o = (size_t)outrow[t] * rows + f;
-        ohi[o] = (uint16_t)hi;
-        olo[o] = (uint16_t)lo;
+        __hip_atomic_store(out + (size_t)outrow[t] * rows + f, hi | (lo << 16), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();   // every store above has completed (the barrier waits for them)
+    if (tid == 0) {
+        __hip_atomic_fetch_add(sync_group(p.sync, grp), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
-
-// ---------------------------------------------------------------------------------------------
-// Down projection + deterministic combine.
-// ---------------------------------------------------------------------------------------------
-struct DownParams {
-    const void* const* table;
-    const uint8_t* single;
-    const uint8_t* shared;
-    int H, FF, FFs, T, k;
-    float z;
-    const SmallMeta* meta;
-    const int* pair_tok;
-    const int* pair_exp;
-    const int* group_first;
-    const int* group_n;
-    const int* slot_pair;
-    const float* w;              // [T][k]
-    const uint16_t *a_hi, *a_lo;
-    const uint16_t *as_hi, *as_lo;
-    float* d;                    // [pairs][H]
-    float* ds;                   // [T][H]
-    float* y;                    // [T][H]
-    int* tile_cnt;
-    int tile_rows;               // R: H rows per tile
-    int tiles, max_groups, shared_groups;
-};
 
 template <int QT, int NT>
-__global__ void __launch_bounds__(kGemvThreads) down_kernel(DownParams p) {
+__device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* lds) {
     constexpr int QK = QTraits<QT>::QK;
-    extern __shared__ float lds[];
-    __shared__ int s_last;
     const int tid = threadIdx.x;
-    int idx = blockIdx.x;
+    const int h0 = tile * p.dn_rows;
+    const int nrows = min(p.dn_rows, p.H - h0);
+    const int nb_r = p.FF / QK;
+    const int nb_s = p.FFs / QK;
+    const int ng = R.n_groups;
+    const int n_units = ng * nb_r + p.shared_groups * nb_s;
+    // Units (group, block column); with few units, S threads split a unit's rows.
+    int S = kGemvThreads / n_units;
+    S = S < 1 ? 1 : (S > nrows ? nrows : S);
+    const int per_round = kGemvThreads / S;
+    const size_t gu_r = (size_t)2 * p.FF * (p.H / QK) * 18, gu_s = (size_t)2 * p.FFs * (p.H / QK) * 18;
 
-    const uint8_t* blob;
-    int K, tile, ntok, arow[NT];
-    const uint16_t *ahi, *alo;
-    float* out;
-    if (idx < p.max_groups * p.tiles) {
-        const int g = idx / p.tiles;
-        tile = idx - g * p.tiles;
-        if (g >= p.meta->n_groups) return;
-        const int first = p.group_first[g];
-        ntok = p.group_n[g];
-        const int e = p.pair_exp[first];
-        blob = p.table ? (const uint8_t*)p.table[e] : p.single;
-        K = p.FF;
+    // part[(unit * dn_rows + r) * NT + t]
+    bool waited = false;
+    for (int u0 = 0; u0 < n_units; u0 += per_round) {
+        const int uu = u0 + tid / S, rs = tid - (tid / S) * S;
+        const bool act = (tid / S) < per_round && uu < n_units;
+        const int u = act ? uu : 0;
+        int g, b, K, nb, ntok;
+        const uint8_t* dcode;
+        if (u < ng * nb_r) {
+            g = u / nb_r;
+            b = u - g * nb_r;
+            K = p.FF;
+            nb = nb_r;
+            const int first = R.group_first[g];
+            ntok = R.group_n[g];
+            dcode = (p.table ? (const uint8_t*)p.table[R.pair_exp[first]] : p.single) + gu_r;
+        } else {
+            const int us = u - ng * nb_r;
+            g = us / nb_s;            // shared group
+            b = us - g * nb_s;
+            K = p.FFs;
+            nb = nb_s;
+            ntok = min(NT, p.T - g * NT);
+            dcode = p.shared + gu_s;
+        }
+        const uint8_t* dscale = dcode + (size_t)p.H * nb * 16;
+        uint4 c[kRowsPerThread];
+        uint16_t sc[kRowsPerThread];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) arow[t] = first + t;
-        ahi = p.a_hi;
-        alo = p.a_lo;
-        out = p.d;
-    } else {
-        idx -= p.max_groups * p.tiles;
-        const int sg = idx / p.tiles;
-        tile = idx - sg * p.tiles;
-        blob = p.shared;
-        K = p.FFs;
-        ntok = min(NT, p.T - sg * NT);
+        for (int i = 0; i < kRowsPerThread; ++i) {
+            const int r = min(rs + i * S, nrows - 1);
+            const size_t blk = (size_t)(h0 + r) * nb + b;
+            c[i] = *reinterpret_cast<const uint4*>(dcode + blk * 16);
+            sc[i] = *reinterpret_cast<const uint16_t*>(dscale + blk * 2);
+        }
+        if (!waited) {
+            // Thread g of the first wave watches group g's tile counter (routed
+            // groups, then shared groups); the wave continues when all are full.
+            if (tid < 64) {
+                long spins = 0;
+                for (int g0 = 0; g0 < ng + p.shared_groups; g0 += 64) {
+                    const int gi = g0 + tid;
+                    const bool mine = gi < ng + p.shared_groups;
+                    const int ctr = gi < ng ? gi : p.max_groups + (gi - ng);
+                    const int need = gi < ng ? p.tiles_gu : p.tiles_gu_s;
+                    while (true) {
+                        const bool ready = !mine || __hip_atomic_load(sync_group(p.sync, ctr), __ATOMIC_RELAXED,
+                                                                      __HIP_MEMORY_SCOPE_AGENT) >= need;
+                        if (__all(ready)) break;
+                        if (++spins > kSpinLimit) {
+                            if (tid == 0)
+                                __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __syncthreads();
+            waited = true;
+        }
+        if (act) {
+            XSlice<QT, 2> xs[NT];
+            const bool sh = u >= ng * nb_r;
+            const uint32_t* abase = sh ? p.as : p.a;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) arow[t] = sg * NT + t;
-        ahi = p.as_hi;
-        alo = p.as_lo;
-        out = p.ds;
-    }
-
-    const int nblk = K / QK;
-    const int P = kGemvThreads / nblk;
-    const bool active = tid < P * nblk;
-    const int rp = tid / nblk, b = tid - (tid / nblk) * nblk;
-    const int R = p.tile_rows;
-    const int h0 = tile * R;
-    const int hend = min(p.H, h0 + R);
-    // The gate and up planes come first: 2 * FF * (H / qk) blocks of 18 bytes.
-    const size_t gu_bytes = (size_t)2 * K * (p.H / QK) * 18;
-    const uint8_t* dcode = blob + gu_bytes;
-    const uint8_t* dscale = dcode + (size_t)p.H * nblk * 16;
-
-    XSlice<QT, 2> xs[NT];
-    if (active) {
+            for (int t = 0; t < NT; ++t) {
+                const int tt = t < ntok ? t : 0;
+                const int row = sh ? g * NT + tt : R.group_first[g] + tt;
+                load_slice_packed<QT>(xs[t], abase + (size_t)row * K + b * QK, p.z);
+            }
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            if (t < ntok)
-                load_slice_bf16<QT, 2>(xs[t], ahi + (size_t)arow[t] * K + b * QK, alo + (size_t)arow[t] * K + b * QK,
-                                       p.z);
-    }
-
-    float* part = lds;
-    for (int base = h0; base < hend; base += P * kMaxPass) {
-        uint4 c[kMaxPass];
-        uint16_t sc[kMaxPass];
+            for (int i = 0; i < kRowsPerThread; ++i) {
+                const int r = rs + i * S;
+                if (r < nrows) {
+                    float o[NT];
+                    block_dot<QT, 2, NT>(c[i], half_bits_to_f32(sc[i]), xs, ntok, o);
 #pragma unroll
-        for (int m = 0; m < kMaxPass; ++m) {
-            const int h = base + m * P + rp;
-            if (active && h < hend) {
-                const size_t blk = (size_t)h * nblk + b;
-                c[m] = *reinterpret_cast<const uint4*>(dcode + blk * 16);
-                sc[m] = *reinterpret_cast<const uint16_t*>(dscale + blk * 2);
+                    for (int t = 0; t < NT; ++t) lds[((size_t)u * p.dn_rows + r) * NT + t] = o[t];
+                }
             }
         }
-#pragma unroll
-        for (int m = 0; m < kMaxPass; ++m) {
-            const int h = base + m * P + rp;
-            if (active && h < hend) {
-                float o[NT];
-                block_dot<QT, 2, NT>(c[m], half_bits_to_f32(sc[m]), xs, ntok, o);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) part[((m * P + rp) * nblk + b) * NT + t] = o[t];
-            }
+    }
+    __syncthreads();
+    // d of every (group, row, token): sum over the group's block columns in order.
+    float* dsum = lds + (size_t)n_units * p.dn_rows * NT;    // [(group or shared group) * dn_rows + r][t]
+    const int n_grp = ng + p.shared_groups;
+    const int n_items = n_grp * nrows * NT;
+    for (int it0 = 0; it0 < n_items; it0 += kGemvThreads / 8) {
+        const int it = it0 + tid / 8, s = tid & 7;
+        const bool valid = it < n_items;
+        const int gg = valid ? it / (nrows * NT) : 0;
+        const int r = valid ? (it / NT) % nrows : 0;
+        const int t = valid ? it % NT : 0;
+        const bool sh = gg >= ng;
+        const int nb = sh ? nb_s : nb_r;
+        const int u_first = sh ? ng * nb_r + (gg - ng) * nb_s : gg * nb_r;
+        const float v = lds_sum8(lds, (u_first * p.dn_rows + r) * NT + t, p.dn_rows * NT, nb, valid, s);
+        if (valid && s == 0) dsum[(gg * p.dn_rows + r) * NT + t] = v;
+    }
+    __syncthreads();
+    // y[t][h] = shared(t)[h] + sum_j w[t][j] * d(pair(t, j))[h], in this order.
+    for (int i = tid; i < p.T * nrows; i += kGemvThreads) {
+        const int t = i / nrows, r = i - t * nrows;
+        float acc = 0.f;
+        if (p.shared) acc = dsum[((ng + t / NT) * p.dn_rows + r) * NT + (t % NT)];
+        const int* src = R.slot_src + t * p.k;
+        const float* wt = R.w + t * p.k;
+#pragma unroll 4
+        for (int j = 0; j < p.k; ++j) {
+            const int gs = src[j];   // group * NT + token in group
+            const int gg = gs / NT, tt = gs - (gs / NT) * NT;
+            acc = __builtin_fmaf(wt[j], dsum[(gg * p.dn_rows + r) * NT + tt], acc);
         }
-        __syncthreads();
-        const int rows_here = min(P * kMaxPass, hend - base);
-        for (int i = tid; i < rows_here * NT; i += kGemvThreads) {
-            const int rr = i / NT, t = i - (i / NT) * NT;
-            if (t >= ntok) continue;
-            float acc = 0.f;
-            for (int bb = 0; bb < nblk; ++bb) acc += part[(rr * nblk + bb) * NT + t];
-            out[(size_t)arow[t] * p.H + base + rr] = acc;
-        }
-        __syncthreads();
+        p.y[(size_t)t * p.H + h0 + r] = acc;
     }
 
-    // The last workgroup to finish this tile of H rows combines it.
-    __threadfence();
+    // Two-level exit count over the down workgroups; the last one resets every counter.
     __syncthreads();
     if (tid == 0) {
-        const int expected = p.meta->n_groups + p.shared_groups;
-        const int old = atomicAdd(&p.tile_cnt[tile], 1);
-        s_last = (old == expected - 1);
+        const int fan = min(kExitFan, p.tiles_dn);
+        const int i = tile % fan;
+        const int members = (p.tiles_dn - i + fan - 1) / fan;
+        int last = 0;
+        if (__hip_atomic_fetch_add(sync_exit(p.sync, i, p.max_groups + p.shared_groups), 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == members - 1)
+            last = __hip_atomic_fetch_add(sync_exit_top(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   fan - 1;
+        R.flag = last;
     }
     __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int rows_tile = hend - h0;
-    for (int i = tid; i < p.T * rows_tile; i += kGemvThreads) {
-        const int t = i / rows_tile, h = h0 + (i - (i / rows_tile) * rows_tile);
-        float acc = p.shared ? p.ds[(size_t)t * p.H + h] : 0.f;
-        for (int j = 0; j < p.k; ++j) {
-            const int pr = p.slot_pair[t * p.k + j];
-            acc = __builtin_fmaf(p.w[t * p.k + j], p.d[(size_t)pr * p.H + h], acc);
+    if (R.flag) {
+        const int n_ctr = p.max_groups + p.shared_groups;
+        const int fan = min(kExitFan, p.tiles_dn);
+        for (int i = tid; i < n_ctr; i += kGemvThreads)
+            __hip_atomic_store(sync_group(p.sync, i), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = tid; i < fan; i += kGemvThreads)
+            __hip_atomic_store(sync_exit(p.sync, i, n_ctr), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            __hip_atomic_store(sync_groups_done(p.sync), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync_exit_top(p.sync), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        p.y[(size_t)t * p.H + h] = acc;
     }
 }
 
+template <int QT, int NT, int NTERM>
+__global__ void __launch_bounds__(kGemvThreads, NT == 1 ? 3 : 2) decode_layer_kernel(DecodeParams p) {
+    extern __shared__ float lds[];
+    __shared__ RouteLDS R;
+    const int tid = threadIdx.x;
+    route_and_bucket<NT>(p, R);
+    const int wg = blockIdx.x;
+    if (wg == 0) {
+        for (int q = tid; q < p.T * p.k; q += kGemvThreads) {
+            if (p.ids_out) p.ids_out[q] = R.id[q];
+            if (p.w_out) p.w_out[q] = R.w[q];
+        }
+    }
+    if (wg < p.n_gu) gateup_role<QT, NT, NTERM>(p, R, wg, lds);
+    else down_role<QT, NT>(p, R, wg - p.n_gu, lds);
+}
+
 // ---------------------------------------------------------------------------------------------
-// Host side.
+// Host side of the decode path.
 // ---------------------------------------------------------------------------------------------
-GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z) {
+GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     GemvShape g{};
     const int qk = codes_per_block(qtype);
+    const int NT = T == 1 ? 1 : kGroup;
     g.H = H;
     g.FF = FF;
     g.FFs = FFs;
@@ -544,111 +767,97 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z) {
     g.z = z;
     const int nblk_gu = H / qk;
     const int P = kGemvThreads / nblk_gu;
-    const int passes = 2;
-    g.tile_rows_gu = P * passes;
+    g.max_groups = T * k;
+    // Enough passes per gate/up workgroup that about 384 of them cover the
+    // routed experts' FF rows (more loads in flight per thread, and every
+    // workgroup of the layer resident at once).
+    {
+        const long rows_all = (long)g.max_groups * FF;
+        int passes = (int)((rows_all + (long)P * 384 - 1) / ((long)P * 384));
+        g.gu_passes = passes < 1 ? 1 : (passes > kMaxPass ? kMaxPass : passes);
+    }
+    g.tile_rows_gu = P * g.gu_passes;
     g.tiles_gu = (FF + g.tile_rows_gu - 1) / g.tile_rows_gu;
     g.tiles_gu_s = FFs ? (FFs + g.tile_rows_gu - 1) / g.tile_rows_gu : 0;
-    const int nblk_dn = FF / qk;
-    const int Pd = kGemvThreads / nblk_dn;
-    g.tile_rows_dn = Pd * 4;
-    g.tiles_dn = (H + g.tile_rows_dn - 1) / g.tile_rows_dn;
+    const int per_expert = (T + NT - 1) / NT;
+    g.shared_groups = FFs ? per_expert : 0;
+    g.n_gu = g.max_groups * g.tiles_gu + g.shared_groups * g.tiles_gu_s;
+    // About 256 down workgroups of at most kMaxRowsDn rows, fewer rows if the
+    // partial sums of every (unit, row, token) would not fit in LDS.  The row
+    // count does not change any summation order.
+    const int nb_r = FF / qk, nb_s = FFs / qk;
+    const size_t units = (size_t)g.max_groups * nb_r + (size_t)g.shared_groups * nb_s;
+    const size_t per_row = (units + g.max_groups + g.shared_groups) * NT * 4;
+    // One thread prefetches at most kRowsPerThread rows of its unit; with few
+    // units, S = 256 / units threads share a unit's rows.
+    int s_min = (int)(kGemvThreads / units);
+    s_min = s_min < 1 ? 1 : s_min;
+    int rows = (H + 255) / 256;
+    rows = rows < 1 ? 1 : (rows > kMaxRowsDn ? kMaxRowsDn : rows);
+    if (rows > kRowsPerThread * s_min) rows = kRowsPerThread * s_min;
+    while (rows > 1 && per_row * rows > kDecodeLdsBudget) --rows;
+    g.tile_rows_dn = rows;
+    g.tiles_dn = (H + rows - 1) / rows;
+    const size_t lds_dn = per_row * rows;
+    const size_t lds_gu = ((size_t)2 * g.tile_rows_gu * nblk_gu * NT + (size_t)2 * g.tile_rows_gu * NT) * 4;
+    g.lds_bytes = lds_dn > lds_gu ? lds_dn : lds_gu;
+    g.grid = g.n_gu + g.tiles_dn;
     return g;
 }
 
-template <int QT, int NT>
-static hipError_t launch_for(const GemvShape& g, const void* const* table, const void* single, const void* shared,
-                             const void* x, int x_dtype, int T, int k, int max_groups, const float* w,
-                             const SmallLayout& L, char* ws, float* y, hipStream_t s) {
-    constexpr int QK = QTraits<QT>::QK;
-    const int shared_groups = shared ? (T + NT - 1) / NT : 0;
-    GateUpParams gp{};
-    gp.table = table;
-    gp.single = (const uint8_t*)single;
-    gp.shared = (const uint8_t*)shared;
-    gp.x = x;
-    gp.H = g.H;
-    gp.FF = g.FF;
-    gp.FFs = g.FFs;
-    gp.T = T;
-    gp.z = g.z;
-    gp.meta = (const SmallMeta*)(ws + L.meta);
-    gp.pair_tok = (const int*)(ws + L.pair_tok);
-    gp.pair_exp = (const int*)(ws + L.pair_exp);
-    gp.group_first = (const int*)(ws + L.group_first);
-    gp.group_n = (const int*)(ws + L.group_n);
-    gp.a_hi = (uint16_t*)(ws + L.a_hi);
-    gp.a_lo = (uint16_t*)(ws + L.a_lo);
-    gp.as_hi = (uint16_t*)(ws + L.as_hi);
-    gp.as_lo = (uint16_t*)(ws + L.as_lo);
-    const int nblk = g.H / QK;
-    const int P = kGemvThreads / nblk;
-    gp.passes = g.tile_rows_gu / P;
-    gp.tiles = g.tiles_gu;
-    gp.tiles_s = g.tiles_gu_s;
-    gp.max_groups = max_groups;
-    const size_t lds_gu = (size_t)2 * g.tile_rows_gu * nblk * NT * sizeof(float);
-    const int grid_gu = max_groups * g.tiles_gu + shared_groups * g.tiles_gu_s;
-    if (x_dtype == 1)
-        hipLaunchKernelGGL((gateup_kernel<QT, NT, 1>), dim3(grid_gu), dim3(kGemvThreads), lds_gu, s, gp);
-    else
-        hipLaunchKernelGGL((gateup_kernel<QT, NT, 2>), dim3(grid_gu), dim3(kGemvThreads), lds_gu, s, gp);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-
-    DownParams dp{};
-    dp.table = table;
-    dp.single = (const uint8_t*)single;
-    dp.shared = (const uint8_t*)shared;
-    dp.H = g.H;
-    dp.FF = g.FF;
-    dp.FFs = g.FFs;
-    dp.T = T;
-    dp.k = k;
-    dp.z = g.z;
-    dp.meta = gp.meta;
-    dp.pair_tok = gp.pair_tok;
-    dp.pair_exp = gp.pair_exp;
-    dp.group_first = gp.group_first;
-    dp.group_n = gp.group_n;
-    dp.slot_pair = (const int*)(ws + L.slot_pair);
-    dp.w = w;
-    dp.a_hi = gp.a_hi;
-    dp.a_lo = gp.a_lo;
-    dp.as_hi = gp.as_hi;
-    dp.as_lo = gp.as_lo;
-    dp.d = (float*)(ws + L.d);
-    dp.ds = (float*)(ws + L.ds);
-    dp.y = y;
-    dp.tile_cnt = (int*)(ws + L.tile_cnt);
-    dp.tile_rows = g.tile_rows_dn;
-    dp.tiles = g.tiles_dn;
-    dp.max_groups = max_groups;
-    dp.shared_groups = shared_groups;
-    const int nb_r = g.FF / QK;
-    const int nb_s = g.FFs ? g.FFs / QK : nb_r;
-    const int nb_max = nb_r > nb_s ? nb_r : nb_s;
-    size_t lds_dn = 0;
-    for (int nb : {nb_r, nb_s}) {
-        const size_t need = (size_t)(kGemvThreads / nb) * kMaxPass * nb * NT * sizeof(float);
-        if (need > lds_dn) lds_dn = need;
+template <int QT, int NT, int NTERM>
+static hipError_t launch_decode_t(const GemvShape& g, DecodeParams& p, hipStream_t s) {
+    static bool attr_set = false;   // allow the dynamic LDS the largest windows need
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)decode_layer_kernel<QT, NT, NTERM>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
     }
-    (void)nb_max;
-    const int grid_dn = (max_groups + shared_groups) * g.tiles_dn;
-    hipLaunchKernelGGL((down_kernel<QT, NT>), dim3(grid_dn), dim3(kGemvThreads), lds_dn, s, dp);
+    hipLaunchKernelGGL((decode_layer_kernel<QT, NT, NTERM>), dim3(g.grid), dim3(kGemvThreads), g.lds_bytes, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_layer(const GemvShape& g, const void* const* table, const void* single_blob,
-                             const void* shared, const void* x, int x_dtype, int T, int k, int max_groups,
-                             const int* /*ids*/, const float* w, const SmallLayout& L, char* ws, float* y,
-                             hipStream_t s) {
-    const bool one = (T == 1);
-    if (g.qtype == 1)
-        return one ? launch_for<1, 1>(g, table, single_blob, shared, x, x_dtype, T, k, max_groups, w, L, ws, y, s)
-                   : launch_for<1, kGroup>(g, table, single_blob, shared, x, x_dtype, T, k, max_groups, w, L, ws, y,
-                                           s);
-    return one ? launch_for<2, 1>(g, table, single_blob, shared, x, x_dtype, T, k, max_groups, w, L, ws, y, s)
-               : launch_for<2, kGroup>(g, table, single_blob, shared, x, x_dtype, T, k, max_groups, w, L, ws, y, s);
+template <int QT, int NT>
+static hipError_t launch_decode(const GemvShape& g, DecodeParams& p, int x_dtype, hipStream_t s) {
+    return x_dtype == 1 ? launch_decode_t<QT, NT, 1>(g, p, s) : launch_decode_t<QT, NT, 2>(g, p, s);
+}
+
+hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, const void* single, const void* shared,
+                               const void* x, int x_dtype, const float* logits, int T, int E, int k, int renorm,
+                               int identity, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
+                               hipStream_t s) {
+    DecodeParams p{};
+    p.table = table;
+    p.single = (const uint8_t*)single;
+    p.shared = (const uint8_t*)shared;
+    p.x = x;
+    p.logits = logits;
+    p.T = T;
+    p.E = E;
+    p.k = k;
+    p.renorm = renorm;
+    p.identity = identity;
+    p.H = g.H;
+    p.FF = g.FF;
+    p.FFs = g.FFs;
+    p.z = g.z;
+    p.ids_out = ids_out;
+    p.w_out = w_out;
+    p.a = (uint32_t*)(ws + L.a);
+    p.as = (uint32_t*)(ws + L.as);
+    p.y = y;
+    p.sync = (int*)(ws + L.sync);
+    p.gu_passes = g.gu_passes;
+    p.tiles_gu = g.tiles_gu;
+    p.tiles_gu_s = g.tiles_gu_s;
+    p.max_groups = g.max_groups;
+    p.shared_groups = g.shared_groups;
+    p.n_gu = g.n_gu;
+    p.dn_rows = g.tile_rows_dn;
+    p.tiles_dn = g.tiles_dn;
+    if (T == 1) return g.qtype == 1 ? launch_decode<1, 1>(g, p, x_dtype, s) : launch_decode<2, 1>(g, p, x_dtype, s);
+    return g.qtype == 1 ? launch_decode<1, kGroup>(g, p, x_dtype, s) : launch_decode<2, kGroup>(g, p, x_dtype, s);
 }
 
 // ---------------------------------------------------------------------------------------------

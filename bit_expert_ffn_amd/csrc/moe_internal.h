@@ -21,22 +21,18 @@ constexpr int kBlockBytes = 18;
 
 inline int codes_per_block(int qtype) { return qtype == 1 ? 64 : (qtype == 2 ? 32 : 0); }
 
-// Routing / bucketing results of the GEMV path, written by the route kernel.
-struct SmallMeta {
-    int n_pairs;    // T * k (token, slot) pairs
-    int n_groups;   // expert-major groups of <= kGroup pairs
-    int n_active;   // distinct experts
-    int pad;
-};
+// Synchronisation area of the fused decode kernel, at offset 0 of the
+// workspace: 64-byte lines holding groups_done, error, the top exit counter,
+// one counter per group and the first-level exit counters.  It must be zero
+// before the first call on a workspace; every call leaves it zero again.
+inline size_t decode_sync_bytes(int max_groups_total) { return (size_t)64 * (4 + max_groups_total + 16); }
 
 // Workspace layout for the GEMV path (T <= kSmallT), byte offsets.
 struct SmallLayout {
-    size_t ids, w, meta, pair_tok, pair_slot, pair_exp, slot_pair, group_first, group_n, active;
-    size_t a_hi, a_lo;       // [pairs][FF] bf16: SwiGLU output split into two bf16 terms
-    size_t as_hi, as_lo;     // [T][FFs] shared expert's
-    size_t d;                // [pairs][H] fp32: per-pair down projection
-    size_t ds;               // [T][H] fp32: shared expert's down projection
-    size_t tile_cnt;         // [tiles] arrival counters of the combine
+    size_t sync;
+    size_t ids, w;           // [T][k] routing when the caller passes no output
+    size_t a;                // [T*k][FF] fp32 SwiGLU output per (expert, token) pair
+    size_t as;               // [T][FFs] fp32 shared expert's
     size_t total;
 };
 
@@ -53,25 +49,24 @@ struct LargeLayout {
 struct GemvShape {
     int H, FF, FFs, qtype;
     float z;
-    int tile_rows_gu;   // rows of FF per gate/up workgroup
-    int tile_rows_dn;   // rows of H per down workgroup
-    int tiles_gu, tiles_gu_s, tiles_dn;
+    int gu_passes, tile_rows_gu, tiles_gu, tiles_gu_s;
+    int max_groups, shared_groups, n_gu;
+    int tile_rows_dn, tiles_dn;
+    size_t lds_bytes;
+    int grid;
 };
 
-SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype);
+SmallLayout small_layout(int T, int k, int FF, int FFs);
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype);
-GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z);
+GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k);
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renorm, int* ids, float* w,
                              hipStream_t s);
-hipError_t launch_route_bucket_small(const float* logits, int T, int E, int k, int renorm, int identity,
-                                     int* ids, float* w, const SmallLayout& L, char* ws, int n_counters,
-                                     hipStream_t s);
-hipError_t launch_gemv_layer(const GemvShape& g, const void* const* table, const void* single_blob,
-                             const void* shared, const void* x, int x_dtype, int T, int k, int max_groups,
-                             const int* ids, const float* w, const SmallLayout& L, char* ws, float* y,
-                             hipStream_t s);
+hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, const void* single, const void* shared,
+                               const void* x, int x_dtype, const float* logits, int T, int E, int k, int renorm,
+                               int identity, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
+                               hipStream_t s);
 hipError_t launch_dequant(const void* blob, int qtype, float z, int rows, int cols, size_t plane_offset,
                           float* out, hipStream_t s);
 

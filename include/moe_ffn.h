@@ -36,7 +36,12 @@
  *     from run to run (no atomics on any value path).  On the decode/verify path
  *     (T <= 8) a token's output is also bitwise independent of the other tokens
  *     in the batch.
- *   - Calls with distinct workspaces may run concurrently on distinct streams.
+ *   - Calls with distinct workspaces may run concurrently on distinct streams;
+ *     calls that share a workspace must be ordered (same stream, or events).
+ *   - Workspace: a device buffer of at least the *_workspace_bytes size,
+ *     256-byte aligned, ZERO-FILLED ONCE after allocation.  Its leading bytes
+ *     hold synchronisation counters of the decode kernel, which every call
+ *     returns to zero; the rest is scratch.
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H

@@ -247,3 +247,55 @@ def test_k_equals_e_and_single_expert():
     y = moe.layer_forward(desc, table[:1].contiguous(), torch.from_numpy(x).to(DEV),
                           torch.zeros((3, 1), device=DEV))
     assert max_err_over_rms(y.cpu().numpy(), oracle.expert_ffn(blobs[0], 2, 7.5, H, FF, x)) <= TOL
+
+
+def test_workspace_sync_words_return_to_zero():
+    """The fused decode kernel's synchronisation area (64-byte lines at the start
+    of the workspace) is zero after every call, and no bounded wait ran out."""
+    w = wl.WORKLOADS["gemma_decode"]
+    arena = wl.DeviceArena(w, device=DEV, layers=[0])
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k, shared_ff=w.shared_ff)
+    for T in (1, 3, 8):
+        ws = moe.workspace(moe.layer_workspace_bytes(desc, T), DEV)
+        x, logits = wl.device_inputs(w, 0, T, device=DEV, tokens=T)
+        y0 = moe.layer_forward(desc, arena.tables[0], x, logits, shared=arena.shared_blob(0), ws=ws)
+        for _ in range(5):
+            y = moe.layer_forward(desc, arena.tables[0], x, logits, shared=arena.shared_blob(0), ws=ws)
+            assert torch.equal(y, y0)
+        torch.cuda.synchronize()
+        nsync = 64 * (4 + T * w.top_k + T + 16)
+        assert int(ws[:nsync].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_graph_replays_match_eager():
+    """Calls captured in a HIP graph give, on every replay, the eager result."""
+    w = wl.WORKLOADS["strata_decode"]
+    arena = wl.DeviceArena(w, device=DEV, layers=[0, 1, 2])
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k)
+    ws = moe.workspace(moe.layer_workspace_bytes(desc, 1), DEV)
+    inputs = [wl.device_inputs(w, l, 9, device=DEV) for l in range(3)]
+    ys = [torch.empty((1, w.hidden), device=DEV) for _ in range(3)]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for l in range(3):
+            moe.layer_forward(desc, arena.tables[l], *inputs[l], y=ys[l], ws=ws, stream=stream)
+    stream.synchronize()
+    eager = [y.clone() for y in ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for l in range(3):
+                moe.layer_forward(desc, arena.tables[l], *inputs[l], y=ys[l], ws=ws, stream=stream)
+    for rep in range(4):
+        for y in ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        stream.synchronize()
+        for l in range(3):
+            assert torch.equal(ys[l], eager[l]), f"replay {rep} layer {l}"
+        # eager work between replays
+        moe.layer_forward(desc, arena.tables[0], *inputs[1], ws=moe.workspace(256 * 1024, DEV))
+        torch.cuda.synchronize()
+    assert int(ws[:64 * (4 + w.top_k + 1 + 16)].view(torch.int32).abs().sum().item()) == 0
