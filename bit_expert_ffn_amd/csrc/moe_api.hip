@@ -150,7 +150,12 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
         return MOE_OK;
     }
-    return fail(MOE_ERR_UNSUPPORTED, "T = %d above %d: matrix-core path not built", T, kSmallT);
+    const LargeLayout L = large_layout(T, k, E, ed.hidden, ed.ff, FFs, ed.qtype);
+    if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
+    hipError_t e = launch_prefill_layer(table, single, shared, ed.qtype, ed.zero_point, ed.hidden, ed.ff, FFs, x, x_dtype,
+                                        logits, T, E, k, renorm, identity ? 1 : 0, ids_out, w_out, L, wsb, y, s);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
+    return MOE_OK;
 }
 
 moe_status moe_expert_ffn(const moe_expert_desc* desc, const void* blob, const void* x, int32_t x_dtype, int32_t T,

@@ -38,11 +38,13 @@ struct SmallLayout {
 
 // Workspace layout for the matrix-core path (T > kSmallT), byte offsets.
 struct LargeLayout {
-    size_t ids, w, counts, offsets, perm, inv, tiles, ntiles;
-    size_t a;                // [pairs][FF] bf16 hi/lo interleaved in 2 planes
-    size_t as;               // [T][FFs] shared
-    size_t ypair;            // [pairs][H] fp32
-    size_t ys;               // [T][H] fp32 shared output
+    size_t ids, w;           // [T][k] routing when the caller passes no output
+    size_t counts, offsets;  // per expert
+    size_t tiles, ntiles;    // row tiles: (expert, first sorted row, rows)
+    size_t perm, inv;        // sorted row -> token; (token, slot) -> sorted row
+    size_t a;                // [rows][FFmax] bf16 hi plane, then the lo plane
+    size_t ypair;            // [rows][H] fp32 down projection per sorted row
+    size_t max_tiles;
     size_t total;
 };
 
@@ -67,6 +69,10 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
                                const void* x, int x_dtype, const float* logits, int T, int E, int k, int renorm,
                                int identity, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
                                hipStream_t s);
+hipError_t launch_prefill_layer(const void* const* table, const void* single, const void* shared, int qtype, float z,
+                                int H, int FF, int FFs, const void* x, int x_dtype, const float* logits, int T, int E,
+                                int k, int renorm, int identity, int* ids_out, float* w_out, const LargeLayout& L,
+                                char* ws, float* y, hipStream_t s);
 hipError_t launch_dequant(const void* blob, int qtype, float z, int rows, int cols, size_t plane_offset,
                           float* out, hipStream_t s);
 
