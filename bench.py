@@ -9,7 +9,11 @@ logits are generated and uploaded before the timed region.  The timed region
 replays a HIP graph holding the K steps.
 
 Prints one JSON line (rank 0).  Default workload: the 48-layer x 512-expert
-2-bit decode stack, one token per step.
+2-bit decode stack, one token per step.  `--workload prefill` measures the
+matrix-core path instead: a step is the 4,096-token prompt through all 4
+layers (256 experts, top-8, H 7168, FF 2048, 4-bit), launched eagerly with HIP
+events at every kernel boundary, reported as prompt tokens/s and as the
+dominant kernel's algorithmic TFLOP/s against the dense bf16 MFMA peak.
 """
 import argparse
 import json
@@ -23,7 +27,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE decode tokens/s (expert stack) + achieved HBM GB/s as % of 8 TB/s"
+PREFILL_METRIC = "MoE prefill prompt tokens/s + grouped-GEMM TFLOP/s as % of dense bf16 MFMA peak"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_KERNELS = ["route_topk_kernel", "prefill_count_kernel", "prefill_place_kernel", "prefill_gateup_kernel",
+                   "prefill_down_kernel", "prefill_combine_kernel"]
 
 
 def log(msg):
@@ -50,9 +58,10 @@ def kernel_source_hash():
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE, each scaled by a copy-kernel calibration), or
-    None when the kernel sources changed since the counters were taken."""
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by a copy-kernel
+    calibration), or None when the kernel sources changed since the counters
+    were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -93,11 +102,194 @@ def cpu_baseline(w, x_host, l_host, budget_s=12.0):
                       f"float64 oracle single-threaded, {t_total:.1f} s"}, ref
 
 
+def prefill_flops(w, n_slots, T):
+    """Algorithmic flops of one layer's two grouped GEMM stages: gate and up are
+    2 x (H x FF) multiply-adds per routed slot, down one more (plus the shared
+    expert's per token)."""
+    gu = 2 * 2 * w.hidden * (w.ff * n_slots + w.shared_ff * T)
+    dn = 2 * w.hidden * (w.ff * n_slots + w.shared_ff * T)
+    return gu, dn
+
+
+def prefill_cpu_baseline(w, x0, l0, got, budget_s=12.0):
+    """The float64 oracle, single-threaded, on a bounded sample: the first
+    tokens of layer 0, step 0 (each token's routing and experts are independent
+    of the other tokens), until the budget is spent.  Also returns the GPU
+    output's max |err| / rms on the sampled tokens."""
+    import oracle
+    import synth
+    from synth import workloads as wl
+    zero = np.zeros(w.blob_bytes, dtype=np.uint8)
+    cache = {}
+    t_total, n, errs, refs = 0.0, 0, [], []
+    chunk = 2
+    while t_total < budget_s and n + chunk <= w.tokens:
+        x = x0[n:n + chunk]
+        lg = l0[n:n + chunk]
+        ids_ref, _ = oracle.route_topk(lg, w.top_k)
+        for e in set(ids_ref.reshape(-1).tolist()):
+            if e not in cache:
+                cache[e] = synth.expert_blob(w.seed, 0, e, w.qk, w.hidden, w.ff, w.sigma)
+        table = [cache.get(e, zero) for e in range(w.experts)]
+        t0 = time.perf_counter()
+        y, _, _ = oracle.layer_forward(table, w.top_k, w.qtype, w.zero_point, w.hidden, w.ff, x, lg,
+                                       shared=wl.host_shared_blob(w, 0), shared_ff=w.shared_ff)
+        t_total += time.perf_counter() - t0
+        refs.append(y)
+        errs.append(np.max(np.abs(got[n:n + chunk] - y)))
+        n += chunk
+    ref = np.concatenate(refs)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return ({"value": n / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+             "sample": f"first {n} of the {w.tokens} prompt tokens of layer 0 (routing, {w.top_k} experts each, "
+                       f"SwiGLU, combine), float64 oracle single-threaded, {t_total:.1f} s"},
+            float(max(errs)) / rms, n)
+
+
+def bench_prefill(args, w):
+    import torch
+
+    import bit_expert_ffn_amd as moe
+    from synth import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K = args.steps if args.steps is not None else 10
+    W = args.warmup if args.warmup is not None else 2
+    nsteps = K + W
+    t0 = time.time()
+    arena = wl.DeviceArena(w, device=dev, progress=lambda l: log(f"arena layer {l + 1}/{w.layers}"))
+    log(f"arena ready: {w.layers} x {w.experts} x {w.blob_bytes} B in {time.time() - t0:.1f} s")
+
+    x_dt = torch.bfloat16 if w.x_dtype == "bf16" else torch.float32
+    xs = torch.empty((nsteps, w.layers, w.tokens, w.hidden), dtype=x_dt, device=dev)
+    lg = torch.empty((nsteps, w.layers, w.tokens, w.experts), dtype=torch.float32, device=dev)
+    x0 = l0 = None
+    for s in range(nsteps):
+        for l in range(w.layers):
+            xh, lh = wl.host_inputs(w, l, s)
+            if s == W and l == 0:
+                x0, l0 = xh, lh
+            xs[s, l].copy_(torch.from_numpy(xh.view(np.int16)).view(torch.bfloat16) if w.x_dtype == "bf16"
+                           else torch.from_numpy(xh))
+            lg[s, l].copy_(torch.from_numpy(lh))
+    log(f"inputs resident: {nsteps} steps x {w.layers} layers x {w.tokens} tokens")
+
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k, shared_ff=w.shared_ff)
+    ws = moe.workspace(moe.layer_workspace_bytes(desc, w.tokens), dev)
+    y = torch.empty((2, w.tokens, w.hidden), dtype=torch.float32, device=dev)
+    y_first = torch.empty((w.tokens, w.hidden), dtype=torch.float32, device=dev)
+    ids = torch.empty((nsteps, w.layers, w.tokens, w.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((nsteps, w.layers, w.tokens, w.top_k), dtype=torch.float32, device=dev)
+    nk = len(PREFILL_KERNELS)
+    stream = torch.cuda.Stream()
+    # One event per kernel boundary of every timed layer call; each is recorded
+    # once up front so that its HIP event exists before the library records it.
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(w.layers)]
+           for _ in range(K)]
+    with torch.cuda.stream(stream):
+        for a in evs:
+            for b in a:
+                for e in b:
+                    e.record(stream)
+
+    def layer(s, l, events=None):
+        out = y_first if (s == W and l == 0) else y[l % 2]
+        if events is None:
+            moe.layer_forward(desc, arena.tables[l], xs[s, l], lg[s, l], shared=arena.shared_blob(l), y=out,
+                              ids=ids[s, l], weights=wts[s, l], ws=ws, stream=stream)
+        else:
+            _, n = moe.layer_forward_timed(desc, arena.tables[l], xs[s, l], lg[s, l], events,
+                                           shared=arena.shared_blob(l), y=out, ids=ids[s, l], weights=wts[s, l],
+                                           ws=ws, stream=stream)
+            assert n == nk, n
+
+    with torch.cuda.stream(stream):
+        for s in range(W):
+            for l in range(w.layers):
+                layer(s, l)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for i, s in enumerate(range(W, nsteps)):
+            for l in range(w.layers):
+                layer(s, l, evs[i][l])
+            log(f"step {i + 1}/{K} enqueued")
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / K
+    tok_s = K * w.tokens / (ms_total / 1e3)
+
+    # Per-kernel durations over the timed region, from the boundary events.
+    dur = np.zeros((K, w.layers, nk))
+    for i in range(K):
+        for l in range(w.layers):
+            for j in range(nk):
+                dur[i, l, j] = evs[i][l][j].elapsed_time(evs[i][l][j + 1])
+    avg_ms = dur.mean(axis=(0, 1))
+    n_slots = w.tokens * w.top_k
+    gu, dn = prefill_flops(w, n_slots, w.tokens)
+    layer_flops = gu + dn
+    step_tflops = w.layers * layer_flops / (ms_step / 1e3) / 1e12
+    stages = {}
+    for j, name in enumerate(PREFILL_KERNELS):
+        st = {"avg_us": round(avg_ms[j] * 1e3, 2), "share": round(float(avg_ms[j] / avg_ms.sum()), 4)}
+        if name == "prefill_gateup_kernel":
+            st["tflops"] = round(gu / (avg_ms[j] / 1e3) / 1e12, 1)
+        if name == "prefill_down_kernel":
+            st["tflops"] = round(dn / (avg_ms[j] / 1e3) / 1e12, 1)
+        stages[name] = st
+    j_dom = 3 if avg_ms[3] >= avg_ms[4] else 4
+    dom = PREFILL_KERNELS[j_dom]
+    dom_flops = gu if j_dom == 3 else dn
+    achieved = dom_flops / (avg_ms[j_dom] / 1e3) / 1e12
+
+    ids_np = ids[W:].cpu().numpy()
+    uniq = float(np.mean([len(np.unique(ids_np[i, l])) for i in range(K) for l in range(w.layers)]))
+    # Algorithmic HBM bytes of the dominant kernel: the weights it multiplies
+    # (gate+up, or down, of every expert with tokens) once, its gathered inputs
+    # once, its outputs once.
+    mat_bytes = w.blob_bytes // 3
+    if j_dom == 3:
+        dom_bytes = uniq * 2 * mat_bytes + n_slots * w.hidden * 2 + n_slots * w.ff * 4
+    else:
+        dom_bytes = uniq * mat_bytes + n_slots * w.ff * 4 + n_slots * w.hidden * 4
+
+    result = {
+        "metric": PREFILL_METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "experts": w.experts, "hidden": w.hidden, "ff": w.ff,
+                   "top_k": w.top_k, "tokens_per_step": w.tokens, "format": "4-bit/32 + fp16 scale"
+                   if w.qtype == 2 else "2-bit/64 + fp16 scale", "shared_ff": w.shared_ff, "graph": False},
+        "step_tflops": round(step_tflops, 1), "mfma_frac_step": round(step_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "flops_per_layer": int(layer_flops), "distinct_experts_per_layer": round(uniq, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name), "kernel": dom,
+                     "launch_us": round(avg_ms[j_dom] * 1e3, 2), "flops_per_launch": int(dom_flops),
+                     "bytes_per_launch": int(dom_bytes)},
+        "stages": stages,
+        "wall_s": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        got = y_first.cpu().numpy()
+        base, err, n = prefill_cpu_baseline(w, x0, l0, got)
+        result["cpu_baseline"] = base
+        result["parity_max_err_over_rms"] = err
+        result["parity_tokens"] = n
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50 decode, 10 prefill)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5 decode, 2 prefill)")
     ap.add_argument("--workload", default="strata_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
@@ -129,10 +321,12 @@ def main():
 
     w = wl.WORKLOADS[args.workload]
     if w.tokens > 8:
-        raise SystemExit("prefill workloads are measured by bench_prefill (matrix-core path)")
+        bench_prefill(args, w)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    K, W = args.steps, args.warmup
+    K = args.steps if args.steps is not None else 50
+    W = args.warmup if args.warmup is not None else 5
     nsteps = K + W
 
     t0 = time.time()

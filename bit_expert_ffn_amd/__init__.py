@@ -21,7 +21,7 @@ QK = {Q2_64: 64, Q4_32: 32}
 
 # Functions the header declares (the CPU test checks that each is exported).
 EXPORTS = ["moe_expert_blob_bytes", "moe_expert_workspace_bytes", "moe_layer_workspace_bytes", "moe_route_topk",
-           "moe_expert_ffn", "moe_layer_forward", "moe_dequant_matrix", "moe_validate_table", "moe_status_str",
+           "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed", "moe_dequant_matrix", "moe_validate_table", "moe_status_str",
            "moe_last_error"]
 
 
@@ -64,6 +64,9 @@ def lib():
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, sz,
                                         vp]
+        L.moe_layer_forward_timed.restype = ctypes.c_int
+        L.moe_layer_forward_timed.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp, i32, vp, i32, vp, vp, vp, vp,
+                                              sz, vp, vp, i32, ctypes.POINTER(i32)]
         L.moe_dequant_matrix.restype = ctypes.c_int
         L.moe_dequant_matrix.argtypes = [ctypes.POINTER(ExpertDesc), vp, i32, vp, vp]
         L.moe_validate_table.restype = ctypes.c_int
@@ -170,6 +173,28 @@ def layer_forward(desc, table, x, logits, shared=None, y=None, ids=None, weights
                                    _ptr(logits), T, _ptr(y), _ptr(ids), _ptr(weights), _ptr(ws), ws.numel(),
                                    _stream(stream)))
     return y
+
+
+def layer_forward_timed(desc, table, x, logits, events, shared=None, y=None, ids=None, weights=None, ws=None,
+                        stream=None):
+    """layer_forward that also records `events` (torch.cuda.Event objects with
+    timing, each already recorded once so that its HIP event exists) at the
+    kernel boundaries on the launch stream.  Returns (y, number of kernels)."""
+    _need_cuda(table, x, logits, shared, y, ids, weights, ws)
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, desc.expert.hidden), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(layer_workspace_bytes(desc, T), x.device)
+    handles = [e.cuda_event for e in events]
+    if any(h == 0 for h in handles):
+        raise ValueError("record every event once before passing it (torch creates HIP events lazily)")
+    arr = (ctypes.c_void_p * max(1, len(handles)))(*handles)
+    nk = ctypes.c_int32(0)
+    _check(lib().moe_layer_forward_timed(ctypes.byref(desc), _ptr(table), _ptr(shared), _ptr(x), _xdtype(x),
+                                         _ptr(logits), T, _ptr(y), _ptr(ids), _ptr(weights), _ptr(ws), ws.numel(),
+                                         _stream(stream), arr, len(handles), ctypes.byref(nk)))
+    return y, nk.value
 
 
 def dequant_matrix(desc, blob, m, stream=None):

@@ -136,7 +136,7 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
 static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_desc& ed, int FFs,
                             const void* const* table, const void* single, const void* shared, const void* x,
                             int x_dtype, const float* logits, float* y, int32_t* ids_out, float* w_out, void* ws,
-                            size_t ws_bytes, hipStream_t s, bool identity) {
+                            size_t ws_bytes, hipStream_t s, bool identity, StageMarks* marks = nullptr) {
     char* wsb = (char*)ws;
     if (T <= kSmallT) {
         const SmallLayout L = small_layout(T, k, ed.ff, FFs);
@@ -146,14 +146,14 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
         if (g.lds_bytes > 128 * 1024)
             return fail(MOE_ERR_UNSUPPORTED, "decode tile needs %zu bytes of LDS", g.lds_bytes);
         hipError_t e = launch_decode_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm,
-                                           identity ? 1 : 0, ids_out, w_out, L, wsb, y, s);
+                                           identity ? 1 : 0, ids_out, w_out, L, wsb, y, s, marks);
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
         return MOE_OK;
     }
     const LargeLayout L = large_layout(T, k, E, ed.hidden, ed.ff, FFs, ed.qtype);
     if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
     hipError_t e = launch_prefill_layer(table, single, shared, ed.qtype, ed.zero_point, ed.hidden, ed.ff, FFs, x, x_dtype,
-                                        logits, T, E, k, renorm, identity ? 1 : 0, ids_out, w_out, L, wsb, y, s);
+                                        logits, T, E, k, renorm, identity ? 1 : 0, ids_out, w_out, L, wsb, y, s, marks);
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
     return MOE_OK;
 }
@@ -174,9 +174,10 @@ moe_status moe_expert_ffn(const moe_expert_desc* desc, const void* blob, const v
                      ws_bytes, (hipStream_t)stream, true);
 }
 
-moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expert_table, const void* shared_blob,
-                             const void* x, int32_t x_dtype, const float* logits, int32_t T, float* y,
-                             int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
+static moe_status layer_forward_checked(const moe_layer_desc* desc, const void* const* expert_table,
+                                        const void* shared_blob, const void* x, int32_t x_dtype, const float* logits,
+                                        int32_t T, float* y, int32_t* ids_out, float* w_out, void* ws,
+                                        size_t ws_bytes, void* stream, StageMarks* marks) {
     moe_status st = check_layer(desc);
     if (st != MOE_OK) return st;
     if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
@@ -193,7 +194,34 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expe
     if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
     return run_layer(T, desc->n_experts, desc->top_k, desc->renormalize, desc->expert, desc->shared_ff, expert_table,
                      nullptr, shared_blob, x, x_dtype, logits, y, ids_out, w_out, ws, ws_bytes, (hipStream_t)stream,
-                     false);
+                     false, marks);
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expert_table, const void* shared_blob,
+                             const void* x, int32_t x_dtype, const float* logits, int32_t T, float* y,
+                             int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream) {
+    return layer_forward_checked(desc, expert_table, shared_blob, x, x_dtype, logits, T, y, ids_out, w_out, ws,
+                                 ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* const* expert_table,
+                                   const void* shared_blob, const void* x, int32_t x_dtype, const float* logits,
+                                   int32_t T, float* y, int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes,
+                                   void* stream, void* const* events, int32_t n_events, int32_t* n_kernels) {
+    if (n_events < 0 || (n_events > 0 && !events))
+        return fail(MOE_ERR_INVALID_ARG, "events must hold n_events >= 0 entries");
+    for (int i = 0; i < n_events; ++i)
+        if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
+    StageMarks m;
+    m.ev = (const hipEvent_t*)events;
+    m.n = n_events;
+    if (n_kernels) *n_kernels = 0;
+    moe_status st = layer_forward_checked(desc, expert_table, shared_blob, x, x_dtype, logits, T, y, ids_out, w_out, ws,
+                                          ws_bytes, stream, &m);
+    if (st != MOE_OK) return st;
+    if (m.err != hipSuccess) return fail(MOE_ERR_DEVICE, "hipEventRecord: %s", hipGetErrorString(m.err));
+    if (n_kernels) *n_kernels = m.next > 0 ? m.next - 1 : 0;
+    return MOE_OK;
 }
 
 moe_status moe_dequant_matrix(const moe_expert_desc* desc, const void* blob, int32_t m, float* out, void* stream) {

@@ -826,7 +826,7 @@ static hipError_t launch_decode(const GemvShape& g, DecodeParams& p, int x_dtype
 hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, const void* single, const void* shared,
                                const void* x, int x_dtype, const float* logits, int T, int E, int k, int renorm,
                                int identity, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
-                               hipStream_t s) {
+                               hipStream_t s, StageMarks* marks) {
     DecodeParams p{};
     p.table = table;
     p.single = (const uint8_t*)single;
@@ -856,8 +856,14 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
     p.n_gu = g.n_gu;
     p.dn_rows = g.tile_rows_dn;
     p.tiles_dn = g.tiles_dn;
-    if (T == 1) return g.qtype == 1 ? launch_decode<1, 1>(g, p, x_dtype, s) : launch_decode<2, 1>(g, p, x_dtype, s);
-    return g.qtype == 1 ? launch_decode<1, kGroup>(g, p, x_dtype, s) : launch_decode<2, kGroup>(g, p, x_dtype, s);
+    stage_mark(marks, s);
+    hipError_t e;
+    if (T == 1)
+        e = g.qtype == 1 ? launch_decode<1, 1>(g, p, x_dtype, s) : launch_decode<2, 1>(g, p, x_dtype, s);
+    else
+        e = g.qtype == 1 ? launch_decode<1, kGroup>(g, p, x_dtype, s) : launch_decode<2, kGroup>(g, p, x_dtype, s);
+    stage_mark(marks, s);
+    return e;
 }
 
 // ---------------------------------------------------------------------------------------------

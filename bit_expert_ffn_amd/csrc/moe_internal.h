@@ -62,17 +62,33 @@ SmallLayout small_layout(int T, int k, int FF, int FFs);
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype);
 GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k);
 
+// Caller-owned HIP events recorded on the launch stream at kernel boundaries
+// (measurement entry point): boundary 0 before the first kernel, boundary i
+// after the i-th.  Boundaries beyond n are counted but not recorded.
+struct StageMarks {
+    const hipEvent_t* ev = nullptr;
+    int n = 0;
+    int next = 0;
+    hipError_t err = hipSuccess;
+};
+
+inline void stage_mark(StageMarks* m, hipStream_t s) {
+    if (!m) return;
+    if (m->next < m->n && m->err == hipSuccess) m->err = hipEventRecord(m->ev[m->next], s);
+    ++m->next;
+}
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renorm, int* ids, float* w,
                              hipStream_t s);
 hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, const void* single, const void* shared,
                                const void* x, int x_dtype, const float* logits, int T, int E, int k, int renorm,
                                int identity, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
-                               hipStream_t s);
+                               hipStream_t s, StageMarks* marks = nullptr);
 hipError_t launch_prefill_layer(const void* const* table, const void* single, const void* shared, int qtype, float z,
                                 int H, int FF, int FFs, const void* x, int x_dtype, const float* logits, int T, int E,
                                 int k, int renorm, int identity, int* ids_out, float* w_out, const LargeLayout& L,
-                                char* ws, float* y, hipStream_t s);
+                                char* ws, float* y, hipStream_t s, StageMarks* marks = nullptr);
 hipError_t launch_dequant(const void* blob, int qtype, float z, int rows, int cols, size_t plane_offset,
                           float* out, hipStream_t s);
 

@@ -431,7 +431,7 @@ __global__ void __launch_bounds__(256) prefill_combine_kernel(PrefillParams p) {
 hipError_t launch_prefill_layer(const void* const* table, const void* single, const void* shared, int qtype, float z,
                                 int H, int FF, int FFs, const void* x, int x_dtype, const float* logits, int T, int E,
                                 int k, int renorm, int identity, int* ids_out, float* w_out, const LargeLayout& L,
-                                char* ws, float* y, hipStream_t s) {
+                                char* ws, float* y, hipStream_t s, StageMarks* marks) {
     PrefillParams p{};
     p.table = table;
     p.single = (const uint8_t*)single;
@@ -462,28 +462,36 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     p.y = y;
     p.max_tiles = (int)L.max_tiles;
 
+    stage_mark(marks, s);
     if (identity)
         hipLaunchKernelGGL(prefill_identity_kernel, dim3((T + 255) / 256), dim3(256), 0, s, ids, w, T);
     else
         launch_route_topk(logits, T, E, k, renorm, ids, w, s);
+    stage_mark(marks, s);
     hipLaunchKernelGGL(prefill_count_kernel, dim3(1), dim3(1024), 0, s, p);
+    stage_mark(marks, s);
     hipLaunchKernelGGL(prefill_place_kernel, dim3((E + 3) / 4), dim3(256), 0, s, p);
+    stage_mark(marks, s);
     const dim3 g_gu(p.max_tiles, (p.ffmax + 63) / 64), g_dn(p.max_tiles, (H + 63) / 64);
     if (qtype == 2) {
         if (x_dtype == 1)
             hipLaunchKernelGGL((prefill_gateup_kernel<2, 1>), g_gu, dim3(kPrefillThreads), 0, s, p);
         else
             hipLaunchKernelGGL((prefill_gateup_kernel<2, 2>), g_gu, dim3(kPrefillThreads), 0, s, p);
+        stage_mark(marks, s);
         hipLaunchKernelGGL((prefill_down_kernel<2>), g_dn, dim3(kPrefillThreads), 0, s, p);
     } else {
         if (x_dtype == 1)
             hipLaunchKernelGGL((prefill_gateup_kernel<1, 1>), g_gu, dim3(kPrefillThreads), 0, s, p);
         else
             hipLaunchKernelGGL((prefill_gateup_kernel<1, 2>), g_gu, dim3(kPrefillThreads), 0, s, p);
+        stage_mark(marks, s);
         hipLaunchKernelGGL((prefill_down_kernel<1>), g_dn, dim3(kPrefillThreads), 0, s, p);
     }
+    stage_mark(marks, s);
     const size_t n4 = (size_t)T * H / 4;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p);
+    stage_mark(marks, s);
     return hipGetLastError();
 }
 

@@ -155,6 +155,22 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expe
                              int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Measurement variant of moe_layer_forward: the same checks and the same work,
+ * plus caller-created HIP events (hipEvent_t passed as void*, timing enabled)
+ * recorded on `stream` at the boundaries of the kernels the call launches:
+ * events[0] before the first kernel, events[i] after the i-th.  Boundaries
+ * past n_events are not recorded.  *n_kernels (if not NULL) receives the
+ * number of kernels launched: 1 on the decode/verify path (the fused layer
+ * kernel); 6 on the prefill path (routing, expert histogram, slot placement,
+ * gate/up + SwiGLU, down, combine).  Events are not owned by the library.
+ * A failing hipEventRecord returns MOE_ERR_DEVICE after the work is enqueued.
+ */
+moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* const* expert_table,
+                                   const void* shared_blob, const void* x, int32_t x_dtype, const float* logits,
+                                   int32_t T, float* y, int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes,
+                                   void* stream, void* const* events, int32_t n_events, int32_t* n_kernels);
+
+/*
  * Debug: dequantize matrix m (0 gate [FF][H], 1 up [FF][H], 2 down [H][FF]) of
  * a blob to fp32 (exact: an fp16 scale times a small integer offset), row-major.
  */

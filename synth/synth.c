@@ -160,11 +160,31 @@ void synth_f32_normal(uint64_t seed, uint64_t stream, float* out, size_t n) {
     FILL_NORMALS(key, n, (float)z, out);
 }
 
-/* Activations of one layer and step: T x H values, bf16 bits (dtype 1) or fp32 (dtype 0). */
+/* Activations of one layer and step: T x H values, bf16 bits (dtype 1) or fp32
+ * (dtype 0).  Element i of the stream is the i-th normal; threads fill
+ * disjoint, pair-aligned ranges, so the values do not depend on the thread count. */
 void synth_activations(uint64_t seed, uint32_t layer, uint32_t step, int64_t T, int64_t H, int dtype, void* out) {
-    uint64_t st = synth_stream(K_X, layer, step, 0);
-    if (dtype == 1) synth_bf16_normal(seed, st, (uint16_t*)out, (size_t)(T * H));
-    else synth_f32_normal(seed, st, (float*)out, (size_t)(T * H));
+    uint64_t key = stream_key(seed, synth_stream(K_X, layer, step, 0));
+    int64_t n = T * H;
+    int64_t npairs = (n + 1) / 2;
+    const int64_t chunk = 1 << 15;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < (npairs + chunk - 1) / chunk; ++c) {
+        int64_t j1 = (c + 1) * chunk < npairs ? (c + 1) * chunk : npairs;
+        for (int64_t j = c * chunk; j < j1; ++j) {
+            double z0, z1;
+            normal_pair(key, (uint64_t)j, &z0, &z1);
+            if (dtype == 1) {
+                uint16_t* o = (uint16_t*)out;
+                o[2 * j] = synth_double_to_bf16(z0);
+                if (2 * j + 1 < n) o[2 * j + 1] = synth_double_to_bf16(z1);
+            } else {
+                float* o = (float*)out;
+                o[2 * j] = (float)z0;
+                if (2 * j + 1 < n) o[2 * j + 1] = (float)z1;
+            }
+        }
+    }
 }
 
 typedef struct { uint64_t key; int32_t idx; } perm_item;

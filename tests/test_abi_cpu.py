@@ -104,3 +104,21 @@ def test_expert_ffn_rejects_bad_arguments(L):
     assert L.moe_expert_ffn(ctypes.byref(d), p, p, 0, 0, p, p, 0, None) == 0
     assert L.moe_dequant_matrix(ctypes.byref(d), p, 3, p, None) == 1
     assert L.moe_validate_table(None, 4, None) == 1
+
+
+def test_layer_forward_timed_rejects_bad_arguments(L):
+    p = ctypes.c_void_p(FAKE)
+    ok = moe.layer_desc(2560, 640, 1, 1.5, 512, 10)
+    nk = ctypes.c_int32(7)
+
+    def call(events, n, ws_bytes=1 << 30, T=1):
+        return L.moe_layer_forward_timed(ctypes.byref(ok), p, None, p, 1, p, T, p, None, None, p, ws_bytes, None,
+                                         events, n, ctypes.byref(nk))
+
+    assert call(None, 2) == 1                                     # events missing
+    assert call((ctypes.c_void_p * 2)(FAKE, None), 2) == 1        # a NULL event
+    assert call(None, -1) == 1                                    # negative count
+    assert call(None, 0, ws_bytes=16) == 3                        # the layer checks still apply
+    assert nk.value == 0
+    assert call(None, 0, T=0) == 0                                # nothing to do, no kernel
+    assert nk.value == 0

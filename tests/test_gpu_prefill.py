@@ -102,3 +102,29 @@ def test_prefill_full_layer_sampled_tokens():
     y_ref, _, _ = oracle.layer_forward([blobs.get(e, zero) for e in range(w.experts)], w.top_k, w.qtype,
                                        w.zero_point, w.hidden, w.ff, hx[sample], hl[sample])
     assert max_err_over_rms(y.cpu().numpy()[sample], y_ref) <= TOL
+
+
+@pytest.mark.parametrize("T,expect", [(3, 1), (150, 6)])
+def test_timed_entry_point_matches_and_records(T, expect):
+    """moe_layer_forward_timed does the same work as moe_layer_forward (bitwise
+    equal outputs) and records one event per kernel boundary, in order."""
+    E, k, H, FF = 16, 4, 256, 128
+    blobs = synth.expert_blobs(9, 0, 0, E, 32, H, FF, 0.02)
+    x = synth.activations(9, 0, 0, T, H, "bf16")
+    logits = synth.logits(9, 0, 0, T, E, 0.6)
+    dev = torch.from_numpy(blobs).to(DEV)
+    table = torch.tensor([dev.data_ptr() + e * blobs.shape[1] for e in range(E)], dtype=torch.int64, device=DEV)
+    desc = moe.layer_desc(H, FF, 2, 7.5, E, k)
+    xt, lt = _x_tensor(x), torch.from_numpy(logits).to(DEV)
+    ws = moe.workspace(moe.layer_workspace_bytes(desc, T), DEV)
+    y0 = moe.layer_forward(desc, table, xt, lt, ws=ws)
+    s = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for e in evs:
+        e.record(s)
+    y1, n = moe.layer_forward_timed(desc, table, xt, lt, evs, ws=ws)
+    torch.cuda.synchronize()
+    assert n == expect
+    np.testing.assert_array_equal(y0.cpu().numpy(), y1.cpu().numpy())
+    times = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+    assert all(t >= 0.0 for t in times) and evs[0].elapsed_time(evs[n]) > 0.0
