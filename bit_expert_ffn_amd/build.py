@@ -12,6 +12,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off",                       # every fused multiply-add is written explicitly
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",         # MFMA results in VGPRs: no accumulator-register copies
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -58,6 +58,9 @@ static moe_status check_expert(const moe_expert_desc* d, const char* what) {
                     d->ff, qk);
     if (d->act != MOE_ACT_SWIGLU) return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d not supported", what, d->act);
     if (!isfinite(d->zero_point)) return fail(MOE_ERR_INVALID_ARG, "%s: zero_point is not finite", what);
+    if (fabsf(d->zero_point) > 64.f || d->zero_point * 2.f != floorf(d->zero_point * 2.f))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: zero_point %g is not a multiple of 0.5 in [-64, 64]", what,
+                    (double)d->zero_point);
     if (d->hidden / qk > kMaxBlocksPerRow || d->ff / qk > kMaxBlocksPerRow)
         return fail(MOE_ERR_UNSUPPORTED, "%s: more than %d blocks per row", what, kMaxBlocksPerRow);
     return MOE_OK;

@@ -47,6 +47,15 @@ __device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) {
     return o < v ? o : v;
 }
 
+// (d & mask) | v in one v_and_or_b32.  gfx9 VOP3 encodings take no literal
+// operands, so the mask goes in an SGPR and the OR value in a VGPR; written as
+// plain C the compiler splits it into two instructions.
+__device__ __forceinline__ uint32_t and_or(uint32_t d, uint32_t mask, uint32_t v) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(d), "s"(mask), "v"(v));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }

@@ -55,14 +55,6 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 
 constexpr uint32_t kMagic = 0x43004300u;   // bf16 pair (128.0, 128.0)
 
-// (d & mask) | magic in one v_and_or_b32.  gfx9 VOP3 encodings take no literal
-// constant and one scalar operand, so the mask goes in an SGPR and the magic
-// in a VGPR (left to itself the compiler emits an AND and an OR).
-__device__ __forceinline__ uint32_t and_or(uint32_t d, uint32_t mask, uint32_t magic_v) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(d), "s"(mask), "v"(magic_v));
-    return r;
-}
 
 __device__ __forceinline__ uint32_t magic_vgpr() {
     uint32_t m;

@@ -9,35 +9,54 @@
 //   2. count    : per-expert counts, offsets and a list of row tiles (<= 128
 //                 (token, slot) rows of one expert each).
 //   3. place    : one wave per expert scans the pairs in (token, slot) order and
-//                 writes the sorted position of each (a stable counting sort).
-//   4. gate/up  : per row tile and 64 FF features, G = X W_g^T and U = X W_u^T
+//                 writes the sorted position of each (a stable counting sort);
+//                 the same launch converts the activations (step 3b).
+//   3b. xprep   : each token's activations as fp16 times a power of two.
+//   4. gate/up  : per row tile and 128 features, G = X W_g^T and U = X W_u^T
 //                 on MFMA, then a = silu(G) * U, stored as bf16 hi + lo.
-//   5. down     : per row tile and 64 H features, Y = a W_d^T on MFMA.
+//   5. down     : per row tile and 256 outputs, Y = a W_d^T on MFMA.
 //   6. combine  : y[t] = shared(t) + sum_j w[t][j] * Y[pair(t, j)], fixed order.
 //
-// Exactness on bf16 MFMA.  A dequantised weight w = s * (c - z) (fp16 scale,
-// code offset of at most 5 significant bits) has at most 16 significant bits,
-// so w = hi + lo with hi = its bf16 truncation and lo = w - hi, both exact
-// bf16.  Activations are exact bf16 (fp32 inputs and the SwiGLU output are
-// split into hi + lo the same way, relative error <= 2^-17).  Gate/up take two
-// MFMAs per tile (x * w_hi + x * w_lo), down three (a_hi w_hi + a_hi w_lo +
-// a_lo w_hi; the dropped a_lo w_lo is below 2^-16 relative).  Products are
-// exact and accumulate in fp32 inside the MFMA across the whole K loop, so no
-// per-block scaling pass is needed.
+// Exact operands.  A weight is w = s * (c - z): an fp16 block scale s times a
+// small half-integer c - z.  The matrix cores multiply by 2(c - z), an exact
+// small integer, and the scale is applied once per block and output element in
+// fp32 (acc += (s / 2) * P_block), so no weight is ever rounded.
+//   gate/up: fp16 MFMA.  x * 2^-e (one e per token, 0 unless |x| >= 2^15) is
+//     exact in fp16 for bf16 input (fp32 input: hi + lo, two MFMA passes); the
+//     weight operand 2c - 2z comes from OR-ing the code into the mantissa of
+//     1024.0 and one packed fp16 subtraction per two weights.
+//   down: bf16 MFMA.  a is split into bf16 hi + lo (16 significant bits, two
+//     MFMA passes); the weight operand c - z is converted through fp32.
+// Products are exact and accumulate in fp32 inside each block.
 //
-// MFMA v_mfma_f32_16x16x32_bf16, lane l: A row l%16 and B column l%16 hold
-// K elements 8*(l/16) .. +7; D column l%16 holds rows 4*(l/16) .. +3.
+// MFMA v_mfma_f32_32x32x16_{f16,bf16}, lane l: A row l%32 and B column l%32
+// hold K elements 8*(l/32) .. +7; D column l%32 holds rows 8*(i/4) + 4*(l/32)
+// + i%4 in register i.  Within a block, lane half h and K step s take codes
+// QK/2*h + 8s .. +7 (any K order works when A and B agree on it).
+//
+// Tiles are mapped to workgroups so that each XCD (8 of them, workgroups
+// dealt round-robin) runs a contiguous run of (row tile, column group) pairs:
+// the column groups of one row tile share its activation rows in that XCD's L2.
+#include <string.h>
+
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kRowsPerTile = 128;          // (token, slot) rows per tile
-constexpr int kRowTiles = kRowsPerTile / 16;
-constexpr int kPrefillThreads = 256;       // 4 waves, 16 output features each
+constexpr int kPrefillThreads = 256;       // 4 waves
+constexpr int kGuThreads = 512;            // gate/up workgroup: 8 waves
+constexpr int kGuFeatures = 256;           // features per gate/up workgroup (32 per wave)
+constexpr int kDnThreads = 512;            // down workgroup: 8 waves
+constexpr int kDnCols = 512;               // outputs per down workgroup (64 per wave)
 
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype) {
     LargeLayout L{};
@@ -47,7 +66,7 @@ LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype)
         off = (off + b + 255) & ~(size_t)255;
         return o;
     };
-    const int qk = codes_per_block(qtype);
+    (void)qtype;
     const size_t n = (size_t)T * k;
     const size_t P = n + (FFs ? (size_t)T : 0);
     const int ffmax = FFs > FF ? FFs : FF;
@@ -60,11 +79,12 @@ LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype)
     L.ntiles = take(4);
     L.perm = take(P * 4);                // sorted row -> token
     L.inv = take(n * 4);                 // (token, slot) -> sorted row
-    L.a = take(P * ffmax * 2 * 2);       // a_hi then a_lo planes, bf16
+    L.xq = take((size_t)2 * T * H * 2 + 256);   // + slack: the last chunk of the last row reads past H
+    L.xe = take((size_t)T * 4);
+    L.a = take(P * ffmax * 2 * 2 + 256); // a_hi then a_lo planes, bf16 (+ slack as for xq)
     L.ypair = take(P * (size_t)H * 4);
     L.max_tiles = max_tiles;
     L.total = off;
-    (void)qk;
     return L;
 }
 
@@ -75,6 +95,7 @@ struct PrefillParams {
     const void* x;            // [T][H]
     int T, E, k, H, FF, FFs, ffmax;
     float z;
+    uint32_t zc16;            // fp16 pair (-(1024 + 2z), -(1024 + 2z))
     const int* ids;
     const float* w;
     int* counts;
@@ -83,6 +104,8 @@ struct PrefillParams {
     int* ntiles;
     int* perm;
     int* inv;
+    uint16_t* xq;             // [2][T][H] fp16
+    int* xe;                  // [T]
     uint16_t* a_hi;
     uint16_t* a_lo;
     float* ypair;
@@ -171,45 +194,67 @@ __global__ void prefill_identity_kernel(int* ids, float* w, int T) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Operand helpers.
+// Activations to fp16.  One workgroup per token: e = max(0, floor(log2 max|x|) - 14)
+// keeps x * 2^-e below 2^15.  Within each group of G = 8 (4-bit) or 16 (2-bit)
+// values, position 2q + r holds value q + r*G/2: the order in which the
+// dequantised weight pairs come out of one code word.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
-// 8 dequantised weights w_j = s * (c_j - z) as two exact bf16 terms (hi = the
-// truncation, lo = the rest), K order j = 0..7.
-__device__ __forceinline__ void weights_hi_lo(const float (&c)[8], float s, float zs, bf16x8_t& hi, bf16x8_t& lo) {
-    uint32_t wb[8], lb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float w = __builtin_fmaf(c[j], s, -zs);                 // exact: <= 16 significant bits
-        wb[j] = __float_as_uint(w);
-        lb[j] = __float_as_uint(w - __uint_as_float(wb[j] & 0xFFFF0000u));   // exact remainder, <= 8 bits
-    }
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[i] = pack_hi16(wb[2 * i], wb[2 * i + 1]);
-        l[i] = pack_hi16(lb[2 * i], lb[2 * i + 1]);
-    }
-    hi = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(h));
-    lo = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(l));
+template <int XDT>
+__device__ __forceinline__ float load_x(const void* x, size_t i) {
+    if constexpr (XDT == 1) return __uint_as_float((uint32_t)((const uint16_t*)x)[i] << 16);
+    else return ((const float*)x)[i];
 }
 
-// Codes k = 8*kq .. 8*kq+7 of one 32-wide K step of a block, as floats.
-template <int QT>
-__device__ __forceinline__ void codes8(const uint8_t* chunk, int step, int kq, float (&c)[8]) {
-    if constexpr (QT == 2) {   // 4-bit: one block = one K step; dword kq holds codes 8kq .. 8kq+7
-        const uint32_t d = *reinterpret_cast<const uint32_t*>(chunk + 4 * kq);
+template <int QT, int XDT>
+__global__ void __launch_bounds__(256) prefill_xprep_kernel(PrefillParams p) {
+    constexpr int G = QT == 1 ? 16 : 8;
+    __shared__ uint32_t red[4];
+    const int t = blockIdx.x;
+    const int H = p.H;
+    const size_t base = (size_t)t * H;
+    uint32_t mx = 0;   // |x| bit patterns order like their values (NaN above every number)
+    for (int i = threadIdx.x; i < H; i += 256) {
+        const uint32_t b = __float_as_uint(load_x<XDT>(p.x, base + i)) & 0x7FFFFFFFu;
+        mx = b > mx ? b : mx;
+    }
+    mx = wave_max_u32(mx);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+    const int eb = (int)(mx >> 23);
+    const int e = (mx < 0x7F800000u && eb > 141) ? eb - 141 : 0;
+    if (threadIdx.x == 0) p.xe[t] = e;
+    _Float16* hi = (_Float16*)p.xq + base;
+    _Float16* lo = (_Float16*)p.xq + (size_t)p.T * H + base;
+    for (int g = threadIdx.x; g < H / G; g += 256) {
+        float v[G];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = (float)((d >> (4 * j)) & 15u);
-    } else {                   // 2-bit: 64 codes = two K steps; codes 32*step + 8*kq .. in dword 2*step + kq/2
-        const uint32_t d = *reinterpret_cast<const uint32_t*>(chunk + 4 * (2 * step + kq / 2));
-        const int sh = 16 * (kq & 1);
+        for (int i = 0; i < G; ++i) v[i] = __builtin_ldexpf(load_x<XDT>(p.x, base + (size_t)g * G + i), -e);
+        _Float16 oh[G], ol[G];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = (float)((d >> (sh + 2 * j)) & 3u);
+        for (int q = 0; q < G / 2; ++q) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const float f = v[q + r * (G / 2)];
+                const _Float16 h = (_Float16)f;
+                oh[2 * q + r] = h;
+                ol[2 * q + r] = (_Float16)(f - (float)h);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < G; i += 8) {
+            *reinterpret_cast<f16x8_t*>(hi + (size_t)g * G + i) =
+                f16x8_t{oh[i], oh[i + 1], oh[i + 2], oh[i + 3], oh[i + 4], oh[i + 5], oh[i + 6], oh[i + 7]};
+            if constexpr (XDT == 0)
+                *reinterpret_cast<f16x8_t*>(lo + (size_t)g * G + i) =
+                    f16x8_t{ol[i], ol[i + 1], ol[i + 2], ol[i + 3], ol[i + 4], ol[i + 5], ol[i + 6], ol[i + 7]};
+        }
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Shared pieces of the two GEMM kernels.
+// ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float half_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
@@ -217,192 +262,478 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+
+// Direct global -> LDS copy of 16 bytes per lane; lane i lands at dst + 16 i.
+__device__ __forceinline__ void load_lds16(const void* src, uint8_t* dst_wave) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst_wave, 16, 0, 0);
+}
+
+// A load the compiler knows reads global memory (a pointer taken from the
+// expert table is otherwise generic, and a generic load could read LDS, which
+// would make it wait for the LDS copies in flight).
+__device__ __forceinline__ uint32_t ldg_u16(const uint8_t* base, uint32_t off) {
+    return *(const __attribute__((address_space(1))) uint16_t*)(base + off);
+}
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// XCD-contiguous mapping of the 1-D grid onto n logical work items; -1 = no work.
+__device__ __forceinline__ int xcd_item(int n) {
+    const int per = (n + 7) >> 3;
+    const int j = (int)(blockIdx.x >> 3);
+    if (j >= per) return -1;
+    const int L = (int)(blockIdx.x & 7) * per + j;
+    return L < n ? L : -1;
+}
+
+// fp16 weight operand 2(c - z) of one K step from one 32-bit code word.
+//   4-bit: word = codes 0..7; pairs (q, q + 4), q = 0..3.
+//   2-bit: word = codes 0..15; step half u takes pairs (q, q + 8), q = 4u .. 4u + 3.
+template <int QT>
+__device__ __forceinline__ f16x8_t weights_f16(uint32_t d, int u, uint32_t magic_v, f16x2_t zc) {
+    uint32_t w[4];
+    if constexpr (QT == 2) {
+        w[0] = and_or(d << 1, 0x001E001Eu, magic_v);
+        w[1] = and_or(d >> 3, 0x001E001Eu, magic_v);
+        w[2] = and_or(d >> 7, 0x001E001Eu, magic_v);
+        w[3] = and_or(d >> 11, 0x001E001Eu, magic_v);
+        (void)u;
+    } else {
+        if (u == 0) {
+            w[0] = and_or(d << 1, 0x00060006u, magic_v);
+            w[1] = and_or(d >> 1, 0x00060006u, magic_v);
+            w[2] = and_or(d >> 3, 0x00060006u, magic_v);
+            w[3] = and_or(d >> 5, 0x00060006u, magic_v);
+        } else {
+            w[0] = and_or(d >> 7, 0x00060006u, magic_v);
+            w[1] = and_or(d >> 9, 0x00060006u, magic_v);
+            w[2] = and_or(d >> 11, 0x00060006u, magic_v);
+            w[3] = and_or(d >> 13, 0x00060006u, magic_v);
+        }
+    }
+    f16x2_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = __builtin_bit_cast(f16x2_t, w[i]) + zc;   // exact: small integers
+    return f16x8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+}
+
+// bf16 weight operand c - z of one K step, natural code order: 8 codes at bits
+// 4j (4-bit) or 2j + shift (2-bit).
+template <int QT>
+__device__ __forceinline__ bf16x8_t weights_bf16(uint32_t d, int u, float z) {
+    float c[8];
+    if constexpr (QT == 2) {
+        const uint32_t lo = d & 0x0F0F0F0Fu, hi = (d >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[2 * i] = (float)((lo >> (8 * i)) & 0xFFu);
+            c[2 * i + 1] = (float)((hi >> (8 * i)) & 0xFFu);
+        }
+    } else {
+        const uint32_t t = d >> (16 * u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t m = (t >> (2 * k)) & 0x03030303u;   // byte i: code 4i + k
+            c[k] = (float)(m & 0xFFu);
+            c[4 + k] = (float)((m >> 8) & 0xFFu);
+        }
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = c[2 * i] - z, b = c[2 * i + 1] - z;   // exact half-integers
+        w[i] = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w));
+}
+
 // ---------------------------------------------------------------------------------------------
-// Gate/up + SwiGLU.
-// grid.x: row tiles, grid.y: groups of 64 FF features (16 per wave).
+// LDS tiles of one K chunk, filled by direct global -> LDS copies (lane i of a
+// copy instruction lands 16 i bytes after the instruction's base):
+//   A: 128 rows of 16 pieces of 16 bytes (K chunk of NTERM planes), row pitch 17
+//      pieces.  16 consecutive rows reading the same piece then start 68 dwords
+//      apart, i.e. on 16 distinct 4-bank groups of the 64 banks.
+//   B: weight rows of BPC code blocks (16 bytes each, a contiguous run in the
+//      blob), row pitch BPITCH pieces (BPC + 1, or 3 for BPC = 1) for the same
+//      reason.  Consecutive lanes copy one row's run.
+// The padding pieces are filled with valid (unused) data, so every lane of every
+// copy instruction is active.  Reads past a row's end in the last, partial
+// chunk stay inside the buffers (slack after the activation planes, the scales
+// plane after the codes) and are never used.
 // ---------------------------------------------------------------------------------------------
+constexpr int kApitch = 17;                           // pieces per A row in LDS
+constexpr int kAbytes = kRowsPerTile * kApitch * 16;  // 34,816
+constexpr int kAcopies = kRowsPerTile * kApitch / 64; // 34 copy instructions per chunk
+static_assert(kRowsPerTile * kApitch % 64 == 0, "A copies cover whole instructions");
+
+__host__ __device__ constexpr int bpitch(int bpc) { return bpc == 1 ? 3 : bpc + 1; }
+
+// Gate/up + SwiGLU.  Workgroup (8 waves, one per CU): one row tile x 256
+// features; wave w owns features 32w .. 32w + 31 of both matrices (NR row
+// sub-tiles x {gate, up} MFMA tiles).  K chunk: 128 / NTERM activations per row
+// (NTERM fp16 planes) and the matching BPC code blocks of the 512 weight rows
+// (gate rows, then up rows); two buffers, one barrier per chunk.
 template <int QT, int NTERM>
-__global__ void __launch_bounds__(kPrefillThreads, 2) prefill_gateup_kernel(PrefillParams p) {
+__global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillParams p) {
     constexpr int QK = QT == 1 ? 64 : 32;
-    constexpr int STEPS = QK / 32;   // 32-wide K steps per block
-    const int tile = blockIdx.x;
-    if (tile >= *p.ntiles) return;
+    constexpr int KC = 128 / NTERM;          // activations per row per chunk
+    constexpr int BPC = KC / QK;             // blocks per chunk
+    constexpr int SPB = QK / 16;             // MFMA K steps per block
+    constexpr int PPP = 16 / NTERM;          // A pieces per plane
+    constexpr int BP = bpitch(BPC);
+    constexpr int BROWS = 2 * kGuFeatures;
+    constexpr int BUF = kAbytes + BROWS * BP * 16;
+    // Two separately declared buffers: the compiler can then tell that reads of
+    // one do not depend on the copies still landing in the other.
+    __shared__ __attribute__((aligned(16))) uint8_t buf0[BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t buf1[BUF];
+    __shared__ __attribute__((aligned(16))) int s_e[kRowsPerTile];
+    const int nft = (p.ffmax + kGuFeatures - 1) / kGuFeatures;
+    const int item = xcd_item(*p.ntiles * nft);
+    if (item < 0) return;
+    const int tile = item / nft, ft = item - tile * nft;
     const int* td = p.tiles + 3 * tile;
     const int e = td[0], row0 = td[1], nrows = td[2];
     const bool sh = e == p.E;
     const int FFe = sh ? p.FFs : p.FF;
-    const int f0 = blockIdx.y * 64;
+    const int f0 = ft * kGuFeatures;
     if (f0 >= FFe) return;
     const uint8_t* blob = sh ? p.shared : (p.table ? (const uint8_t*)p.table[e] : p.single);
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int col = lane & 15, kq = lane >> 4;
-    const int f = min(f0 + 16 * wv + col, FFe - 1);
-    const int nblk = p.H / QK;
+    const int H = p.H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+    const int nblk = H / QK;
     const size_t plane = (size_t)FFe * nblk;
-    const uint8_t* gcode = blob + (size_t)f * nblk * 16;
-    const uint8_t* gscale = blob + plane * 16 + (size_t)f * nblk * 2;
-    const uint8_t* ucode = blob + plane * 18 + (size_t)f * nblk * 16;
-    const uint8_t* uscale = blob + plane * 18 + plane * 16 + (size_t)f * nblk * 2;
-    const int nrt = (nrows + 15) / 16;
+    if (tid < kRowsPerTile) s_e[tid] = p.xe[p.perm[row0 + min(tid, nrows - 1)]];
 
-    // Tokens of this lane's A rows (row tile r, row l%16); rows past the tile repeat its last row.
-    int tok[kRowTiles];
+    // A copies: wave w issues copies g = w + 8 j (g < 34); piece 64 g + lane is
+    // row / 17, piece % 17 (piece 16: padding, copies piece 0 again).
+    constexpr int AJ = (kAcopies + 7) / 8;
+    uint32_t xoff[AJ];
 #pragma unroll
-    for (int r = 0; r < kRowTiles; ++r) tok[r] = p.perm[row0 + min(16 * r + col, nrows - 1)];
-
-    f32x4_t accg[kRowTiles], accu[kRowTiles];
-#pragma unroll
-    for (int r = 0; r < kRowTiles; ++r) {
-        accg[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        accu[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < AJ; ++j) {
+        const int P = 64 * (wv + 8 * j) + lane;
+        const int row = min(P / kApitch, kRowsPerTile - 1), pc = P % kApitch;
+        const int q = pc == 16 ? 0 : pc;
+        xoff[j] = (uint32_t)((q / PPP) * p.T * H + p.perm[row0 + min(row, nrows - 1)] * H + 8 * (q % PPP));
     }
+    // B copies: wave w fills rows 64 w .. 64 w + 63 with BP copies; piece 64 j + lane
+    // of the wave is row 64 w + (64 j + lane) / BP, piece (64 j + lane) % BP.
+    uint32_t boff[BP];
+#pragma unroll
+    for (int j = 0; j < BP; ++j) {
+        const int L = 64 * j + lane;
+        const int row = 64 * wv + L / BP, pc = L % BP;
+        const int m = row / kGuFeatures, fr = min(f0 + row % kGuFeatures, FFe - 1);
+        boff[j] = (uint32_t)(m * plane * 18 + ((size_t)fr * nblk + (pc < BPC ? pc : 0)) * 16);
+    }
+    const uint8_t* xq = (const uint8_t*)p.xq;
+    auto issue = [&](int c, uint8_t* buf) {
+        const uint32_t k0 = (uint32_t)(c * KC);
+#pragma unroll
+        for (int j = 0; j < AJ; ++j)
+            if (wv + 8 * j < kAcopies) load_lds16(xq + 2 * (xoff[j] + k0), buf + 1024 * (wv + 8 * j));
+        const uint32_t kb = (uint32_t)(c * BPC * 16);
+#pragma unroll
+        for (int j = 0; j < BP; ++j) load_lds16(blob + (boff[j] + kb), buf + kAbytes + (64 * wv * BP + 64 * j) * 16);
+    };
+    // Scales of this lane's gate and up rows, one chunk ahead in registers.
+    const int fl = min(f0 + 32 * wv + col, FFe - 1);
+    const uint32_t gsoff = (uint32_t)(plane * 16 + (size_t)fl * nblk * 2);
+    const uint32_t usoff = gsoff + (uint32_t)(plane * 18);
+    uint32_t nsg[BPC], nsu[BPC];
+    auto load_s = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < BPC; ++i) {
+            const uint32_t blk = (uint32_t)min(c * BPC + i, nblk - 1);
+            nsg[i] = ldg_u16(blob, gsoff + 2 * blk);
+            nsu[i] = ldg_u16(blob, usoff + 2 * blk);
+        }
+    };
+    // This lane's LDS read bases: A row col (+ 32 r rows), B rows of its features.
+    const uint32_t a_base = (uint32_t)(col * kApitch * 16 + (QK / 2) * hh * 2);
+    const uint32_t g_base = (uint32_t)(kAbytes + (32 * wv + col) * BP * 16);
+    const uint32_t u_base = g_base + (uint32_t)(kGuFeatures * BP * 16);
 
-    for (int b = 0; b < nblk; ++b) {
-        const float sg = half_to_f32(*reinterpret_cast<const uint16_t*>(gscale + 2 * b));
-        const float su = half_to_f32(*reinterpret_cast<const uint16_t*>(uscale + 2 * b));
+    // The chunk loop and epilogue, specialised on the number NR of 32-row MFMA
+    // sub-tiles that hold rows (a tile of n rows needs ceil(n / 32)).
+    auto run = [&](auto nr_c) {
+        constexpr int NR = decltype(nr_c)::value;
+        f32x16_t accg[NR], accu[NR];
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            float cg[8], cu[8];
-            codes8<QT>(gcode + 16 * b, st, kq, cg);
-            codes8<QT>(ucode + 16 * b, st, kq, cu);
-            bf16x8_t bgh, bgl, buh, bul;
-            weights_hi_lo(cg, sg, p.z * sg, bgh, bgl);
-            weights_hi_lo(cu, su, p.z * su, buh, bul);
-            const int k0 = QK * b + 32 * st + 8 * kq;
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int r = 0; r < kRowTiles; ++r) {
-                if (r < nrt) {
-                    if constexpr (NTERM == 1) {
-                        const uint4 xv = *reinterpret_cast<const uint4*>((const uint16_t*)p.x + (size_t)tok[r] * p.H + k0);
-                        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xv);
-                        accg[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bgh, accg[r], 0, 0, 0);
-                        accg[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bgl, accg[r], 0, 0, 0);
-                        accu[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, buh, accu[r], 0, 0, 0);
-                        accu[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bul, accu[r], 0, 0, 0);
-                    } else {
-                        // fp32 activations: two bf16 terms (hi + lo); x_lo * w_lo is dropped (< 2^-16).
-                        const float* xs = (const float*)p.x + (size_t)tok[r] * p.H + k0;
-                        const float4 v0 = *reinterpret_cast<const float4*>(xs);
-                        const float4 v1 = *reinterpret_cast<const float4*>(xs + 4);
-                        const float xv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                        uint32_t hb[8], lb[8];
+            for (int i = 0; i < 16; ++i) {
+                accg[r][i] = 0.f;
+                accu[r][i] = 0.f;
+            }
+        const uint32_t magic_v = [] {
+            uint32_t m;
+            asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+            return m;
+        }();
+        const f16x2_t zc = __builtin_bit_cast(f16x2_t, p.zc16);
+        const f32x16_t zero = {};
+        const int nchunks = (H + KC - 1) / KC;
+        auto chunk = [&](int c, const uint8_t* buf, uint8_t* next) {
+            wait_loads();
+            __syncthreads();
+            float fg[BPC], fu[BPC];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            hb[j] = __float_as_uint(xv[j]) & 0xFFFF0000u;
-                            lb[j] = __float_as_uint(xv[j] - __uint_as_float(hb[j]));
+            for (int i = 0; i < BPC; ++i) {
+                fg[i] = 0.5f * half_to_f32((uint16_t)nsg[i]);
+                fu[i] = 0.5f * half_to_f32((uint16_t)nsu[i]);
+            }
+            if (c + 1 < nchunks) {
+                issue(c + 1, next);
+                load_s(c + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < BPC; ++i) {
+                if (c * BPC + i >= nblk) break;
+                const uint4 g4 = *reinterpret_cast<const uint4*>(buf + g_base + i * 16);
+                const uint4 u4 = *reinterpret_cast<const uint4*>(buf + u_base + i * 16);
+                const uint32_t gw[2] = {hh ? g4.z : g4.x, hh ? g4.w : g4.y};   // bytes 8 hh .. 8 hh + 7
+                const uint32_t uw[2] = {hh ? u4.z : u4.x, hh ? u4.w : u4.y};
+                f16x8_t wg[SPB], wu[SPB];
+#pragma unroll
+                for (int s = 0; s < SPB; ++s) {
+                    const int wd = (QT == 2) ? s : (s >> 1);
+                    wg[s] = weights_f16<QT>(gw[wd], s & 1, magic_v, zc);
+                    wu[s] = weights_f16<QT>(uw[wd], s & 1, magic_v, zc);
+                }
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    f32x16_t pg = zero, pu = zero;
+#pragma unroll
+                    for (int s = 0; s < SPB; ++s) {
+#pragma unroll
+                        for (int t = 0; t < NTERM; ++t) {
+                            // activations K = QK i + QK/2 hh + 8 s of plane t (hh is in a_base)
+                            const int off = 32 * r * kApitch * 16 + (PPP * t + (i * QK + 8 * s) / 8) * 16;
+                            const f16x8_t av = *reinterpret_cast<const f16x8_t*>(buf + a_base + off);
+                            pg = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, wg[s], pg, 0, 0, 0);
+                            pu = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, wu[s], pu, 0, 0, 0);
                         }
-                        uint32_t h4[4], l4[4];
+                    }
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            h4[i] = pack_hi16(hb[2 * i], hb[2 * i + 1]);
-                            l4[i] = pack_hi16(lb[2 * i], lb[2 * i + 1]);
-                        }
-                        const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(h4));
-                        const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(l4));
-                        accg[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bgh, accg[r], 0, 0, 0);
-                        accg[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bgl, accg[r], 0, 0, 0);
-                        accg[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bgh, accg[r], 0, 0, 0);
-                        accu[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, buh, accu[r], 0, 0, 0);
-                        accu[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bul, accu[r], 0, 0, 0);
-                        accu[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, buh, accu[r], 0, 0, 0);
+                    for (int k = 0; k < 16; ++k) {
+                        accg[r][k] = __builtin_fmaf(fg[i], pg[k], accg[r][k]);
+                        accu[r][k] = __builtin_fmaf(fu[i], pu[k], accu[r][k]);
                     }
                 }
             }
+        };
+        issue(0, buf0);
+        load_s(0);
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(c, buf0, buf1);
+            if (c + 1 < nchunks) chunk(c + 1, buf1, buf0);
         }
-    }
-    // a = silu(g) * u as bf16 hi + lo, at [sorted row][feature].
-    const int fo = f0 + 16 * wv + col;
-    if (fo < FFe) {
+
+        // a = silu(g) * u with g, u rescaled by the token's 2^e; stored as bf16 hi + lo.
+        // The row exponents are read before any store (an LDS read here waits for
+        // all outstanding memory operations, stores included).
+        int ex[NR][16];
 #pragma unroll
-        for (int r = 0; r < kRowTiles; ++r) {
-            if (r < nrt) {
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * r + 4 * kq + i;
+            for (int kk = 0; kk < 4; ++kk) {
+                const int4 e4 = *reinterpret_cast<const int4*>(s_e + 32 * r + 8 * kk + 4 * hh);
+                ex[r][4 * kk] = e4.x;
+                ex[r][4 * kk + 1] = e4.y;
+                ex[r][4 * kk + 2] = e4.z;
+                ex[r][4 * kk + 3] = e4.w;
+            }
+        const int fo = f0 + 32 * wv + col;
+        if (fo < FFe) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int rr = 32 * r + 8 * (k >> 2) + 4 * hh + (k & 3);
                     if (rr < nrows) {
-                        const float g = accg[r][i], u = accu[r][i];
-                        const float a = g / (1.f + expf(-g)) * u;
-                        const uint32_t hi = f32_to_bf16_rne(a);
-                        const uint32_t lo = f32_to_bf16_rne(a - __uint_as_float(hi << 16));
+                        const float g = __builtin_ldexpf(accg[r][k], ex[r][k]);
+                        const float u = __builtin_ldexpf(accu[r][k], ex[r][k]);
+                        // silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (~1 ulp each)
+                        const float a = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * g)) * u;
+                        const uint32_t ah = f32_to_bf16_rne(a);
+                        const uint32_t al = f32_to_bf16_rne(a - __uint_as_float(ah << 16));
                         const size_t o = (size_t)(row0 + rr) * p.ffmax + fo;
-                        p.a_hi[o] = (uint16_t)hi;
-                        p.a_lo[o] = (uint16_t)lo;
+                        p.a_hi[o] = (uint16_t)ah;
+                        p.a_lo[o] = (uint16_t)al;
                     }
                 }
             }
         }
+    };
+    switch ((nrows + 31) >> 5) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
     }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Down projection: Y[row][h] = sum_f a[row][f] W_d[h][f].
-// grid.x: row tiles, grid.y: groups of 64 H features.
+// Down projection: Y[row][h] = sum_f a[row][f] W_d[h][f].  Workgroup (8 waves,
+// one per CU): one row tile x 512 outputs; wave w owns outputs 64w .. 64w + 63
+// (NR row sub-tiles x 2 column sub-tiles).  K chunk: 64 features of a_hi
+// (pieces 0..7 of an A row) and a_lo (pieces 8..15), and the matching BPC code
+// blocks of the 512 weight rows.
 // ---------------------------------------------------------------------------------------------
 template <int QT>
-__global__ void __launch_bounds__(kPrefillThreads, 2) prefill_down_kernel(PrefillParams p) {
+__global__ void __launch_bounds__(kDnThreads, 1) prefill_down_kernel(PrefillParams p) {
     constexpr int QK = QT == 1 ? 64 : 32;
-    constexpr int STEPS = QK / 32;
-    const int tile = blockIdx.x;
-    if (tile >= *p.ntiles) return;
+    constexpr int KC = 64;
+    constexpr int BPC = KC / QK;
+    constexpr int SPB = QK / 16;
+    constexpr int BP = bpitch(BPC);
+    constexpr int BUF = kAbytes + kDnCols * BP * 16;
+    __shared__ __attribute__((aligned(16))) uint8_t buf0[BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t buf1[BUF];
+    const int H = p.H;
+    const int nht = (H + kDnCols - 1) / kDnCols;
+    const int item = xcd_item(*p.ntiles * nht);
+    if (item < 0) return;
+    const int tile = item / nht, ht = item - tile * nht;
     const int* td = p.tiles + 3 * tile;
     const int e = td[0], row0 = td[1], nrows = td[2];
     const bool sh = e == p.E;
     const int FFe = sh ? p.FFs : p.FF;
-    const int h0 = blockIdx.y * 64;
-    if (h0 >= p.H) return;
     const uint8_t* blob = sh ? p.shared : (p.table ? (const uint8_t*)p.table[e] : p.single);
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int col = lane & 15, kq = lane >> 4;
-    const int h = min(h0 + 16 * wv + col, p.H - 1);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int col = lane & 31, hh = lane >> 5;
     const int nblk = FFe / QK;
-    const uint8_t* dcode = blob + (size_t)2 * FFe * (p.H / QK) * 18;
-    const uint8_t* dscale = dcode + (size_t)p.H * nblk * 16;
-    const uint8_t* hcode = dcode + (size_t)h * nblk * 16;
-    const uint8_t* hscale = dscale + (size_t)h * nblk * 2;
-    const int nrt = (nrows + 15) / 16;
+    const uint32_t dco = (uint32_t)((size_t)2 * FFe * (H / QK) * 18);   // down codes plane
+    const uint32_t dso = dco + (uint32_t)((size_t)H * nblk * 16);       // down scales plane
+    const int hbase = ht * kDnCols;
 
-    int arow[kRowTiles];
+    constexpr int AJ = (kAcopies + 7) / 8;
+    const uint8_t* abase = (const uint8_t*)p.a_hi;   // a_lo follows at a fixed distance
+    const uint32_t aplane = (uint32_t)((const uint8_t*)p.a_lo - abase);
+    uint32_t aoff[AJ];
 #pragma unroll
-    for (int r = 0; r < kRowTiles; ++r) arow[r] = row0 + min(16 * r + col, nrows - 1);
-
-    f32x4_t acc[kRowTiles];
-#pragma unroll
-    for (int r = 0; r < kRowTiles; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int b = 0; b < nblk; ++b) {
-        const float s = half_to_f32(*reinterpret_cast<const uint16_t*>(hscale + 2 * b));
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            float c[8];
-            codes8<QT>(hcode + 16 * b, st, kq, c);
-            bf16x8_t bh, bl;
-            weights_hi_lo(c, s, p.z * s, bh, bl);
-            const int k0 = QK * b + 32 * st + 8 * kq;
-#pragma unroll
-            for (int r = 0; r < kRowTiles; ++r) {
-                if (r < nrt) {
-                    const size_t o = (size_t)arow[r] * p.ffmax + k0;
-                    const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p.a_hi + o));
-                    const bf16x8_t al = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p.a_lo + o));
-                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[r], 0, 0, 0);
-                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[r], 0, 0, 0);
-                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[r], 0, 0, 0);
-                }
-            }
-        }
+    for (int j = 0; j < AJ; ++j) {
+        const int P = 64 * (wv + 8 * j) + lane;
+        const int row = min(P / kApitch, kRowsPerTile - 1), pc = P % kApitch;
+        const int q = pc == 16 ? 0 : pc;
+        aoff[j] = (q >> 3 ? aplane : 0u) + 2u * (uint32_t)((row0 + min(row, nrows - 1)) * p.ffmax + 8 * (q & 7));
     }
-    const int ho = h0 + 16 * wv + col;
-    if (ho < p.H) {
+    uint32_t boff[BP];
 #pragma unroll
-        for (int r = 0; r < kRowTiles; ++r) {
-            if (r < nrt) {
+    for (int j = 0; j < BP; ++j) {
+        const int L = 64 * j + lane;
+        const int hr = min(hbase + 64 * wv + L / BP, H - 1), pc = L % BP;
+        boff[j] = dco + (uint32_t)(((size_t)hr * nblk + (pc < BPC ? pc : 0)) * 16);
+    }
+    auto issue = [&](int c, uint8_t* buf) {
+        const uint32_t k0 = (uint32_t)(c * KC * 2);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * r + 4 * kq + i;
-                    if (rr < nrows) p.ypair[(size_t)(row0 + rr) * p.H + ho] = acc[r][i];
+        for (int j = 0; j < AJ; ++j)
+            if (wv + 8 * j < kAcopies) load_lds16(abase + (aoff[j] + k0), buf + 1024 * (wv + 8 * j));
+        const uint32_t kb = (uint32_t)(c * BPC * 16);
+#pragma unroll
+        for (int j = 0; j < BP; ++j) load_lds16(blob + (boff[j] + kb), buf + kAbytes + (64 * wv * BP + 64 * j) * 16);
+    };
+    uint32_t soff[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+        soff[n] = dso + (uint32_t)((size_t)min(hbase + 64 * wv + 32 * n + col, H - 1) * nblk * 2);
+    uint32_t nsd[2][BPC];
+    auto load_s = [&](int c) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < BPC; ++i)
+                nsd[n][i] = ldg_u16(blob, soff[n] + 2u * (uint32_t)min(c * BPC + i, nblk - 1));
+    };
+    const uint32_t a_base = (uint32_t)(col * kApitch * 16 + (QK / 2) * hh * 2);
+    const uint32_t b_base = (uint32_t)(kAbytes + (64 * wv + col) * BP * 16);
+
+    auto run = [&](auto nr_c) {
+        constexpr int NR = decltype(nr_c)::value;
+        f32x16_t acc[NR][2];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[r][n][i] = 0.f;
+        const f32x16_t zero = {};
+        const float z = p.z;
+        const int nchunks = (FFe + KC - 1) / KC;
+        auto chunk = [&](int c, const uint8_t* buf, uint8_t* next) {
+            wait_loads();
+            __syncthreads();
+            float fs[2][BPC];
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int i = 0; i < BPC; ++i) fs[n][i] = half_to_f32((uint16_t)nsd[n][i]);
+            if (c + 1 < nchunks) {
+                issue(c + 1, next);
+                load_s(c + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < BPC; ++i) {
+                if (c * BPC + i >= nblk) break;
+                bf16x8_t wb[2][SPB];
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const uint4 d4 = *reinterpret_cast<const uint4*>(buf + b_base + (32 * n * BP + i) * 16);
+                    const uint32_t dw[2] = {hh ? d4.z : d4.x, hh ? d4.w : d4.y};
+#pragma unroll
+                    for (int s = 0; s < SPB; ++s) wb[n][s] = weights_bf16<QT>(dw[(QT == 2) ? s : (s >> 1)], s & 1, z);
+                }
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    bf16x8_t ah[SPB], al[SPB];
+#pragma unroll
+                    for (int s = 0; s < SPB; ++s) {
+                        const int off = 32 * r * kApitch * 16 + ((i * QK + 8 * s) / 8) * 16;
+                        ah[s] = *reinterpret_cast<const bf16x8_t*>(buf + a_base + off);
+                        al[s] = *reinterpret_cast<const bf16x8_t*>(buf + a_base + off + 8 * 16);
+                    }
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        f32x16_t pp = zero;
+#pragma unroll
+                        for (int s = 0; s < SPB; ++s) {
+                            pp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[s], wb[n][s], pp, 0, 0, 0);
+                            pp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[s], wb[n][s], pp, 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int k = 0; k < 16; ++k) acc[r][n][k] = __builtin_fmaf(fs[n][i], pp[k], acc[r][n][k]);
+                    }
                 }
             }
+        };
+        issue(0, buf0);
+        load_s(0);
+        for (int c = 0; c < nchunks; c += 2) {
+            chunk(c, buf0, buf1);
+            if (c + 1 < nchunks) chunk(c + 1, buf1, buf0);
         }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int ho = hbase + 64 * wv + 32 * n + col;
+            if (ho < H) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r)
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) {
+                        const int rr = 32 * r + 8 * (k >> 2) + 4 * hh + (k & 3);
+                        if (rr < nrows) p.ypair[(size_t)(row0 + rr) * H + ho] = acc[r][n][k];
+                    }
+            }
+        }
+    };
+    switch ((nrows + 31) >> 5) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
     }
 }
 
@@ -428,6 +759,25 @@ __global__ void __launch_bounds__(256) prefill_combine_kernel(PrefillParams p) {
 // ---------------------------------------------------------------------------------------------
 // Host orchestration.
 // ---------------------------------------------------------------------------------------------
+static uint32_t f16_bits(float v) {   // exact for the values used here (integers below 2048)
+    const _Float16 h = (_Float16)v;
+    uint16_t b;
+    memcpy(&b, &h, 2);
+    return b;
+}
+
+template <int QT>
+static void launch_gemms(const PrefillParams& p, int x_dtype, hipStream_t s, StageMarks* marks) {
+    const int nft = (p.ffmax + kGuFeatures - 1) / kGuFeatures, nht = (p.H + kDnCols - 1) / kDnCols;
+    const unsigned g_gu = (unsigned)((p.max_tiles * nft + 7) & ~7), g_dn = (unsigned)((p.max_tiles * nht + 7) & ~7);
+    if (x_dtype == 1)
+        hipLaunchKernelGGL((prefill_gateup_kernel<QT, 1>), dim3(g_gu), dim3(kGuThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_gateup_kernel<QT, 2>), dim3(g_gu), dim3(kGuThreads), 0, s, p);
+    stage_mark(marks, s);
+    hipLaunchKernelGGL((prefill_down_kernel<QT>), dim3(g_dn), dim3(kDnThreads), 0, s, p);
+}
+
 hipError_t launch_prefill_layer(const void* const* table, const void* single, const void* shared, int qtype, float z,
                                 int H, int FF, int FFs, const void* x, int x_dtype, const float* logits, int T, int E,
                                 int k, int renorm, int identity, int* ids_out, float* w_out, const LargeLayout& L,
@@ -445,6 +795,8 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     p.FFs = FFs;
     p.ffmax = FFs > FF ? FFs : FF;
     p.z = z;
+    const uint32_t zb = f16_bits(-(1024.f + 2.f * z));
+    p.zc16 = zb | (zb << 16);
     int* ids = ids_out ? ids_out : (int*)(ws + L.ids);
     float* w = w_out ? w_out : (float*)(ws + L.w);
     p.ids = ids;
@@ -455,6 +807,8 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     p.ntiles = (int*)(ws + L.ntiles);
     p.perm = (int*)(ws + L.perm);
     p.inv = (int*)(ws + L.inv);
+    p.xq = (uint16_t*)(ws + L.xq);
+    p.xe = (int*)(ws + L.xe);
     const size_t P = (size_t)T * k + (FFs ? (size_t)T : 0);
     p.a_hi = (uint16_t*)(ws + L.a);
     p.a_lo = p.a_hi + P * p.ffmax;
@@ -466,28 +820,21 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     if (identity)
         hipLaunchKernelGGL(prefill_identity_kernel, dim3((T + 255) / 256), dim3(256), 0, s, ids, w, T);
     else
-        launch_route_topk(logits, T, E, k, renorm, ids, w, s);
+        (void)launch_route_topk(logits, T, E, k, renorm, ids, w, s);
     stage_mark(marks, s);
     hipLaunchKernelGGL(prefill_count_kernel, dim3(1), dim3(1024), 0, s, p);
     stage_mark(marks, s);
     hipLaunchKernelGGL(prefill_place_kernel, dim3((E + 3) / 4), dim3(256), 0, s, p);
-    stage_mark(marks, s);
-    const dim3 g_gu(p.max_tiles, (p.ffmax + 63) / 64), g_dn(p.max_tiles, (H + 63) / 64);
     if (qtype == 2) {
-        if (x_dtype == 1)
-            hipLaunchKernelGGL((prefill_gateup_kernel<2, 1>), g_gu, dim3(kPrefillThreads), 0, s, p);
-        else
-            hipLaunchKernelGGL((prefill_gateup_kernel<2, 2>), g_gu, dim3(kPrefillThreads), 0, s, p);
-        stage_mark(marks, s);
-        hipLaunchKernelGGL((prefill_down_kernel<2>), g_dn, dim3(kPrefillThreads), 0, s, p);
+        if (x_dtype == 1) hipLaunchKernelGGL((prefill_xprep_kernel<2, 1>), dim3(T), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((prefill_xprep_kernel<2, 0>), dim3(T), dim3(256), 0, s, p);
     } else {
-        if (x_dtype == 1)
-            hipLaunchKernelGGL((prefill_gateup_kernel<1, 1>), g_gu, dim3(kPrefillThreads), 0, s, p);
-        else
-            hipLaunchKernelGGL((prefill_gateup_kernel<1, 2>), g_gu, dim3(kPrefillThreads), 0, s, p);
-        stage_mark(marks, s);
-        hipLaunchKernelGGL((prefill_down_kernel<1>), g_dn, dim3(kPrefillThreads), 0, s, p);
+        if (x_dtype == 1) hipLaunchKernelGGL((prefill_xprep_kernel<1, 1>), dim3(T), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((prefill_xprep_kernel<1, 0>), dim3(T), dim3(256), 0, s, p);
     }
+    stage_mark(marks, s);
+    if (qtype == 2) launch_gemms<2>(p, x_dtype, s, marks);
+    else launch_gemms<1>(p, x_dtype, s, marks);
     stage_mark(marks, s);
     const size_t n4 = (size_t)T * H / 4;
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, p);

@@ -78,7 +78,9 @@ typedef struct {
     int32_t hidden;      /* H: model width = input and output length */
     int32_t ff;          /* FF: expert intermediate width */
     int32_t qtype;       /* moe_qtype */
-    float zero_point;    /* z: 1.5 (2-bit) / 7.5 (4-bit) in the measured shapes; 1.0 is the Strata mapping */
+    float zero_point;    /* z: 1.5 (2-bit) / 7.5 (4-bit) in the measured shapes; 1.0 is the Strata mapping.
+                            Must be a multiple of 0.5 in [-64, 64] (MOE_ERR_UNSUPPORTED otherwise): the
+                            matrix-core path multiplies by 2(c - z), which is then an exact small integer */
     int32_t act;         /* moe_act */
 } moe_expert_desc;
 

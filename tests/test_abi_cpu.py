@@ -93,6 +93,9 @@ def test_layer_forward_rejects_bad_arguments(L):
     assert call(bad_act) == 2
     big = moe.layer_desc(2560 * 8, 640, 1, 1.5, 512, 10)                      # 320 blocks per row
     assert call(big) == 2
+    assert call(moe.layer_desc(2560, 640, 1, 1.25, 512, 10)) == 2             # zero point not a multiple of 0.5
+    assert call(moe.layer_desc(2560, 640, 1, 70.0, 512, 10)) == 2             # zero point beyond 64
+    assert call(moe.layer_desc(2560, 640, 1, -2.5, 512, 10), ws_bytes=16) == 3  # negative half-integer: accepted
 
 
 def test_expert_ffn_rejects_bad_arguments(L):
