@@ -111,21 +111,37 @@ def prefill_flops(w, n_slots, T):
     return gu, dn
 
 
-def prefill_cpu_baseline(w, x0, l0, got, budget_s=12.0):
-    """The float64 oracle, single-threaded, on a bounded sample: the first
-    tokens of layer 0, step 0 (each token's routing and experts are independent
-    of the other tokens), until the budget is spent.  Also returns the GPU
-    output's max |err| / rms on the sampled tokens."""
+def prefill_sample(w, l0, n=64):
+    """A deterministic sample of n prompt tokens of layer 0: a token routed to
+    the hottest expert, one routed to the coldest, then the first tokens."""
+    import oracle
+    ids, _ = oracle.route_topk(l0, w.top_k)
+    counts = np.bincount(ids.reshape(-1), minlength=w.experts)
+    hot, cold = int(np.argmax(counts)), int(np.argmin(counts))
+    pick = [int(np.nonzero((ids == hot).any(1))[0][0]), int(np.nonzero((ids == cold).any(1))[0][0])]
+    for t in range(w.tokens):
+        if len(pick) >= n:
+            break
+        if t not in pick:
+            pick.append(t)
+    return sorted(pick), hot, cold
+
+
+def prefill_cpu_baseline(w, x0, l0, got, n=64):
+    """The float64 oracle, single-threaded, on a bounded sample of layer 0 of
+    the prompt: 64 tokens including ones routed to the hottest and the coldest
+    expert (each token's routing and experts are independent of the others).
+    Also returns the GPU output's max |err| / rms on the sampled tokens."""
     import oracle
     import synth
     from synth import workloads as wl
+    sample, hot, cold = prefill_sample(w, l0, n)
     zero = np.zeros(w.blob_bytes, dtype=np.uint8)
     cache = {}
-    t_total, n, errs, refs = 0.0, 0, [], []
-    chunk = 2
-    while t_total < budget_s and n + chunk <= w.tokens:
-        x = x0[n:n + chunk]
-        lg = l0[n:n + chunk]
+    t_total, refs = 0.0, []
+    for c in range(0, len(sample), 4):
+        rows = sample[c:c + 4]
+        x, lg = x0[rows], l0[rows]
         ids_ref, _ = oracle.route_topk(lg, w.top_k)
         for e in set(ids_ref.reshape(-1).tolist()):
             if e not in cache:
@@ -136,14 +152,14 @@ def prefill_cpu_baseline(w, x0, l0, got, budget_s=12.0):
                                        shared=wl.host_shared_blob(w, 0), shared_ff=w.shared_ff)
         t_total += time.perf_counter() - t0
         refs.append(y)
-        errs.append(np.max(np.abs(got[n:n + chunk] - y)))
-        n += chunk
     ref = np.concatenate(refs)
     rms = float(np.sqrt(np.mean(ref ** 2)))
-    return ({"value": n / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-             "sample": f"first {n} of the {w.tokens} prompt tokens of layer 0 (routing, {w.top_k} experts each, "
-                       f"SwiGLU, combine), float64 oracle single-threaded, {t_total:.1f} s"},
-            float(max(errs)) / rms, n)
+    err = float(np.max(np.abs(got[sample] - ref))) / rms
+    return ({"value": len(sample) / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+             "sample": f"{len(sample)} of the {w.tokens} prompt tokens of layer 0 (tokens routed to the hottest "
+                       f"expert {hot} and the coldest expert {cold}, then the first tokens), float64 oracle "
+                       f"single-threaded, {t_total:.1f} s"},
+            err, len(sample))
 
 
 def bench_prefill(args, w):

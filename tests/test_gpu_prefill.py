@@ -94,8 +94,13 @@ def test_prefill_full_layer_sampled_tokens():
     assert np.max(np.abs(wt.cpu().numpy() - w_ref)) <= 1e-6
     counts = np.bincount(ids_ref.reshape(-1), minlength=w.experts)
     hot, cold = int(np.argmax(counts)), int(np.argmin(counts))
-    sample = sorted({int(np.nonzero((ids_ref == hot).any(1))[0][0]), int(np.nonzero((ids_ref == cold).any(1))[0][0]),
-                     0, 1, 777, 2048, 4095})
+    # 64 tokens: ones routed to the hottest and the coldest expert, the last
+    # token, and a deterministic spread over the prompt.
+    must = [int(np.nonzero((ids_ref == hot).any(1))[0][0]), int(np.nonzero((ids_ref == cold).any(1))[0][0]),
+            w.tokens - 1]
+    spread = [t for t in range(0, w.tokens, w.tokens // 61) if t not in must]
+    sample = sorted(must + spread[:64 - len(must)])
+    assert len(sample) == 64
     need = sorted(set(ids_ref[sample].reshape(-1).tolist()))
     blobs = {e: synth.expert_blob(w.seed, 0, e, w.qk, w.hidden, w.ff, w.sigma) for e in need}
     zero = np.zeros(w.blob_bytes, dtype=np.uint8)
