@@ -24,26 +24,33 @@ __device__ __forceinline__ float from_order_bits(uint32_t k) {
     return __uint_as_float(u);
 }
 
-// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.
+// DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror, and the broadcasts of lane 15 of each row to the next row and of
+// lane 31 to rows 2 and 3.
 constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-template <int CTRL>
+// max(v, v from the DPP source lane).  Lanes of rows outside ROWM, and lanes
+// without a source, see the identity 0, so the compiler can fold the DPP move
+// into the v_max (one instruction per step).
+template <int CTRL, int ROWM = 0xF>
 __device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
-    const uint32_t o = dpp_u32<CTRL>(v);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWM, 0xF, false);
     return o > v ? o : v;
 }
 
-template <int CTRL>
+template <int CTRL, int ROWM = 0xF>
 __device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) {
-    const uint32_t o = dpp_u32<CTRL>(v);
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, CTRL, ROWM, 0xF, false);
     return o < v ? o : v;
 }
 
@@ -61,16 +68,16 @@ __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
 }
 
 // Maximum / minimum over the 64 lanes of a wave (every lane active); uniform
-// result.  Four DPP steps give each row of 16 lanes its extremum; the four
-// rows combine on the scalar unit.
+// result.  Four DPP steps give each row of 16 lanes its extremum; two row
+// broadcasts carry it up to lane 63, which is read once.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = dpp_max_u32<kDppXor1>(v);
     v = dpp_max_u32<kDppXor2>(v);
     v = dpp_max_u32<kDppHalfMirror>(v);
     v = dpp_max_u32<kDppMirror>(v);
-    const uint32_t a = max(readlane_u32(v, 0), readlane_u32(v, 16));
-    const uint32_t b = max(readlane_u32(v, 32), readlane_u32(v, 48));
-    return max(a, b);
+    v = dpp_max_u32<kDppBcast15, 0xA>(v);
+    v = dpp_max_u32<kDppBcast31, 0xC>(v);
+    return readlane_u32(v, 63);
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -78,9 +85,9 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     v = dpp_min_u32<kDppXor2>(v);
     v = dpp_min_u32<kDppHalfMirror>(v);
     v = dpp_min_u32<kDppMirror>(v);
-    const uint32_t a = min(readlane_u32(v, 0), readlane_u32(v, 16));
-    const uint32_t b = min(readlane_u32(v, 32), readlane_u32(v, 48));
-    return min(a, b);
+    v = dpp_min_u32<kDppBcast15, 0xA>(v);
+    v = dpp_min_u32<kDppBcast31, 0xC>(v);
+    return readlane_u32(v, 63);
 }
 
 template <int CTRL>

@@ -66,6 +66,8 @@ __device__ __forceinline__ uint32_t magic_vgpr() {
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 constexpr uint32_t kOnes = 0x3F803F80u;    // bf16 pair (1.0, 1.0)
+constexpr int kCpolSc1 = 16;               // cache policy bits of a buffer load: sc1 (agent coherence)
+constexpr int kRsrcWord3 = 0x00020000;     // buffer resource word 3: 32-bit data format, raw access
 constexpr int kMaxPass = 8;    // gate/up passes per tile (tile rows = P * passes)
 
 template <int QT>
@@ -193,18 +195,23 @@ __device__ __forceinline__ void load_slice_f32(XSlice<QT, 2>& s, const float* sr
 // SwiGLU output as the gate/up stage publishes it): de-interleave into the two
 // terms' dot pairs.
 template <int QT>
-__device__ __forceinline__ void load_slice_packed(XSlice<QT, 2>& s, const uint32_t* pk, float z) {
+// `a` is read with agent-coherent (sc1) buffer loads: it was written by other
+// workgroups, possibly on other XCDs, before their ready flags were raised, so
+// these loads see it without invalidating this XCD's L2.
+__device__ __forceinline__ void load_slice_packed(XSlice<QT, 2>& s, __amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off,
+                                                  float z) {
     constexpr int QK = QTraits<QT>::QK;
     constexpr int HALF = QT == 1 ? 8 : 4;   // pair (v, v + HALF) within a dword's codes
     constexpr int PER = QT == 1 ? 16 : 8;   // values per code dword
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     uint32_t w[QK];
 #pragma unroll
     for (int v = 0; v < QK / 4; ++v) {
-        const uint4 u = reinterpret_cast<const uint4*>(pk)[v];
-        w[4 * v + 0] = u.x;
-        w[4 * v + 1] = u.y;
-        w[4 * v + 2] = u.z;
-        w[4 * v + 3] = u.w;
+        const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(byte_off + 16 * v), 0, kCpolSc1);
+        w[4 * v + 0] = u[0];
+        w[4 * v + 1] = u[1];
+        w[4 * v + 2] = u[2];
+        w[4 * v + 3] = u[3];
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d)
@@ -289,18 +296,21 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
 // Every workgroup first recomputes the routing and the expert-major buckets of
 // the <= 8 tokens from the logits (a few KB, served from L2).  Workgroups
 // [0, n_gu) run gate/up + SwiGLU tiles and publish their rows of `a` with
-// agent-coherent stores; each tile then bumps its group's counter, and the
-// last tile of a group bumps `groups_done`.  Workgroups [n_gu, grid) own a
-// tile of H output rows: they issue the loads of their down-projection weights
-// for every selected expert at once, wait until every group is done, read
-// `a`, and finish the down projection and the weighted combine for their rows
-// (no second pass).  Workgroups are dispatched in index order on each XCD, so
+// agent-coherent stores; each tile then bumps its group's counter, and the tile
+// that completes a group raises the group's ready flag in each of n_ready
+// replicas (4 KB apart).  Workgroups [n_gu, grid) own a tile of H output rows:
+// they issue the loads of their down-projection weights for every selected
+// expert at once, wait until every group's flag in their replica (tile %
+// n_ready) is raised, read `a`, and finish the down projection and the
+// weighted combine for their rows (no second pass).  Polling one replica per
+// 16 workgroups keeps the pollers off the lines that the counters and flags
+// are written on.  Workgroups are dispatched in index order on each XCD, so
 // every gate/up workgroup is running or done before any down workgroup on the
 // same XCD starts waiting; the wait is bounded anyway and flags an error if
 // the bound is ever reached.  The last down workgroup to leave returns every
-// counter to zero for the next call.  Same-address atomics serialise (about
-// 12 ns each), so counters are per group, on separate 64-byte lines, and the
-// exit count is two-level.
+// counter and flag to zero for the next call.  Same-address atomics serialise
+// (about 12 ns each), so counters are per group, on separate 64-byte lines,
+// and the exit count is two-level.
 // ---------------------------------------------------------------------------------------------
 constexpr int kMaxPairs = kSmallT * kMaxK;   // 256
 constexpr size_t kDecodeLdsBudget = 112 * 1024;   // dynamic LDS of the fused decode kernel
@@ -326,6 +336,7 @@ struct DecodeParams {
     int* sync;                   // DecodeSync words, see sync_* below
     int gu_passes, tiles_gu, tiles_gu_s, max_groups, shared_groups, n_gu;
     int dn_rows, tiles_dn;
+    int n_ready;                 // ready-flag replicas in use: min(kReadyReplicas, tiles_dn)
 };
 
 // Word offsets inside the synchronisation area (ints; 16 ints = one 64-byte line).
@@ -334,6 +345,11 @@ __device__ __forceinline__ int* sync_groups_done(int* s) { return s; }
 __device__ __forceinline__ int* sync_error(int* s) { return s + 16; }
 __device__ __forceinline__ int* sync_exit_top(int* s) { return s + 32; }
 __device__ __forceinline__ int* sync_exit(int* s, int i, int max_groups) { return s + 16 * (4 + max_groups + i); }
+// Ready flag of group g in replica r (replicas kReadyStride bytes apart, after the lines above).
+__device__ __forceinline__ int* sync_ready(int* s, int r, int g, int n_ctr) {
+    const size_t lines = (decode_sync_lines_bytes(n_ctr) + kReadyStride - 1) / kReadyStride * kReadyStride;
+    return s + (lines + (size_t)r * kReadyStride) / 4 + g;
+}
 
 struct RouteLDS {
     int id[kMaxPairs];
@@ -561,8 +577,22 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();   // every store above has completed (the barrier waits for them)
-    if (tid == 0) {
-        __hip_atomic_fetch_add(sync_group(p.sync, grp), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Count this tile; the tile that completes its group raises the group's
+    // ready flag in every replica (down workgroups each poll one replica).
+    if (tid < 64) {
+        int old = 0;
+        if (tid == 0)
+            old = __hip_atomic_fetch_add(sync_group(p.sync, grp), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        const int need = grp < p.max_groups ? p.tiles_gu : p.tiles_gu_s;
+        const int n_ctr = p.max_groups + p.shared_groups;
+        if (old == need - 1 && tid < p.n_ready)
+            __hip_atomic_store(sync_ready(p.sync, tid, grp, n_ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The first tile of group 0 to finish also raises the prefetch hint (slot
+        // n_ctr): from then on the down weights may be loaded.  A hint that lands
+        // late only starts a later call's prefetch early.
+        if (old == 0 && grp == 0 && tid < p.n_ready)
+            __hip_atomic_store(sync_ready(p.sync, tid, n_ctr, n_ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -581,6 +611,24 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
     S = S < 1 ? 1 : (S > nrows ? nrows : S);
     const int per_round = kGemvThreads / S;
     const size_t gu_r = (size_t)2 * p.FF * (p.H / QK) * 18, gu_s = (size_t)2 * p.FFs * (p.H / QK) * 18;
+
+    // One buffer resource over `a` and the shared expert's rows after it.
+    const uint32_t as_off = (uint32_t)((const char*)p.as - (const char*)p.a);
+    const uint32_t a_bytes = as_off + (uint32_t)((size_t)p.T * p.FFs * 4);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.a, 0, (int)a_bytes, kRsrcWord3);
+
+    // The down weights are prefetched only once a first gate/up tile is done:
+    // until then the gate/up weight loads, which are on the critical path, have
+    // the memory system to themselves.
+    {
+        const int rep = tile % p.n_ready;
+        const int n_ctr = p.max_groups + p.shared_groups;
+        long spins = 0;
+        while (__hip_atomic_load(sync_ready(p.sync, rep, n_ctr, n_ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   0 &&
+               ++spins < kSpinLimit)
+            __builtin_amdgcn_s_sleep(1);
+    }
 
     // part[(unit * dn_rows + r) * NT + t]
     bool waited = false;
@@ -618,41 +666,72 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
             sc[i] = *reinterpret_cast<const uint16_t*>(dscale + blk * 2);
         }
         if (!waited) {
-            // Thread g of the first wave watches group g's tile counter (routed
-            // groups, then shared groups); the wave continues when all are full.
+            // Thread g of the first wave watches group g's ready flag (routed
+            // groups, then shared groups) in this workgroup's replica; the wave
+            // continues when all are raised.
             if (tid < 64) {
                 long spins = 0;
+                const int rep = tile % p.n_ready;
+                const int n_ctr = p.max_groups + p.shared_groups;
                 for (int g0 = 0; g0 < ng + p.shared_groups; g0 += 64) {
                     const int gi = g0 + tid;
                     const bool mine = gi < ng + p.shared_groups;
                     const int ctr = gi < ng ? gi : p.max_groups + (gi - ng);
-                    const int need = gi < ng ? p.tiles_gu : p.tiles_gu_s;
                     while (true) {
-                        const bool ready = !mine || __hip_atomic_load(sync_group(p.sync, ctr), __ATOMIC_RELAXED,
-                                                                      __HIP_MEMORY_SCOPE_AGENT) >= need;
+                        const bool ready = !mine || __hip_atomic_load(sync_ready(p.sync, rep, ctr, n_ctr),
+                                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
                         if (__all(ready)) break;
                         if (++spins > kSpinLimit) {
                             if (tid == 0)
                                 __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                             break;
                         }
-                        __builtin_amdgcn_s_sleep(2);
+                        __builtin_amdgcn_s_sleep(1);
                     }
                 }
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
             waited = true;
+            // Two-level count of the down workgroups that are past their wait; the
+            // last one returns every counter and flag to zero for the next call
+            // (no workgroup reads them any more).
+            if (tid == 0) {
+                const int fan = min(kExitFan, p.tiles_dn);
+                const int i = tile % fan;
+                const int members = (p.tiles_dn - i + fan - 1) / fan;
+                int last = 0;
+                if (__hip_atomic_fetch_add(sync_exit(p.sync, i, p.max_groups + p.shared_groups), 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == members - 1)
+                    last = __hip_atomic_fetch_add(sync_exit_top(p.sync), 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT) == fan - 1;
+                R.flag = last;
+            }
+            __syncthreads();
+            if (R.flag) {
+                const int n_ctr = p.max_groups + p.shared_groups;
+                const int fan = min(kExitFan, p.tiles_dn);
+                for (int i = tid; i < n_ctr; i += kGemvThreads)
+                    __hip_atomic_store(sync_group(p.sync, i), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int i = tid; i < p.n_ready * (n_ctr + 1); i += kGemvThreads)
+                    __hip_atomic_store(sync_ready(p.sync, i / (n_ctr + 1), i % (n_ctr + 1), n_ctr), 0,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int i = tid; i < fan; i += kGemvThreads)
+                    __hip_atomic_store(sync_exit(p.sync, i, n_ctr), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (tid == 0) {
+                    __hip_atomic_store(sync_groups_done(p.sync), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(sync_exit_top(p.sync), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
         }
         if (act) {
             XSlice<QT, 2> xs[NT];
             const bool sh = u >= ng * nb_r;
-            const uint32_t* abase = sh ? p.as : p.a;
+            const uint32_t base = sh ? as_off : 0u;   // byte offset of this unit's `a` rows
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int tt = t < ntok ? t : 0;
                 const int row = sh ? g * NT + tt : R.group_first[g] + tt;
-                load_slice_packed<QT>(xs[t], abase + (size_t)row * K + b * QK, p.z);
+                load_slice_packed<QT>(xs[t], a_rsrc, base + 4u * (uint32_t)(row * K + b * QK), p.z);
             }
 #pragma unroll
             for (int i = 0; i < kRowsPerThread; ++i) {
@@ -700,32 +779,6 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
         p.y[(size_t)t * p.H + h0 + r] = acc;
     }
 
-    // Two-level exit count over the down workgroups; the last one resets every counter.
-    __syncthreads();
-    if (tid == 0) {
-        const int fan = min(kExitFan, p.tiles_dn);
-        const int i = tile % fan;
-        const int members = (p.tiles_dn - i + fan - 1) / fan;
-        int last = 0;
-        if (__hip_atomic_fetch_add(sync_exit(p.sync, i, p.max_groups + p.shared_groups), 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT) == members - 1)
-            last = __hip_atomic_fetch_add(sync_exit_top(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   fan - 1;
-        R.flag = last;
-    }
-    __syncthreads();
-    if (R.flag) {
-        const int n_ctr = p.max_groups + p.shared_groups;
-        const int fan = min(kExitFan, p.tiles_dn);
-        for (int i = tid; i < n_ctr; i += kGemvThreads)
-            __hip_atomic_store(sync_group(p.sync, i), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int i = tid; i < fan; i += kGemvThreads)
-            __hip_atomic_store(sync_exit(p.sync, i, n_ctr), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (tid == 0) {
-            __hip_atomic_store(sync_groups_done(p.sync), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(sync_exit_top(p.sync), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
 
 template <int QT, int NT, int NTERM>
@@ -848,6 +901,7 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
     p.n_gu = g.n_gu;
     p.dn_rows = g.tile_rows_dn;
     p.tiles_dn = g.tiles_dn;
+    p.n_ready = g.tiles_dn < kReadyReplicas ? g.tiles_dn : kReadyReplicas;
     stage_mark(marks, s);
     hipError_t e;
     if (T == 1)

@@ -25,7 +25,16 @@ inline int codes_per_block(int qtype) { return qtype == 1 ? 64 : (qtype == 2 ? 3
 // workspace: 64-byte lines holding groups_done, error, the top exit counter,
 // one counter per group and the first-level exit counters.  It must be zero
 // before the first call on a workspace; every call leaves it zero again.
-inline size_t decode_sync_bytes(int max_groups_total) { return (size_t)64 * (4 + max_groups_total + 16); }
+// Synchronisation area of the fused decode kernel: 4 + groups + 16 lines of 64
+// bytes (flags, per-group counters, exit counters), then kReadyReplicas
+// replicas of the per-group ready flags, kReadyStride bytes apart.
+constexpr int kReadyReplicas = 16;
+constexpr int kReadyStride = 4096;
+__host__ __device__ inline size_t decode_sync_lines_bytes(int max_groups_total) { return (size_t)64 * (4 + max_groups_total + 16); }
+__host__ __device__ inline size_t decode_sync_bytes(int max_groups_total) {
+    const size_t lines = (decode_sync_lines_bytes(max_groups_total) + kReadyStride - 1) / kReadyStride * kReadyStride;
+    return lines + (size_t)kReadyReplicas * kReadyStride;
+}
 
 // Workspace layout for the GEMV path (T <= kSmallT), byte offsets.
 struct SmallLayout {

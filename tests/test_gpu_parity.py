@@ -263,7 +263,8 @@ def test_workspace_sync_words_return_to_zero():
             y = moe.layer_forward(desc, arena.tables[0], x, logits, shared=arena.shared_blob(0), ws=ws)
             assert torch.equal(y, y0)
         torch.cuda.synchronize()
-        nsync = 64 * (4 + T * w.top_k + T + 16)
+        lines = 64 * (4 + T * w.top_k + T + 16)
+        nsync = (lines + 4095) // 4096 * 4096 + 16 * 4096   # counters, then 16 replicas of the ready flags
         assert int(ws[:nsync].view(torch.int32).abs().sum().item()) == 0
 
 
