@@ -588,10 +588,10 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         const int n_ctr = p.max_groups + p.shared_groups;
         if (old == need - 1 && tid < p.n_ready)
             __hip_atomic_store(sync_ready(p.sync, tid, grp, n_ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // The first tile of group 0 to finish also raises the prefetch hint (slot
-        // n_ctr): from then on the down weights may be loaded.  A hint that lands
-        // late only starts a later call's prefetch early.
-        if (old == 0 && grp == 0 && tid < p.n_ready)
+        // The first tile of each group to finish also raises the prefetch hint
+        // (slot n_ctr): from then on the down weights may be loaded.  A hint that
+        // lands late only starts a later call's prefetch early.
+        if (old == 0 && tid < p.n_ready)
             __hip_atomic_store(sync_ready(p.sync, tid, n_ctr, n_ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
