@@ -117,13 +117,81 @@ __device__ __forceinline__ float group8_sum_f32(float v) {
 }
 
 // One wave: top-k of one token's E <= 64 * KPL logits (every lane active).
-// Lane l holds logits l, l + 64, ... (KPL slots) and first sorts them by
-// (key descending, index ascending) with a sorting network.  Each round takes the wave maximum of the lanes' heads; the owner
-// is the single lane holding it, or on an exact tie the one whose head has the
-// lowest expert index; the owner then shifts its list by one.  Lane j < k
+// Lane l holds logits l, l + 64, ... (KPL slots) as 64-bit keys
+// order_bits(logit) << 32 | ~index, so that a larger key ranks first (higher
+// logit, then lower expert index) and no two keys are equal.  Lane j < k
 // returns the j-th selected expert and its routing weight: softmax over the k
 // selected logits (renorm) or the full softmax over E read at the selected
 // experts; an all -inf selection gets equal weights.
+//
+// Selection goes by threshold (topk_threshold): few elements lie at or above
+// the k-th largest lane maximum, and only those are ranked.  When more than 64
+// do (heavy ties near the top), k rounds of a wave maximum over per-lane sorted
+// lists pick the winners one by one instead (topk_rounds).  Both give the same
+// keys: the k largest, in descending order.
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return (uint64_t)hi << 32 | lo;
+}
+
+// Number of lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Threshold selection.  thr = the k-th largest of the 64 lane maxima of the
+// 32-bit order keys, found bit by bit from the top: a bit stays set when at
+// least k lane maxima reach the value with it.  The k lanes whose maxima reach
+// thr hold k distinct elements >= thr, so the k-th largest element is >= thr
+// and every selected element is among those >= thr.  When at most 64 are, they
+// are gathered one per lane through `scratch` (64 keys of LDS owned by this
+// wave), each counts the larger keys among them, and the k of rank < k are
+// written back at their ranks.  Returns false (nothing selected) when more than
+// 64 elements reach thr; the outcome is uniform across the wave.
+template <int KPL>
+__device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k, int lane, uint64_t* scratch,
+                                               uint64_t* sel) {
+    uint32_t hi[KPL];
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        hi[i] = (uint32_t)(key[i] >> 32);
+        lmax = hi[i] > lmax ? hi[i] : lmax;
+    }
+    uint32_t thr = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = thr | (1u << b);
+        if (__popcll(__ballot(lmax >= c)) >= k) thr = c;
+    }
+    uint64_t mask[KPL];
+    int base[KPL];
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        mask[i] = __ballot(hi[i] >= thr);
+        base[i] = n;
+        n += __popcll(mask[i]);
+    }
+    if (n > 64) return false;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+        if (hi[i] >= thr) scratch[base[i] + lanes_below(mask[i])] = key[i];
+    // LDS accesses of one wave complete in program order; the barrier keeps the
+    // compiler from moving them across each other.
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t mine = lane < n ? scratch[lane] : 0ull;
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += readlane_u64(mine, j) > mine;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < n && rank < k) scratch[rank] = mine;
+    __builtin_amdgcn_wave_barrier();
+    *sel = lane < k ? scratch[lane] : 0ull;
+    __builtin_amdgcn_wave_barrier();
+    return true;
+}
+
 // Batcher odd-even merge sort networks (compare-exchange index pairs) for
 // 2, 4, 8 and 16 keys, listed as constants so every index is static.
 template <int KPL> struct SortNet;
@@ -159,9 +227,38 @@ __device__ __forceinline__ void sort_desc(uint64_t (&key)[KPL]) {
     }
 }
 
+// Rounds selection: each lane sorts its keys (descending); each round takes
+// the wave maximum of the lanes' heads, whose owner (a single lane: keys are
+// distinct) shifts its list by one.  Lane r < k gets the round-r key.
+template <int KPL>
+__device__ __forceinline__ uint64_t topk_rounds(uint64_t (&key)[KPL], int k, int lane) {
+    sort_desc<KPL>(key);
+    uint64_t sel = 0;
+    for (int r = 0; r < k; ++r) {
+        const uint32_t head = (uint32_t)(key[0] >> 32);
+        const uint32_t m = wave_max_u32(head);
+        const uint64_t cand = __ballot(head == m);
+        int owner;
+        if (__popcll(cand) == 1) {
+            owner = __ffsll((unsigned long long)cand) - 1;
+        } else {   // equal logits: the lowest expert index among the candidates
+            const uint32_t ix = 0xFFFFFFFFu - (uint32_t)key[0];
+            owner = (int)(wave_min_u32(head == m ? ix : 0xFFFFFFFFu) & 63u);
+        }
+        const uint64_t won = readlane_u64(key[0], owner);
+        if (lane == r) sel = won;
+        if (lane == owner) {
+#pragma unroll
+            for (int i = 0; i + 1 < KPL; ++i) key[i] = key[i + 1];
+            key[KPL - 1] = 0ull;
+        }
+    }
+    return sel;
+}
+
 template <int KPL>
 __device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int E, int k, int renorm, int lane,
-                                              int* out_id, float* out_w) {
+                                              uint64_t* scratch, int* out_id, float* out_w) {
     uint64_t key[KPL];
     float lv[KPL];
     // Every load is unconditional (clamped address) so that all of them are in
@@ -177,33 +274,11 @@ __device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int
         const uint64_t valid = 0ull - (uint64_t)(e < (uint32_t)E);
         key[i] = (((uint64_t)order_bits(lv[i]) << 32) | (uint64_t)(0xFFFFFFFFu - e)) & valid;
     }
-    sort_desc<KPL>(key);
-
-    int my_id = -1;
-    uint32_t my_key = 0, top_key = 0;
-    for (int r = 0; r < k; ++r) {
-        const uint32_t head = (uint32_t)(key[0] >> 32);
-        const uint32_t m = wave_max_u32(head);
-        const uint64_t cand = __ballot(head == m);
-        int owner;
-        if (__popcll(cand) == 1) {
-            owner = __ffsll((unsigned long long)cand) - 1;
-        } else {   // exact tie: the lowest expert index among the candidates
-            const uint32_t ix = 0xFFFFFFFFu - (uint32_t)key[0];
-            owner = (int)(wave_min_u32(head == m ? ix : 0xFFFFFFFFu) & 63u);
-        }
-        const int id = (int)(0xFFFFFFFFu - (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[0], owner));
-        if (lane == r) {
-            my_id = id;
-            my_key = m;
-        }
-        if (r == 0) top_key = m;
-        if (lane == owner) {
-#pragma unroll
-            for (int i = 0; i + 1 < KPL; ++i) key[i] = key[i + 1];
-            key[KPL - 1] = 0ull;
-        }
-    }
+    uint64_t sel;
+    if (!topk_threshold<KPL>(key, k, lane, scratch, &sel)) sel = topk_rounds<KPL>(key, k, lane);
+    const uint32_t my_key = (uint32_t)(sel >> 32);
+    const uint32_t top_key = readlane_u32(my_key, 0);
+    const int my_id = lane < k ? (int)(0xFFFFFFFFu - (uint32_t)sel) : -1;
     const float top = from_order_bits(top_key);
     const float my_logit = from_order_bits(my_key);
     const bool all_neg_inf = (top == -INFINITY);
@@ -225,12 +300,13 @@ __device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int
     *out_w = e_sel / denom;
 }
 
+// `scratch`: 64 keys of LDS owned by the calling wave.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm, int lane,
-                                          int* out_id, float* out_w) {
-    if (E <= 128) wave_topk_kpl<2>(row, E, k, renorm, lane, out_id, out_w);
-    else if (E <= 256) wave_topk_kpl<4>(row, E, k, renorm, lane, out_id, out_w);
-    else if (E <= 512) wave_topk_kpl<8>(row, E, k, renorm, lane, out_id, out_w);
-    else wave_topk_kpl<16>(row, E, k, renorm, lane, out_id, out_w);
+                                          uint64_t* scratch, int* out_id, float* out_w) {
+    if (E <= 128) wave_topk_kpl<2>(row, E, k, renorm, lane, scratch, out_id, out_w);
+    else if (E <= 256) wave_topk_kpl<4>(row, E, k, renorm, lane, scratch, out_id, out_w);
+    else if (E <= 512) wave_topk_kpl<8>(row, E, k, renorm, lane, scratch, out_id, out_w);
+    else wave_topk_kpl<16>(row, E, k, renorm, lane, scratch, out_id, out_w);
 }
 
 }  // namespace moe

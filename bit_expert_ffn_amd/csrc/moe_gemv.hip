@@ -358,6 +358,7 @@ struct RouteLDS {
     int group_first[kMaxPairs], group_n[kMaxPairs], group_of_pair[kMaxPairs];
     int rank[kMaxPairs], pos[kMaxPairs], cnt[kMaxPairs];
     int slot_src[kMaxPairs];   // slot (t, j) -> group * NT + token-in-group of its pair
+    uint64_t topk[kGemvThreads / 64][64];   // each wave's top-k scratch
     int n_groups;
     int flag;
 };
@@ -374,7 +375,7 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
         if (wv == 0) {
             int id = 0;
             float wt = 1.f;
-            if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, &id, &wt);
+            if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, R.topk[0], &id, &wt);
             int rank = 0;
             for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(id, i) < id;
             if (lane < k) {
@@ -396,7 +397,7 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     for (int t = wv; t < T; t += kGemvThreads / 64) {
         int id = 0;
         float wt = 1.f;
-        if (!p.identity) wave_topk(p.logits + (size_t)t * p.E, p.E, k, p.renorm, lane, &id, &wt);
+        if (!p.identity) wave_topk(p.logits + (size_t)t * p.E, p.E, k, p.renorm, lane, R.topk[wv], &id, &wt);
         if (lane < k) {
             R.id[t * k + lane] = id;
             R.w[t * k + lane] = wt;
@@ -457,6 +458,28 @@ __device__ __forceinline__ float lds_sum8(const float* part, int base, int strid
     if (valid)
         for (int i = s; i < count; i += 8) v += part[base + i * stride];
     return group8_sum_f32(v);
+}
+
+// q[0] + q[1] + ... + q[n - 1], added in that order; q is 16-byte aligned LDS.
+__device__ __forceinline__ float sum_columns(const float* q, int n) {
+    const float4* q4 = reinterpret_cast<const float4*>(q);
+    float acc = 0.f;
+    int b = 0;
+#pragma unroll 2
+    for (; b + 4 <= n; b += 4) {
+        const float4 v = q4[b / 4];
+        acc += v.x;
+        acc += v.y;
+        acc += v.z;
+        acc += v.w;
+    }
+    if (b < n) {
+        const float4 v = q4[b / 4];
+        acc += v.x;
+        if (b + 1 < n) acc += v.y;
+        if (b + 2 < n) acc += v.z;
+    }
+    return acc;
 }
 
 template <int QT, int NT, int NTERM>
@@ -630,7 +653,12 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
             __builtin_amdgcn_s_sleep(1);
     }
 
-    // part[(unit * dn_rows + r) * NT + t]
+    // Partials part[((group * dn_rows + r) * NT + t) * nbp + b]: a (group, row,
+    // token)'s block columns are contiguous, padded to a multiple of 4.  Routed
+    // groups first, then shared groups from sh_off on.
+    const int D = p.dn_rows * NT;
+    const int nbp_r = (nb_r + 3) & ~3, nbp_s = (nb_s + 3) & ~3;
+    const int sh_off = ng * D * nbp_r;
     bool waited = false;
     for (int u0 = 0; u0 < n_units; u0 += per_round) {
         const int uu = u0 + tid / S, rs = tid - (tid / S) * S;
@@ -739,28 +767,24 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
                 if (r < nrows) {
                     float o[NT];
                     block_dot<QT, 2, NT>(c[i], half_bits_to_f32(sc[i]), xs, ntok, o);
+                    const int nbp = sh ? nbp_s : nbp_r;
+                    float* dst = lds + (sh ? sh_off : 0) + ((g * p.dn_rows + r) * NT) * nbp + b;
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) lds[((size_t)u * p.dn_rows + r) * NT + t] = o[t];
+                    for (int t = 0; t < NT; ++t) dst[t * nbp] = o[t];
                 }
             }
         }
     }
     __syncthreads();
-    // d of every (group, row, token): sum over the group's block columns in order.
-    float* dsum = lds + (size_t)n_units * p.dn_rows * NT;    // [(group or shared group) * dn_rows + r][t]
-    const int n_grp = ng + p.shared_groups;
-    const int n_items = n_grp * nrows * NT;
-    for (int it0 = 0; it0 < n_items; it0 += kGemvThreads / 8) {
-        const int it = it0 + tid / 8, s = tid & 7;
-        const bool valid = it < n_items;
-        const int gg = valid ? it / (nrows * NT) : 0;
-        const int r = valid ? (it / NT) % nrows : 0;
-        const int t = valid ? it % NT : 0;
-        const bool sh = gg >= ng;
-        const int nb = sh ? nb_s : nb_r;
-        const int u_first = sh ? ng * nb_r + (gg - ng) * nb_s : gg * nb_r;
-        const float v = lds_sum8(lds, (u_first * p.dn_rows + r) * NT + t, p.dn_rows * NT, nb, valid, s);
-        if (valid && s == 0) dsum[(gg * p.dn_rows + r) * NT + t] = v;
+    // d of every (group, row, token), item (group * dn_rows + r) * NT + t: its
+    // block-column partials summed in column order, one thread per item (items
+    // of rows past nrows are computed from unused LDS and never read).
+    float* dsum = lds + sh_off + p.shared_groups * D * nbp_s;
+    const int n_items = (ng + p.shared_groups) * D;
+    for (int i = tid; i < n_items; i += kGemvThreads) {
+        const bool sh = i >= ng * D;
+        const float* q = lds + (sh ? sh_off + (i - ng * D) * nbp_s : i * nbp_r);
+        dsum[i] = sum_columns(q, sh ? nb_s : nb_r);
     }
     __syncthreads();
     // y[t][h] = shared(t)[h] + sum_j w[t][j] * d(pair(t, j))[h], in this order.
@@ -783,7 +807,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
 
 template <int QT, int NT, int NTERM>
 __global__ void __launch_bounds__(kGemvThreads, NT == 1 ? 3 : 2) decode_layer_kernel(DecodeParams p) {
-    extern __shared__ float lds[];
+    extern __shared__ __align__(16) float lds[];   // 16-byte aligned: float4 reads
     __shared__ RouteLDS R;
     const int tid = threadIdx.x;
     route_and_bucket<NT>(p, R);
@@ -832,7 +856,10 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     // count does not change any summation order.
     const int nb_r = FF / qk, nb_s = FFs / qk;
     const size_t units = (size_t)g.max_groups * nb_r + (size_t)g.shared_groups * nb_s;
-    const size_t per_row = (units + g.max_groups + g.shared_groups) * NT * 4;
+    // partials padded to 4 columns per (group, row, token), plus one sum each
+    const size_t per_row =
+        ((size_t)g.max_groups * ((nb_r + 3) & ~3) + (size_t)g.shared_groups * ((nb_s + 3) & ~3) + g.max_groups +
+         g.shared_groups) * NT * 4;
     // One thread prefetches at most kRowsPerThread rows of its unit; with few
     // units, S = 256 / units threads share a unit's rows.
     int s_min = (int)(kGemvThreads / units);

@@ -2,8 +2,9 @@
 // weights"; kairos-engine README "The MoE forward": top-k over the router
 // logits).  Order: logit descending, expert index ascending on ties; -0 == +0;
 // NaN below every number.  One wavefront owns one token: each lane holds up to
-// 16 logits as 64-bit keys and k rounds of a DPP wave maximum pick the experts
-// in rank order.  Every comparison is on integers derived from the same fp32
+// 16 logits as 64-bit keys; the few at or above a ballot-searched threshold are
+// ranked against each other (k rounds of a DPP wave maximum when ties leave too
+// many).  Every comparison is on integers derived from the same fp32
 // values the oracle sorts, so ids are exact.  Weights: softmax over the k
 // selected logits, or the full softmax read at the selected experts.
 #include "moe_device.h"
@@ -15,12 +16,13 @@ namespace moe {
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int renorm, int* __restrict__ ids,
                                                          float* __restrict__ w) {
+    __shared__ uint64_t scratch[4][64];
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     int id;
     float wt;
-    wave_topk(logits + (size_t)t * E, E, k, renorm, lane, &id, &wt);
+    wave_topk(logits + (size_t)t * E, E, k, renorm, lane, scratch[threadIdx.x >> 6], &id, &wt);
     if (lane < k) {
         ids[(size_t)t * k + lane] = id;
         w[(size_t)t * k + lane] = wt;

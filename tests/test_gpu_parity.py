@@ -55,6 +55,64 @@ def test_route_topk_special_values():
         assert np.max(np.abs(wg[finite] - w_ref[finite])) <= 1e-6
 
 
+def _top_heavy_rows(E, k, seed):
+    """Logit rows built around how many logits reach the k-th largest maximum of
+    the 64 strided lanes (lane l holds experts l, l + 64, ...): the largest
+    logits crowded into one lane, exactly 64 and 65 logits tied at the top, and
+    ties on a value just below a few clear winners."""
+    rng = np.random.default_rng(seed)
+    base = rng.normal(size=E).astype(np.float32)
+    assert base.max() < 6.0
+    per_lane = E // 64
+    rows = []
+    a = base.copy()
+    a[3 + 64 * np.arange(per_lane)] = 10.0 + np.arange(per_lane, dtype=np.float32)
+    rows.append(a)
+    for n_tied in (64, 65):
+        b = base.copy()
+        b[rng.choice(E, n_tied, replace=False)] = 7.0
+        rows.append(b)
+    d = base.copy()
+    d[rng.choice(E, 3 * k, replace=False)] = 5.5
+    d[rng.choice(E, k // 2, replace=False)] = 9.0
+    rows.append(d)
+    e = base.copy()
+    e[64 * np.arange(per_lane)] = 8.0          # lane 0 holds a tied block
+    e[1 + 64 * np.arange(per_lane)] = 8.0      # and lane 1 another
+    rows.append(e)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("E,k", [(512, 10), (1024, 32), (256, 8), (128, 2)])
+def test_route_topk_crowded_and_tied_tops(E, k):
+    l = _top_heavy_rows(E, k, E + k)
+    for renorm in (True, False):
+        ids_ref, w_ref = oracle.route_topk(l, k, renorm)
+        ids, w = moe.route_topk(torch.from_numpy(l).to(DEV), k, renorm)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+        assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6
+
+
+def test_layer_routing_crowded_and_tied_tops():
+    """The fused decode kernel's own routing (T = 1 and a window of 5) on the same rows."""
+    E, k, H, FF = 512, 10, 256, 128
+    l = _top_heavy_rows(E, k, 5)
+    rng = np.random.default_rng(11)
+    blob = torch.from_numpy(random_expert(rng, 1, H, FF, 0.05)[0]).to(DEV)
+    table = torch.full((E,), blob.data_ptr(), dtype=torch.int64, device=DEV)
+    desc = moe.layer_desc(H, FF, 1, 1.5, E, k)
+    x = torch.from_numpy(rng.normal(size=(l.shape[0], H)).astype(np.float32)).to(DEV)
+    ids_ref, w_ref = oracle.route_topk(l, k, True)
+    for rows in [[t] for t in range(l.shape[0])] + [list(range(l.shape[0]))]:
+        T = len(rows)
+        ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        wts = torch.empty((T, k), dtype=torch.float32, device=DEV)
+        moe.layer_forward(desc, table, x[rows].contiguous(), torch.from_numpy(l[rows]).to(DEV), ids=ids,
+                          weights=wts)
+        np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref[rows])
+        assert np.max(np.abs(wts.cpu().numpy() - w_ref[rows])) <= 1e-6
+
+
 def test_route_topk_zipf_logits():
     for s, E, k in [(1.0, 512, 10), (0.8, 128, 8), (0.6, 256, 8)]:
         l = synth.logits(0, 3, 0, 300, E, s)
