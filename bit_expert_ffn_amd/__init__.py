@@ -109,7 +109,7 @@ def expert_workspace_bytes(desc, T):
 
 
 def workspace(nbytes, device):
-    """A workspace buffer: zeroed once, as the library requires of its first 256 bytes."""
+    """A workspace buffer, zeroed once as the library requires."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 

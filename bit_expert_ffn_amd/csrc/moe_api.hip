@@ -35,14 +35,16 @@ SmallLayout small_layout(int T, int k, int FF, int FFs) {
     SmallLayout L{};
     Bump b;
     const size_t n = (size_t)T * k;
-    L.sync = b.take(decode_sync_bytes(T * k + T));
+    L.sync = b.take(decode_sync_bytes(kSmallT * k + kSmallT));
+    L.a = b.take((size_t)kSmallT * k * FF * 4);
+    L.as = b.take((size_t)kSmallT * FFs * 4);
     L.ids = b.take(n * 4);
     L.w = b.take(n * 4);
-    L.a = b.take(n * FF * 4);
-    L.as = b.take((size_t)T * FFs * 4);
     L.total = b.off;
     return L;
 }
+
+size_t small_fixed_bytes(int k, int FF, int FFs) { return small_layout(0, k, FF, FFs).ids; }
 
 }  // namespace moe
 

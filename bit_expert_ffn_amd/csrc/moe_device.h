@@ -63,6 +63,22 @@ __device__ __forceinline__ uint32_t and_or(uint32_t d, uint32_t mask, uint32_t v
     return r;
 }
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
+// only, so that an outstanding global atomic whose result is not needed does
+// not hold the workgroup (a __syncthreads also waits for every global memory
+// operation).  The memory clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Relaxed device-scope atomic add whose result is not needed, issued so that
+// the compiler's wait tracking does not see it: later waits for unrelated
+// loads then do not wait for this atomic's round trip.  The expcnt wait
+// covers the hardware's reading of the operand registers before they are
+// reused.
+__device__ __forceinline__ void atomic_add_detached(int* p, int v) {
+    asm volatile("global_atomic_add %0, %1, off\n\ts_waitcnt expcnt(0)" ::"v"(p), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
@@ -108,14 +124,6 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Sum over aligned groups of 8 lanes (every lane active); each lane gets its group's sum.
-__device__ __forceinline__ float group8_sum_f32(float v) {
-    v = dpp_add_f32<kDppXor1>(v);
-    v = dpp_add_f32<kDppXor2>(v);
-    v = dpp_add_f32<kDppHalfMirror>(v);
-    return v;
-}
-
 // One wave: top-k of one token's E <= 64 * KPL logits (every lane active).
 // Lane l holds logits l, l + 64, ... (KPL slots) as 64-bit keys
 // order_bits(logit) << 32 | ~index, so that a larger key ranks first (higher
@@ -141,15 +149,16 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Threshold selection.  thr = the k-th largest of the 64 lane maxima of the
-// 32-bit order keys, found bit by bit from the top: a bit stays set when at
-// least k lane maxima reach the value with it.  The k lanes whose maxima reach
+// Threshold selection.  P = the largest 16-bit value that at least k of the
+// 64 lane maxima reach in their top 16 bits (a search two bits at a time, with
+// three ballot counts per step); thr = P << 16.  The k lanes whose maxima reach
 // thr hold k distinct elements >= thr, so the k-th largest element is >= thr
 // and every selected element is among those >= thr.  When at most 64 are, they
-// are gathered one per lane through `scratch` (64 keys of LDS owned by this
-// wave), each counts the larger keys among them, and the k of rank < k are
-// written back at their ranks.  Returns false (nothing selected) when more than
-// 64 elements reach thr; the outcome is uniform across the wave.
+// are gathered one per lane through `scratch` (128 keys of LDS owned by this
+// wave; slots 64.. take the writes of lanes with nothing to store), each counts
+// the larger keys among them, and the k of rank < k are written back at their
+// ranks.  Returns false (nothing selected) when more than 64 elements reach
+// thr; the outcome is uniform across the wave.
 template <int KPL>
 __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k, int lane, uint64_t* scratch,
                                                uint64_t* sel) {
@@ -160,11 +169,17 @@ __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k
         hi[i] = (uint32_t)(key[i] >> 32);
         lmax = hi[i] > lmax ? hi[i] : lmax;
     }
-    uint32_t thr = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t c = thr | (1u << b);
-        if (__popcll(__ballot(lmax >= c)) >= k) thr = c;
+    const uint32_t l16 = lmax >> 16;
+    uint32_t p = 0;
+#pragma unroll
+    for (int sh = 14; sh >= 0; sh -= 2) {
+        const uint32_t c1 = p | (1u << sh), c2 = p | (2u << sh), c3 = p | (3u << sh);
+        const int n1 = __popcll(__ballot(l16 >= c1));
+        const int n2 = __popcll(__ballot(l16 >= c2));
+        const int n3 = __popcll(__ballot(l16 >= c3));
+        p = n3 >= k ? c3 : (n2 >= k ? c2 : (n1 >= k ? c1 : p));
     }
+    const uint32_t thr = p << 16;
     uint64_t mask[KPL];
     int base[KPL];
     int n = 0;
@@ -176,16 +191,21 @@ __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k
     }
     if (n > 64) return false;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i)
-        if (hi[i] >= thr) scratch[base[i] + lanes_below(mask[i])] = key[i];
+    for (int i = 0; i < KPL; ++i) scratch[hi[i] >= thr ? base[i] + lanes_below(mask[i]) : 64 + lane] = key[i];
     // LDS accesses of one wave complete in program order; the barrier keeps the
     // compiler from moving them across each other.
     __builtin_amdgcn_wave_barrier();
     const uint64_t mine = lane < n ? scratch[lane] : 0ull;
+    // Lanes n.. hold key 0, which is larger than no key: the count may run on
+    // to a multiple of 8.
     int rank = 0;
-    for (int j = 0; j < n; ++j) rank += readlane_u64(mine, j) > mine;
+    const int n8 = (n + 7) & ~7;
+    for (int j = 0; j < n8; j += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += readlane_u64(mine, j + u) > mine;
+    }
     __builtin_amdgcn_wave_barrier();
-    if (lane < n && rank < k) scratch[rank] = mine;
+    scratch[lane < n && rank < k ? rank : 64 + lane] = mine;
     __builtin_amdgcn_wave_barrier();
     *sel = lane < k ? scratch[lane] : 0ull;
     __builtin_amdgcn_wave_barrier();
@@ -300,7 +320,7 @@ __device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int
     *out_w = e_sel / denom;
 }
 
-// `scratch`: 64 keys of LDS owned by the calling wave.
+// `scratch`: 128 keys of LDS owned by the calling wave.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm, int lane,
                                           uint64_t* scratch, int* out_id, float* out_w) {
     if (E <= 128) wave_topk_kpl<2>(row, E, k, renorm, lane, scratch, out_id, out_w);

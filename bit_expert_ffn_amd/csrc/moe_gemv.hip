@@ -191,20 +191,16 @@ __device__ __forceinline__ void load_slice_f32(XSlice<QT, 2>& s, const float* sr
     finish_slice<QT, 2>(s, z);
 }
 
-// A slice stored as packed words pk[j] = bf16 hi(v_j) | bf16 lo(v_j) << 16 (the
-// SwiGLU output as the gate/up stage publishes it): de-interleave into the two
-// terms' dot pairs.
+// A slice stored as packed words w[j] = bf16 hi(v_j) | bf16 lo(v_j) << 16 (the
+// SwiGLU output as the gate/up stage publishes it).  `a` is read with
+// agent-coherent (sc1) buffer loads: it is written by other workgroups,
+// possibly on other XCDs, and these loads see it without invalidating this
+// XCD's L2.  Returns whether every word has been written (is non-zero).
 template <int QT>
-// `a` is read with agent-coherent (sc1) buffer loads: it was written by other
-// workgroups, possibly on other XCDs, before their ready flags were raised, so
-// these loads see it without invalidating this XCD's L2.
-__device__ __forceinline__ void load_slice_packed(XSlice<QT, 2>& s, __amdgpu_buffer_rsrc_t rsrc, uint32_t byte_off,
-                                                  float z) {
+__device__ __forceinline__ bool load_packed_words(uint32_t (&w)[QTraits<QT>::QK], __amdgpu_buffer_rsrc_t rsrc,
+                                                  uint32_t byte_off) {
     constexpr int QK = QTraits<QT>::QK;
-    constexpr int HALF = QT == 1 ? 8 : 4;   // pair (v, v + HALF) within a dword's codes
-    constexpr int PER = QT == 1 ? 16 : 8;   // values per code dword
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    uint32_t w[QK];
 #pragma unroll
     for (int v = 0; v < QK / 4; ++v) {
         const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(byte_off + 16 * v), 0, kCpolSc1);
@@ -213,6 +209,17 @@ __device__ __forceinline__ void load_slice_packed(XSlice<QT, 2>& s, __amdgpu_buf
         w[4 * v + 2] = u[2];
         w[4 * v + 3] = u[3];
     }
+    uint32_t m = w[0];
+#pragma unroll
+    for (int i = 1; i < QK; ++i) m = w[i] < m ? w[i] : m;
+    return m != 0u;
+}
+
+// De-interleave packed words into the two terms' dot pairs.
+template <int QT>
+__device__ __forceinline__ void slice_from_packed(XSlice<QT, 2>& s, const uint32_t (&w)[QTraits<QT>::QK], float z) {
+    constexpr int HALF = QT == 1 ? 8 : 4;   // pair (v, v + HALF) within a dword's codes
+    constexpr int PER = QT == 1 ? 16 : 8;   // values per code dword
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -224,7 +231,20 @@ __device__ __forceinline__ void load_slice_packed(XSlice<QT, 2>& s, __amdgpu_buf
     finish_slice<QT, 2>(s, z);
 }
 
-// sum_i s * (c_i - z) x_i of one block for NT tokens (ntok valid).
+// A SwiGLU output as the gate/up stage publishes it: two bf16 terms hi + lo
+// (relative error <= 2^-17) in one word, hi | lo << 16.  The word is never 0:
+// a value that rounds to +0 is stored as -0 (0x8000), a NaN as the canonical
+// quiet NaN, so 0 marks a word not yet written.
+__device__ __forceinline__ uint32_t pack_a(float a) {
+    if (a != a) a = __uint_as_float(0x7FC00000u);
+    const uint32_t hi = bf16_rne(a);
+    const uint32_t lo = bf16_rne(a - bf16_to_f32(hi));
+    const uint32_t w = hi | (lo << 16);
+    return w == 0u ? 0x8000u : w;
+}
+
+// sum_i s * (c_i - z) x_i of one block for NT tokens (ntok valid; one token
+// needs no check, which keeps the code free of branches).
 template <int QT, int NTERM, int NT>
 __device__ __forceinline__ void block_dot(const uint4 codes, float scale, const XSlice<QT, NTERM> (&xs)[NT],
                                           int ntok, float (&out)[NT]) {
@@ -252,7 +272,7 @@ __device__ __forceinline__ void block_dot(const uint4 codes, float scale, const 
             p[7] = and_or(D12, 0x000C000Cu, mg);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                if (t < ntok) {
+                if (NT == 1 || t < ntok) {
 #pragma unroll
                     for (int tm = 0; tm < NTERM; ++tm)
 #pragma unroll
@@ -268,7 +288,7 @@ __device__ __forceinline__ void block_dot(const uint4 codes, float scale, const 
             p[3] = and_or(D >> 12, 0x000F000Fu, mg);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                if (t < ntok) {
+                if (NT == 1 || t < ntok) {
 #pragma unroll
                     for (int tm = 0; tm < NTERM; ++tm)
 #pragma unroll
@@ -317,7 +337,7 @@ constexpr size_t kDecodeLdsBudget = 112 * 1024;   // dynamic LDS of the fused de
 constexpr int kMaxRowsDn = 12;               // H rows per down workgroup
 constexpr int kRowsPerThread = 6;            // down rows one thread prefetches
 constexpr long kSpinLimit = 1l << 22;
-constexpr int kExitFan = 16;                 // first-level exit counters
+constexpr int kLoadFan = 16;                 // counters of the down workgroups done loading `a`
 
 struct DecodeParams {
     const void* const* table;
@@ -337,14 +357,14 @@ struct DecodeParams {
     int gu_passes, tiles_gu, tiles_gu_s, max_groups, shared_groups, n_gu;
     int dn_rows, tiles_dn;
     int n_ready;                 // ready-flag replicas in use: min(kReadyReplicas, tiles_dn)
+    int stage_words;             // `a` words each down workgroup copies to LDS first (one token), else 0
 };
 
 // Word offsets inside the synchronisation area (ints; 16 ints = one 64-byte line).
 __device__ __forceinline__ int* sync_group(int* s, int g) { return s + 16 * (4 + g); }
-__device__ __forceinline__ int* sync_groups_done(int* s) { return s; }
 __device__ __forceinline__ int* sync_error(int* s) { return s + 16; }
-__device__ __forceinline__ int* sync_exit_top(int* s) { return s + 32; }
-__device__ __forceinline__ int* sync_exit(int* s, int i, int max_groups) { return s + 16 * (4 + max_groups + i); }
+// Count i of the down workgroups done loading `a` (workgroup tile counts in i = tile % kLoadFan).
+__device__ __forceinline__ int* sync_loaded(int* s, int i, int n_ctr) { return s + 16 * (4 + n_ctr + i); }
 // Ready flag of group g in replica r (replicas kReadyStride bytes apart, after the lines above).
 __device__ __forceinline__ int* sync_ready(int* s, int r, int g, int n_ctr) {
     const size_t lines = (decode_sync_lines_bytes(n_ctr) + kReadyStride - 1) / kReadyStride * kReadyStride;
@@ -358,7 +378,7 @@ struct RouteLDS {
     int group_first[kMaxPairs], group_n[kMaxPairs], group_of_pair[kMaxPairs];
     int rank[kMaxPairs], pos[kMaxPairs], cnt[kMaxPairs];
     int slot_src[kMaxPairs];   // slot (t, j) -> group * NT + token-in-group of its pair
-    uint64_t topk[kGemvThreads / 64][64];   // each wave's top-k scratch
+    uint64_t topk[kGemvThreads / 64][128];   // each wave's top-k scratch
     int n_groups;
     int flag;
 };
@@ -371,23 +391,22 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k, T = p.T;
     if (T == 1) {
-        // One token: the pairs are its k slots, sorted by expert; each is its own group.
+        // One token: each of its k slots is its own pair and group, in rank
+        // order (group numbering changes no arithmetic).
         if (wv == 0) {
             int id = 0;
             float wt = 1.f;
             if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, R.topk[0], &id, &wt);
-            int rank = 0;
-            for (int i = 0; i < k; ++i) rank += __builtin_amdgcn_readlane(id, i) < id;
             if (lane < k) {
                 R.id[lane] = id;
                 R.w[lane] = wt;
-                R.slot_pair[lane] = rank;
-                R.pair_tok[rank] = 0;
-                R.pair_exp[rank] = id;
-                R.group_first[rank] = rank;
-                R.group_n[rank] = 1;
-                R.group_of_pair[rank] = rank;
-                R.slot_src[lane] = rank * NT;
+                R.slot_pair[lane] = lane;
+                R.pair_tok[lane] = 0;
+                R.pair_exp[lane] = id;
+                R.group_first[lane] = lane;
+                R.group_n[lane] = 1;
+                R.group_of_pair[lane] = lane;
+                R.slot_src[lane] = lane * NT;
             }
             if (lane == 0) R.n_groups = k;
         }
@@ -450,16 +469,6 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     __syncthreads();
 }
 
-// Sum of `count` LDS partials part[base + i * stride] by 8 lanes: lane s adds
-// i = s, s + 8, ... in order, then the 8 lanes combine by DPP.  Called by every
-// lane of the wave; lanes with valid == false contribute 0.
-__device__ __forceinline__ float lds_sum8(const float* part, int base, int stride, int count, bool valid, int s) {
-    float v = 0.f;
-    if (valid)
-        for (int i = s; i < count; i += 8) v += part[base + i * stride];
-    return group8_sum_f32(v);
-}
-
 // q[0] + q[1] + ... + q[n - 1], added in that order; q is 16-byte aligned LDS.
 __device__ __forceinline__ float sum_columns(const float* q, int n) {
     const float4* q4 = reinterpret_cast<const float4*>(q);
@@ -480,6 +489,29 @@ __device__ __forceinline__ float sum_columns(const float* q, int n) {
         if (b + 2 < n) acc += v.z;
     }
     return acc;
+}
+
+// The same sum in four interleaved chains (column j in chain j % 4), combined
+// as (c0 + c1) + (c2 + c3).
+__device__ __forceinline__ float sum_columns4(const float* q, int n) {
+    const float4* q4 = reinterpret_cast<const float4*>(q);
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+    int b = 0;
+#pragma unroll 4
+    for (; b + 4 <= n; b += 4) {
+        const float4 v = q4[b / 4];
+        c0 += v.x;
+        c1 += v.y;
+        c2 += v.z;
+        c3 += v.w;
+    }
+    if (b < n) {
+        const float4 v = q4[b / 4];
+        c0 += v.x;
+        if (b + 1 < n) c1 += v.y;
+        if (b + 2 < n) c2 += v.z;
+    }
+    return (c0 + c1) + (c2 + c3);
 }
 
 template <int QT, int NT, int NTERM>
@@ -556,7 +588,9 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         else
             load_slice_f32<QT>(xs[t], (const float*)p.x + (size_t)toks[t] * p.H + b * QK, p.z);
     }
-    // part[(mat * Rr + rr) * nblk + b][t]
+    // Partials part[((mat * Rr + rr) * NT + t) * nbp + b]: a row's block
+    // columns are contiguous, padded to a multiple of 4.
+    const int nbp = (nblk + 3) & ~3;
 #pragma unroll
     for (int m = 0; m < kMaxPass; ++m) {
         const int f = f0 + m * P + rp;
@@ -567,39 +601,27 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
             const int rr = m * P + rp;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                lds[((0 * Rr + rr) * nblk + b) * NT + t] = og[t];
-                lds[((1 * Rr + rr) * nblk + b) * NT + t] = ou[t];
+                lds[((0 * Rr + rr) * NT + t) * nbp + b] = og[t];
+                lds[((1 * Rr + rr) * NT + t) * nbp + b] = ou[t];
             }
         }
     }
     __syncthreads();
-    // Row sums: item (mat, rr, t) by 8 lanes; results to red[(mat * Rr + rr) * NT + t].
-    float* red = lds + 2 * Rr * nblk * NT;
-    const int n_items = 2 * Rr * NT;
-    for (int it0 = 0; it0 < n_items; it0 += kGemvThreads / 8) {
-        const int it = it0 + tid / 8, s = tid & 7;
-        const bool valid = it < n_items;
-        const int mat = valid ? it / (Rr * NT) : 0;
-        const int rr = valid ? (it / NT) % Rr : 0;
-        const int t = valid ? it % NT : 0;
-        const float v = lds_sum8(lds, ((mat * Rr + rr) * nblk) * NT + t, NT, nblk, valid, s);
-        if (valid && s == 0) red[(mat * Rr + rr) * NT + t] = v;
-    }
-    __syncthreads();
+    // One thread per (row, token): both row sums, SwiGLU, the store.
     for (int i = tid; i < Rr * NT; i += kGemvThreads) {
         const int rr = i / NT, t = i - rr * NT;
         const int f = f0 + rr;
         if (f >= rows || t >= ntok) continue;
-        const float g = red[(0 * Rr + rr) * NT + t];
-        const float u = red[(1 * Rr + rr) * NT + t];
+        const float g = sum_columns4(lds + ((0 * Rr + rr) * NT + t) * nbp, nblk);
+        const float u = sum_columns4(lds + ((1 * Rr + rr) * NT + t) * nbp, nblk);
         const float a = g / (1.f + expf(-g)) * u;
-        // two bf16 terms hi + lo (relative error <= 2^-17), split once here
-        const uint32_t hi = bf16_rne(a);
-        const uint32_t lo = bf16_rne(a - bf16_to_f32(hi));
-        __hip_atomic_store(out + (size_t)outrow[t] * rows + f, hi | (lo << 16), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(out + (size_t)outrow[t] * rows + f, pack_a(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();   // every store above has completed (the barrier waits for them)
+    // Every store above has completed (the barrier waits for them), so a flag
+    // raised after this count is seen after the words.  Readers still check
+    // each word (see pack_a): a flag that ran ahead would cost a reload, not a
+    // wrong value.
+    __syncthreads();
     // Count this tile; the tile that completes its group raises the group's
     // ready flag in every replica (down workgroups each poll one replica).
     if (tid < 64) {
@@ -616,6 +638,80 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         // lands late only starts a later call's prefetch early.
         if (old == 0 && tid < p.n_ready)
             __hip_atomic_store(sync_ready(p.sync, tid, n_ctr, n_ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// One token: the down workgroup copies every `a` word it reads (the routed
+// rows 0..ng-1, then the shared row) into LDS once, with LDS DMA (no
+// registers held), instead of each thread loading its own slices (which would
+// read the same words several times).  The 16-byte chunks of a slice of QK
+// words are stored in XOR-swizzled order, chunk v of slice s at position
+// v ^ (s % CPS), so that the slice reads of a wave spread over every LDS bank.
+// Each thread then checks the chunks its lane brought in and reads again any
+// with a word still 0.
+constexpr int kStagePasses = 8;                             // 16-byte chunks per thread
+constexpr int kStageMaxWords = kStagePasses * kGemvThreads * 4;
+
+__host__ __device__ constexpr int stage_bytes(int words) {   // whole passes of 256 chunks
+    return (words / 4 + kGemvThreads - 1) / kGemvThreads * kGemvThreads * 16;
+}
+
+// LDS DMA of 16 bytes per lane with an agent-coherent (sc1) read: lane i's
+// chunk lands at dst_wave + 16 i.
+__device__ __forceinline__ void load_lds16_sc1(const void* src, uint8_t* dst_wave) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst_wave, 16, 0, kCpolSc1);
+}
+
+template <int QK>
+__device__ __forceinline__ uint32_t stage_src_off(int q, int routed_words, uint32_t as_off) {
+    constexpr int CPS = QK / 4;
+    const int sl = q / CPS, v = (q % CPS) ^ (sl % CPS);
+    const int wd = sl * QK + 4 * v;
+    return wd < routed_words ? 4u * (uint32_t)wd : as_off + 4u * (uint32_t)(wd - routed_words);
+}
+
+template <int QK>
+__device__ __forceinline__ void stage_a(const DecodeParams& p, __amdgpu_buffer_rsrc_t rsrc, const uint8_t* a_base,
+                                        uint32_t as_off, int routed_words, uint8_t* dst) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int tid = threadIdx.x, wv = tid >> 6;
+    int lane = tid & 63;
+    // The addresses below are computed here, not hoisted to the start of the
+    // caller (where holding them would spill registers).
+    asm volatile("" : "+v"(lane));
+    const int n_chunks = p.stage_words / 4;
+    // Pass j of wave wv fills LDS chunks [64 (4 j + wv), +64): lane i the i-th.
+    // Positions past the last chunk (inside the last pass) take a copy of it.
+#pragma unroll
+    for (int j = 0; j < kStagePasses; ++j) {
+        const int q0 = 64 * (4 * j + wv);
+        if (q0 < n_chunks) {
+            const int q = min(q0 + lane, n_chunks - 1);
+            load_lds16_sc1(a_base + stage_src_off<QK>(q, routed_words, as_off), dst + 16 * q0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < kStagePasses; ++j) {
+        const int q0 = 64 * (4 * j + wv);
+        if (q0 < n_chunks && q0 + lane < n_chunks) {
+            const int q = q0 + lane;
+            u32x4* slot = reinterpret_cast<u32x4*>(dst + 16 * q);
+            u32x4 v = *slot;
+            if (min(min(v[0], v[1]), min(v[2], v[3])) == 0u) {   // not landed yet (rare): read it again
+                long spins = 0;
+                const uint32_t off = stage_src_off<QK>(q, routed_words, as_off);
+                do {
+                    if (++spins > kSpinLimit) {
+                        __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                    v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, kCpolSc1);
+                } while (min(min(v[0], v[1]), min(v[2], v[3])) == 0u);
+                *slot = v;
+            }
+        }
     }
 }
 
@@ -659,6 +755,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
     const int D = p.dn_rows * NT;
     const int nbp_r = (nb_r + 3) & ~3, nbp_s = (nb_s + 3) & ~3;
     const int sh_off = ng * D * nbp_r;
+    float* part = lds + (p.stage_words ? stage_bytes(p.stage_words) / 4 : 0);   // after the staged `a`, if any
     bool waited = false;
     for (int u0 = 0; u0 < n_units; u0 += per_round) {
         const int uu = u0 + tid / S, rs = tid - (tid / S) * S;
@@ -720,47 +817,55 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
             }
             __syncthreads();
             waited = true;
-            // Two-level count of the down workgroups that are past their wait; the
-            // last one returns every counter and flag to zero for the next call
-            // (no workgroup reads them any more).
-            if (tid == 0) {
-                const int fan = min(kExitFan, p.tiles_dn);
-                const int i = tile % fan;
-                const int members = (p.tiles_dn - i + fan - 1) / fan;
-                int last = 0;
-                if (__hip_atomic_fetch_add(sync_exit(p.sync, i, p.max_groups + p.shared_groups), 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) == members - 1)
-                    last = __hip_atomic_fetch_add(sync_exit_top(p.sync), 1, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT) == fan - 1;
-                R.flag = last;
-            }
-            __syncthreads();
-            if (R.flag) {
-                const int n_ctr = p.max_groups + p.shared_groups;
-                const int fan = min(kExitFan, p.tiles_dn);
-                for (int i = tid; i < n_ctr; i += kGemvThreads)
-                    __hip_atomic_store(sync_group(p.sync, i), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                for (int i = tid; i < p.n_ready * (n_ctr + 1); i += kGemvThreads)
-                    __hip_atomic_store(sync_ready(p.sync, i / (n_ctr + 1), i % (n_ctr + 1), n_ctr), 0,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                for (int i = tid; i < fan; i += kGemvThreads)
-                    __hip_atomic_store(sync_exit(p.sync, i, n_ctr), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (tid == 0) {
-                    __hip_atomic_store(sync_groups_done(p.sync), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(sync_exit_top(p.sync), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+            if (p.stage_words) {
+                stage_a<QK>(p, a_rsrc, reinterpret_cast<const uint8_t*>(p.a), as_off, ng * p.FF,
+                            reinterpret_cast<uint8_t*>(lds));
+                // Every load has landed; saying so leaves the compiler no load
+                // to wait for after the atomic below.
+                __builtin_amdgcn_s_waitcnt(0);
+                lds_barrier();
+                // Every `a` word this workgroup reads is in LDS: count the
+                // workgroup (without waiting for the atomic).
+                if (tid == 0)
+                    atomic_add_detached(sync_loaded(p.sync, tile % kLoadFan, p.max_groups + p.shared_groups), 1);
             }
         }
+        XSlice<QT, 2> xs[NT];
+        const bool sh = u >= ng * nb_r;
         if (act) {
-            XSlice<QT, 2> xs[NT];
-            const bool sh = u >= ng * nb_r;
             const uint32_t base = sh ? as_off : 0u;   // byte offset of this unit's `a` rows
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int tt = t < ntok ? t : 0;
                 const int row = sh ? g * NT + tt : R.group_first[g] + tt;
-                load_slice_packed<QT>(xs[t], a_rsrc, base + 4u * (uint32_t)(row * K + b * QK), p.z);
+                const uint32_t off = base + 4u * (uint32_t)(row * K + b * QK);
+                uint32_t w[QK];
+                if (p.stage_words) {
+                    const int slice = ((sh ? ng * p.FF : 0) + row * K) / QK + b;
+                    const uint4* src = reinterpret_cast<const uint4*>(lds) + slice * (QK / 4);
+#pragma unroll
+                    for (int v = 0; v < QK / 4; ++v) {
+                        const uint4 q = src[v ^ (slice % (QK / 4))];
+                        w[4 * v + 0] = q.x;
+                        w[4 * v + 1] = q.y;
+                        w[4 * v + 2] = q.z;
+                        w[4 * v + 3] = q.w;
+                    }
+                } else {
+                    // A word still 0 has not landed yet: read the slice again.
+                    long spins = 0;
+                    while (!load_packed_words<QT>(w, a_rsrc, off)) {
+                        if (++spins > kSpinLimit) {
+                            __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                slice_from_packed<QT>(xs[t], w, p.z);
             }
+        }
+        if (act) {
 #pragma unroll
             for (int i = 0; i < kRowsPerThread; ++i) {
                 const int r = rs + i * S;
@@ -768,25 +873,35 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
                     float o[NT];
                     block_dot<QT, 2, NT>(c[i], half_bits_to_f32(sc[i]), xs, ntok, o);
                     const int nbp = sh ? nbp_s : nbp_r;
-                    float* dst = lds + (sh ? sh_off : 0) + ((g * p.dn_rows + r) * NT) * nbp + b;
+                    float* dst = part + (sh ? sh_off : 0) + ((g * p.dn_rows + r) * NT) * nbp + b;
 #pragma unroll
                     for (int t = 0; t < NT; ++t) dst[t * nbp] = o[t];
                 }
             }
         }
     }
-    __syncthreads();
+    if (!p.stage_words) {
+        // Every load of this workgroup has landed (its results are used); saying
+        // so leaves the compiler no load to wait for after the atomic below.
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        // Every `a` word this workgroup reads has been used: count the workgroup
+        // (without waiting for the atomic).
+        if (tid == 0) atomic_add_detached(sync_loaded(p.sync, tile % kLoadFan, p.max_groups + p.shared_groups), 1);
+    } else {
+        lds_barrier();
+    }
     // d of every (group, row, token), item (group * dn_rows + r) * NT + t: its
     // block-column partials summed in column order, one thread per item (items
     // of rows past nrows are computed from unused LDS and never read).
-    float* dsum = lds + sh_off + p.shared_groups * D * nbp_s;
+    float* dsum = part + sh_off + p.shared_groups * D * nbp_s;
     const int n_items = (ng + p.shared_groups) * D;
     for (int i = tid; i < n_items; i += kGemvThreads) {
         const bool sh = i >= ng * D;
-        const float* q = lds + (sh ? sh_off + (i - ng * D) * nbp_s : i * nbp_r);
+        const float* q = part + (sh ? sh_off + (i - ng * D) * nbp_s : i * nbp_r);
         dsum[i] = sum_columns(q, sh ? nb_s : nb_r);
     }
-    __syncthreads();
+    lds_barrier();
     // y[t][h] = shared(t)[h] + sum_j w[t][j] * d(pair(t, j))[h], in this order.
     for (int i = tid; i < p.T * nrows; i += kGemvThreads) {
         const int t = i / nrows, r = i - t * nrows;
@@ -805,6 +920,55 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
 
 }
 
+// The workgroup after the down tiles returns the call's shared state to zero
+// for the next call, off every other workgroup's path: once every ready flag
+// of every replica is up (so every gate/up counter update has landed) and
+// every down workgroup has counted its `a` words as loaded (so every `a` store
+// has landed and no one reads `a` again), it clears the counters, the flags,
+// the load count and the `a` words of this call.
+template <int NT>
+__device__ void janitor_role(const DecodeParams& p, RouteLDS& R) {
+    const int tid = threadIdx.x;
+    const int ng = R.n_groups, nsg = p.shared_groups, n_ctr = p.max_groups + p.shared_groups;
+    const int n_flags = p.n_ready * (ng + nsg);
+    for (int i = tid; i < n_flags; i += kGemvThreads) {
+        const int r = i / (ng + nsg), gi = i - r * (ng + nsg);
+        const int ctr = gi < ng ? gi : p.max_groups + (gi - ng);
+        long spins = 0;
+        while (__hip_atomic_load(sync_ready(p.sync, r, ctr, n_ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+            if (++spins > kSpinLimit) {
+                __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    const int fan = min(kLoadFan, p.tiles_dn);
+    if (tid < fan) {
+        const int members = (p.tiles_dn - tid + kLoadFan - 1) / kLoadFan;
+        long spins = 0;
+        while (__hip_atomic_load(sync_loaded(p.sync, tid, n_ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               members) {
+            if (++spins > kSpinLimit) {
+                __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < n_ctr; i += kGemvThreads)
+        __hip_atomic_store(sync_group(p.sync, i), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < p.n_ready * (n_ctr + 1); i += kGemvThreads)
+        __hip_atomic_store(sync_ready(p.sync, i / (n_ctr + 1), i % (n_ctr + 1), n_ctr), 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < fan) __hip_atomic_store(sync_loaded(p.sync, tid, n_ctr), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int na = p.max_groups * p.FF, nas = p.T * p.FFs;
+    for (int i = tid; i < na; i += kGemvThreads) __hip_atomic_store(p.a + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = tid; i < nas; i += kGemvThreads)
+        __hip_atomic_store(p.as + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int QT, int NT, int NTERM>
 __global__ void __launch_bounds__(kGemvThreads, NT == 1 ? 3 : 2) decode_layer_kernel(DecodeParams p) {
     extern __shared__ __align__(16) float lds[];   // 16-byte aligned: float4 reads
@@ -819,7 +983,8 @@ __global__ void __launch_bounds__(kGemvThreads, NT == 1 ? 3 : 2) decode_layer_ke
         }
     }
     if (wg < p.n_gu) gateup_role<QT, NT, NTERM>(p, R, wg, lds);
-    else down_role<QT, NT>(p, R, wg - p.n_gu, lds);
+    else if (wg - p.n_gu < p.tiles_dn) down_role<QT, NT>(p, R, wg - p.n_gu, lds);
+    else janitor_role<NT>(p, R);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -867,13 +1032,17 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     int rows = (H + 255) / 256;
     rows = rows < 1 ? 1 : (rows > kMaxRowsDn ? kMaxRowsDn : rows);
     if (rows > kRowsPerThread * s_min) rows = kRowsPerThread * s_min;
-    while (rows > 1 && per_row * rows > kDecodeLdsBudget) --rows;
+    // One token: the `a` words are staged in LDS ahead of the partials.
+    const long words = (long)g.max_groups * FF + FFs;
+    g.stage_words = (T == 1 && words <= kStageMaxWords) ? (int)words : 0;
+    const size_t stage = g.stage_words ? (size_t)stage_bytes(g.stage_words) : 0;
+    while (rows > 1 && per_row * rows + stage > kDecodeLdsBudget) --rows;
     g.tile_rows_dn = rows;
     g.tiles_dn = (H + rows - 1) / rows;
-    const size_t lds_dn = per_row * rows;
-    const size_t lds_gu = ((size_t)2 * g.tile_rows_gu * nblk_gu * NT + (size_t)2 * g.tile_rows_gu * NT) * 4;
+    const size_t lds_dn = per_row * rows + stage;
+    const size_t lds_gu = (size_t)2 * g.tile_rows_gu * ((nblk_gu + 3) & ~3) * NT * 4;
     g.lds_bytes = lds_dn > lds_gu ? lds_dn : lds_gu;
-    g.grid = g.n_gu + g.tiles_dn;
+    g.grid = g.n_gu + g.tiles_dn + 1;   // + the workgroup that resets the shared state
     return g;
 }
 
@@ -929,6 +1098,7 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
     p.dn_rows = g.tile_rows_dn;
     p.tiles_dn = g.tiles_dn;
     p.n_ready = g.tiles_dn < kReadyReplicas ? g.tiles_dn : kReadyReplicas;
+    p.stage_words = g.stage_words;
     stage_mark(marks, s);
     hipError_t e;
     if (T == 1)

@@ -38,10 +38,15 @@ __host__ __device__ inline size_t decode_sync_bytes(int max_groups_total) {
 
 // Workspace layout for the GEMV path (T <= kSmallT), byte offsets.
 struct SmallLayout {
+    // The first three regions sit at the same offsets for every T <= kSmallT
+    // (sized for kSmallT tokens), and the matrix-core layout starts after
+    // them, so that calls of any size can share one workspace: the sync
+    // words, and `a`, whose words are never 0 once written and are returned
+    // to 0 by each call that wrote them.
     size_t sync;
+    size_t a;                // [T*k][FF] SwiGLU output per (expert, token) pair, packed bf16 hi | lo << 16
+    size_t as;               // [T][FFs] the shared expert's
     size_t ids, w;           // [T][k] routing when the caller passes no output
-    size_t a;                // [T*k][FF] fp32 SwiGLU output per (expert, token) pair
-    size_t as;               // [T][FFs] fp32 shared expert's
     size_t total;
 };
 
@@ -64,11 +69,13 @@ struct GemvShape {
     int gu_passes, tile_rows_gu, tiles_gu, tiles_gu_s;
     int max_groups, shared_groups, n_gu;
     int tile_rows_dn, tiles_dn;
+    int stage_words;          // `a` words each down workgroup stages in LDS (one token), else 0
     size_t lds_bytes;
     int grid;
 };
 
 SmallLayout small_layout(int T, int k, int FF, int FFs);
+size_t small_fixed_bytes(int k, int FF, int FFs);   // sync + a + as: where every layout's own regions start
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype);
 GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k);
 

@@ -40,8 +40,10 @@
  *     calls that share a workspace must be ordered (same stream, or events).
  *   - Workspace: a device buffer of at least the *_workspace_bytes size,
  *     256-byte aligned, ZERO-FILLED ONCE after allocation.  Its leading bytes
- *     hold synchronisation counters of the decode kernel, which every call
- *     returns to zero; the rest is scratch.
+ *     hold the decode kernel's state (synchronisation words and the hand-off
+ *     buffer between its gate/up and down stages), which every call returns
+ *     to zero; the rest is scratch.  One workspace may serve calls of any T,
+ *     decode and prefill alike (size it for the largest).
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H
