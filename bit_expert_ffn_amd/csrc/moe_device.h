@@ -111,6 +111,16 @@ __device__ __forceinline__ float dpp_add_f32(float v) {
     return v + __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
 }
 
+// Sum over each row of 16 lanes in a fixed order (deterministic); every lane
+// of the row gets the row's sum.
+__device__ __forceinline__ float row_sum_f32(float v) {
+    v = dpp_add_f32<kDppXor1>(v);
+    v = dpp_add_f32<kDppXor2>(v);
+    v = dpp_add_f32<kDppHalfMirror>(v);
+    v = dpp_add_f32<kDppMirror>(v);
+    return v;
+}
+
 // Sum over the 64 lanes of a wave in a fixed order (deterministic); uniform result.
 __device__ __forceinline__ float wave_sum_f32(float v) {
     v = dpp_add_f32<kDppXor1>(v);

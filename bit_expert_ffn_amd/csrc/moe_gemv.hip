@@ -691,26 +691,31 @@ __device__ __forceinline__ void stage_a(const DecodeParams& p, __amdgpu_buffer_r
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Check every chunk this lane brought in (one LDS read each, all issued
+    // together); the rare chunk with a word still 0 is read again.
+    uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
     for (int j = 0; j < kStagePasses; ++j) {
-        const int q0 = 64 * (4 * j + wv);
-        if (q0 < n_chunks && q0 + lane < n_chunks) {
-            const int q = q0 + lane;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(dst + 16 * min(64 * (4 * j + wv) + lane, n_chunks - 1));
+        m = min(m, min(min(v[0], v[1]), min(v[2], v[3])));
+    }
+    if (m == 0u) {
+        for (int j = 0; j < kStagePasses; ++j) {
+            const int q = 64 * (4 * j + wv) + lane;
+            if (q >= n_chunks) break;
             u32x4* slot = reinterpret_cast<u32x4*>(dst + 16 * q);
             u32x4 v = *slot;
-            if (min(min(v[0], v[1]), min(v[2], v[3])) == 0u) {   // not landed yet (rare): read it again
-                long spins = 0;
-                const uint32_t off = stage_src_off<QK>(q, routed_words, as_off);
-                do {
-                    if (++spins > kSpinLimit) {
-                        __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                    v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, kCpolSc1);
-                } while (min(min(v[0], v[1]), min(v[2], v[3])) == 0u);
-                *slot = v;
+            long spins = 0;
+            while (min(min(v[0], v[1]), min(v[2], v[3])) == 0u) {
+                if (++spins > kSpinLimit) {
+                    __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)stage_src_off<QK>(q, routed_words, as_off), 0,
+                                                          kCpolSc1);
             }
+            *slot = v;
         }
     }
 }
@@ -891,33 +896,33 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
     } else {
         lds_barrier();
     }
-    // d of every (group, row, token), item (group * dn_rows + r) * NT + t: its
-    // block-column partials summed in column order, one thread per item (items
-    // of rows past nrows are computed from unused LDS and never read).
-    float* dsum = part + sh_off + p.shared_groups * D * nbp_s;
-    const int n_items = (ng + p.shared_groups) * D;
-    for (int i = tid; i < n_items; i += kGemvThreads) {
-        const bool sh = i >= ng * D;
-        const float* q = part + (sh ? sh_off + (i - ng * D) * nbp_s : i * nbp_r);
-        dsum[i] = sum_columns(q, sh ? nb_s : nb_r);
-    }
-    lds_barrier();
-    // y[t][h] = shared(t)[h] + sum_j w[t][j] * d(pair(t, j))[h], in this order.
-    for (int i = tid; i < p.T * nrows; i += kGemvThreads) {
-        const int t = i / nrows, r = i - t * nrows;
-        float acc = 0.f;
-        if (p.shared) acc = dsum[((ng + t / NT) * p.dn_rows + r) * NT + (t % NT)];
-        const int* src = R.slot_src + t * p.k;
-        const float* wt = R.w + t * p.k;
-#pragma unroll 4
-        for (int j = 0; j < p.k; ++j) {
-            const int gs = src[j];   // group * NT + token in group
+    // y[t][h0 + r] = shared(t)[r] + sum over the token's k slots of w * d,
+    // where d (of the slot's group, row and token) is its block-column
+    // partials summed in column order.  Lane j of a group of JS lanes takes
+    // slot j; the slot terms are summed by a fixed tree over the group.
+    const int JS = p.k <= 16 ? 16 : 32;
+    const int n_out = p.T * nrows;
+    for (int base = 0; base < n_out; base += kGemvThreads / JS) {
+        const int it = base + tid / JS, j = tid % JS;
+        const bool live = it < n_out;
+        const int t = live ? it / nrows : 0, r = live ? it - t * nrows : 0;
+        float v = 0.f;
+        if (live && j < p.k) {
+            const int gs = R.slot_src[t * p.k + j];   // group * NT + token in group
             const int gg = gs / NT, tt = gs - (gs / NT) * NT;
-            acc = __builtin_fmaf(wt[j], dsum[(gg * p.dn_rows + r) * NT + tt], acc);
+            v = R.w[t * p.k + j] * sum_columns(part + ((gg * p.dn_rows + r) * NT + tt) * nbp_r, nb_r);
         }
-        p.y[(size_t)t * p.H + h0 + r] = acc;
+        v = row_sum_f32(v);
+        if (JS == 32) v += __shfl_xor(v, 16);
+        if (live && j == 0) {
+            float acc = v;
+            if (p.shared) {
+                const int sg = t / NT, st = t - sg * NT;
+                acc = sum_columns(part + sh_off + ((sg * p.dn_rows + r) * NT + st) * nbp_s, nb_s) + v;
+            }
+            p.y[(size_t)t * p.H + h0 + r] = acc;
+        }
     }
-
 }
 
 // The workgroup after the down tiles returns the call's shared state to zero
