@@ -55,6 +55,19 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 
 constexpr uint32_t kMagic = 0x43004300u;   // bf16 pair (128.0, 128.0)
 
+// Loads through global-address-space pointers: the expert blobs and the
+// activations come as generic pointers, and generic (flat) loads would make
+// every wait for one of them also wait for LDS traffic and for all other loads.
+__device__ __forceinline__ uint4 ldg_u4(const void* p) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = *(const __attribute__((address_space(1))) v4u*)p;
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint16_t ldg_u16(const void* p) {
+    return *(const __attribute__((address_space(1))) uint16_t*)p;
+}
+
+
 
 __device__ __forceinline__ uint32_t magic_vgpr() {
     uint32_t m;
@@ -155,7 +168,7 @@ __device__ __forceinline__ void load_slice_bf16(XSlice<QT, NTERM>& s, const uint
         const uint4* p = reinterpret_cast<const uint4*>(tm == 0 ? hi : lo);
 #pragma unroll
         for (int v = 0; v < NW / 4; ++v) {
-            uint4 u = p[v];
+            uint4 u = ldg_u4(p + v);
             nat[4 * v + 0] = u.x;
             nat[4 * v + 1] = u.y;
             nat[4 * v + 2] = u.z;
@@ -173,7 +186,8 @@ __device__ __forceinline__ void load_slice_f32(XSlice<QT, 2>& s, const float* sr
     uint32_t nhi[QK / 2], nlo[QK / 2];
 #pragma unroll
     for (int v = 0; v < QK / 4; ++v) {
-        float4 f = reinterpret_cast<const float4*>(src)[v];
+        const uint4 fu = ldg_u4(reinterpret_cast<const float4*>(src) + v);
+        float4 f = make_float4(__uint_as_float(fu.x), __uint_as_float(fu.y), __uint_as_float(fu.z), __uint_as_float(fu.w));
         float vals[4] = {f.x, f.y, f.z, f.w};
         uint32_t h[4], l[4];
 #pragma unroll
@@ -310,6 +324,16 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);   // exact, subnormals included
 }
 
+
+// A block scale converted where it is used: the empty asm keeps the
+// conversion (and so the wait for its load) from being moved up to the load,
+// where it would hold back the loads issued after it.
+__device__ __forceinline__ float scale_at_use(uint16_t bits) {
+    uint32_t b = bits;
+    asm volatile("" : "+v"(b));
+    return half_bits_to_f32((uint16_t)b);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Fused decode / verify layer: one kernel per layer.
 //
@@ -382,6 +406,11 @@ struct RouteLDS {
     int n_groups;
     int flag;
 };
+
+// Expert e's blob from the device table (a global load of one pointer).
+__device__ __forceinline__ const uint8_t* expert_blob(const DecodeParams& p, int e) {
+    return (const uint8_t*)((const __attribute__((address_space(1))) uint64_t*)p.table)[e];
+}
 
 // Routing of the T tokens (wave w takes tokens w, w + 4) and the buckets: pairs
 // (token, slot) sorted by (expert, token); runs of <= NT pairs of one expert
@@ -528,7 +557,7 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         grp = g;
         const int first = R.group_first[g];
         ntok = R.group_n[g];
-        blob = p.table ? (const uint8_t*)p.table[R.pair_exp[first]] : p.single;
+        blob = p.table ? expert_blob(p, R.pair_exp[first]) : p.single;
         rows = p.FF;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -574,10 +603,10 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         if (m < p.gu_passes) {
             const int f = min(f0 + m * P + rp, rows - 1);
             const size_t blk = (size_t)f * nblk + b;
-            cg[m] = *reinterpret_cast<const uint4*>(gcode + blk * 16);
-            cu[m] = *reinterpret_cast<const uint4*>(ucode + blk * 16);
-            sg_[m] = *reinterpret_cast<const uint16_t*>(gscale + blk * 2);
-            su_[m] = *reinterpret_cast<const uint16_t*>(uscale + blk * 2);
+            cg[m] = ldg_u4(gcode + blk * 16);
+            cu[m] = ldg_u4(ucode + blk * 16);
+            sg_[m] = ldg_u16(gscale + blk * 2);
+            su_[m] = ldg_u16(uscale + blk * 2);
         }
     }
     XSlice<QT, NTERM> xs[NT];
@@ -596,8 +625,8 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         const int f = f0 + m * P + rp;
         if (m < p.gu_passes && active && f < rows) {
             float og[NT], ou[NT];
-            block_dot<QT, NTERM, NT>(cg[m], half_bits_to_f32(sg_[m]), xs, ntok, og);
-            block_dot<QT, NTERM, NT>(cu[m], half_bits_to_f32(su_[m]), xs, ntok, ou);
+            block_dot<QT, NTERM, NT>(cg[m], scale_at_use(sg_[m]), xs, ntok, og);
+            block_dot<QT, NTERM, NT>(cu[m], scale_at_use(su_[m]), xs, ntok, ou);
             const int rr = m * P + rp;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -775,7 +804,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
             nb = nb_r;
             const int first = R.group_first[g];
             ntok = R.group_n[g];
-            dcode = (p.table ? (const uint8_t*)p.table[R.pair_exp[first]] : p.single) + gu_r;
+            dcode = (p.table ? expert_blob(p, R.pair_exp[first]) : p.single) + gu_r;
         } else {
             const int us = u - ng * nb_r;
             g = us / nb_s;            // shared group
@@ -792,8 +821,8 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
         for (int i = 0; i < kRowsPerThread; ++i) {
             const int r = min(rs + i * S, nrows - 1);
             const size_t blk = (size_t)(h0 + r) * nb + b;
-            c[i] = *reinterpret_cast<const uint4*>(dcode + blk * 16);
-            sc[i] = *reinterpret_cast<const uint16_t*>(dscale + blk * 2);
+            c[i] = ldg_u4(dcode + blk * 16);
+            sc[i] = ldg_u16(dscale + blk * 2);
         }
         if (!waited) {
             // Thread g of the first wave watches group g's ready flag (routed
@@ -876,7 +905,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
                 const int r = rs + i * S;
                 if (r < nrows) {
                     float o[NT];
-                    block_dot<QT, 2, NT>(c[i], half_bits_to_f32(sc[i]), xs, ntok, o);
+                    block_dot<QT, 2, NT>(c[i], scale_at_use(sc[i]), xs, ntok, o);
                     const int nbp = sh ? nbp_s : nbp_r;
                     float* dst = part + (sh ? sh_off : 0) + ((g * p.dn_rows + r) * NT) * nbp + b;
 #pragma unroll
