@@ -245,6 +245,46 @@ __device__ __forceinline__ void slice_from_packed(XSlice<QT, 2>& s, const uint32
     finish_slice<QT, 2>(s, z);
 }
 
+// An arranged activation slice in LDS: the dot pairs, then the per-q offsets
+// and z * sum x, padded to a multiple of 4 words.
+template <int QT, int NTERM>
+struct SliceWords {
+    static constexpr int N = (NTERM * QTraits<QT>::NPAIR + QTraits<QT>::NQ + 1 + 3) & ~3;
+};
+
+template <int QT, int NTERM>
+__device__ __forceinline__ void slice_to_lds(const XSlice<QT, NTERM>& s, uint32_t* d) {
+    constexpr int NP = QTraits<QT>::NPAIR, NQ = QTraits<QT>::NQ;
+#pragma unroll
+    for (int tm = 0; tm < NTERM; ++tm)
+#pragma unroll
+        for (int i = 0; i < NP; ++i) d[tm * NP + i] = s.pr[tm][i];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) d[NTERM * NP + q] = __float_as_uint(s.neg_c[q]);
+    d[NTERM * NP + NQ] = __float_as_uint(s.zx);
+}
+
+template <int QT, int NTERM>
+__device__ __forceinline__ void slice_from_lds(XSlice<QT, NTERM>& s, const uint32_t* d) {
+    constexpr int NP = QTraits<QT>::NPAIR, NQ = QTraits<QT>::NQ, SW = SliceWords<QT, NTERM>::N;
+    uint32_t w[SW];
+#pragma unroll
+    for (int v = 0; v < SW / 4; ++v) {
+        const uint4 u = reinterpret_cast<const uint4*>(d)[v];
+        w[4 * v + 0] = u.x;
+        w[4 * v + 1] = u.y;
+        w[4 * v + 2] = u.z;
+        w[4 * v + 3] = u.w;
+    }
+#pragma unroll
+    for (int tm = 0; tm < NTERM; ++tm)
+#pragma unroll
+        for (int i = 0; i < NP; ++i) s.pr[tm][i] = w[tm * NP + i];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) s.neg_c[q] = __uint_as_float(w[NTERM * NP + q]);
+    s.zx = __uint_as_float(w[NTERM * NP + NQ]);
+}
+
 // A SwiGLU output as the gate/up stage publishes it: two bf16 terms hi + lo
 // (relative error <= 2^-17) in one word, hi | lo << 16.  The word is never 0:
 // a value that rounds to +0 is stored as -0 (0x8000), a NaN as the canonical
@@ -382,6 +422,7 @@ struct DecodeParams {
     int dn_rows, tiles_dn;
     int n_ready;                 // ready-flag replicas in use: min(kReadyReplicas, tiles_dn)
     int stage_words;             // `a` words each down workgroup copies to LDS first (one token), else 0
+    int x_off;                   // one token: LDS word offset of the arranged activation slices (gate/up), else -1
 };
 
 // Word offsets inside the synchronisation area (ints; 16 ints = one 64-byte line).
@@ -610,12 +651,17 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         }
     }
     XSlice<QT, NTERM> xs[NT];
+    if (NT == 1 && p.x_off >= 0) {   // arranged while the routing ran
+        slice_from_lds<QT, NTERM>(xs[0], reinterpret_cast<const uint32_t*>(lds) + p.x_off +
+                                             b * SliceWords<QT, NTERM>::N);
+    } else {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        if constexpr (NTERM == 1)
-            load_slice_bf16<QT, 1>(xs[t], (const uint16_t*)p.x + (size_t)toks[t] * p.H + b * QK, nullptr, p.z);
-        else
-            load_slice_f32<QT>(xs[t], (const float*)p.x + (size_t)toks[t] * p.H + b * QK, p.z);
+        for (int t = 0; t < NT; ++t) {
+            if constexpr (NTERM == 1)
+                load_slice_bf16<QT, 1>(xs[t], (const uint16_t*)p.x + (size_t)toks[t] * p.H + b * QK, nullptr, p.z);
+            else
+                load_slice_f32<QT>(xs[t], (const float*)p.x + (size_t)toks[t] * p.H + b * QK, p.z);
+        }
     }
     // Partials part[((mat * Rr + rr) * NT + t) * nbp + b]: a row's block
     // columns are contiguous, padded to a multiple of 4.
@@ -1008,8 +1054,23 @@ __global__ void __launch_bounds__(kGemvThreads, NT == 1 ? 3 : 2) decode_layer_ke
     extern __shared__ __align__(16) float lds[];   // 16-byte aligned: float4 reads
     __shared__ RouteLDS R;
     const int tid = threadIdx.x;
-    route_and_bucket<NT>(p, R);
     const int wg = blockIdx.x;
+    if (NT == 1 && p.x_off >= 0 && wg < p.n_gu && tid >= 64) {
+        // One token: while the first wave routes, the others arrange the
+        // token's activation slice of every block column in LDS (the routing's
+        // closing barrier publishes them).
+        constexpr int QK = QTraits<QT>::QK;
+        const int nblk = p.H / QK;
+        for (int b = tid - 64; b < nblk; b += kGemvThreads - 64) {
+            XSlice<QT, NTERM> xsl;
+            if constexpr (NTERM == 1)
+                load_slice_bf16<QT, 1>(xsl, (const uint16_t*)p.x + b * QK, nullptr, p.z);
+            else
+                load_slice_f32<QT>(xsl, (const float*)p.x + b * QK, p.z);
+            slice_to_lds<QT, NTERM>(xsl, reinterpret_cast<uint32_t*>(lds) + p.x_off + b * SliceWords<QT, NTERM>::N);
+        }
+    }
+    route_and_bucket<NT>(p, R);
     if (wg == 0) {
         for (int q = tid; q < p.T * p.k; q += kGemvThreads) {
             if (p.ids_out) p.ids_out[q] = R.id[q];
@@ -1074,7 +1135,12 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     g.tile_rows_dn = rows;
     g.tiles_dn = (H + rows - 1) / rows;
     const size_t lds_dn = per_row * rows + stage;
-    const size_t lds_gu = (size_t)2 * g.tile_rows_gu * ((nblk_gu + 3) & ~3) * NT * 4;
+    // One token: the arranged activation slices follow the gate/up partials
+    // (sized for fp32 activations, the larger slice).
+    const size_t part_gu = (size_t)2 * g.tile_rows_gu * ((nblk_gu + 3) & ~3) * NT * 4;
+    g.x_off = T == 1 ? (int)(part_gu / 4) : -1;
+    const int sw = ((qk == 64 ? 64 : 32) + (qk == 64 ? 3 : 1) + 1 + 3) & ~3;
+    const size_t lds_gu = part_gu + (T == 1 ? (size_t)nblk_gu * sw * 4 : 0);
     g.lds_bytes = lds_dn > lds_gu ? lds_dn : lds_gu;
     g.grid = g.n_gu + g.tiles_dn + 1;   // + the workgroup that resets the shared state
     return g;
@@ -1133,6 +1199,7 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
     p.tiles_dn = g.tiles_dn;
     p.n_ready = g.tiles_dn < kReadyReplicas ? g.tiles_dn : kReadyReplicas;
     p.stage_words = g.stage_words;
+    p.x_off = g.x_off;
     stage_mark(marks, s);
     hipError_t e;
     if (T == 1)

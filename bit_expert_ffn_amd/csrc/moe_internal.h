@@ -70,6 +70,7 @@ struct GemvShape {
     int max_groups, shared_groups, n_gu;
     int tile_rows_dn, tiles_dn;
     int stage_words;          // `a` words each down workgroup stages in LDS (one token), else 0
+    int x_off;                // one token: LDS word offset of the gate/up activation slices, else -1
     size_t lds_bytes;
     int grid;
 };
