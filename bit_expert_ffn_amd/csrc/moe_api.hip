@@ -31,20 +31,23 @@ struct Bump {
     }
 };
 
-SmallLayout small_layout(int T, int k, int FF, int FFs) {
+SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype) {
     SmallLayout L{};
     Bump b;
     const size_t n = (size_t)T * k;
-    L.sync = b.take(decode_sync_bytes(kSmallT * k + kSmallT));
+    const size_t s1 = decode_sync_bytes(kSmallT * k + kSmallT);
+    const size_t sw = window_sync_bytes(k, window_shape(H, FF, FFs, qtype, MOE_F32, kSmallT, k).n_chunks);
+    L.sync = b.take(s1 > sw ? s1 : sw);
     L.a = b.take((size_t)kSmallT * k * FF * 4);
     L.as = b.take((size_t)kSmallT * FFs * 4);
+    L.d = b.take((size_t)(kSmallT * k + kSmallT) * H * 4);
     L.ids = b.take(n * 4);
     L.w = b.take(n * 4);
     L.total = b.off;
     return L;
 }
 
-size_t small_fixed_bytes(int k, int FF, int FFs) { return small_layout(0, k, FF, FFs).ids; }
+size_t small_fixed_bytes(int k, int H, int FF, int FFs, int qtype) { return small_layout(0, k, H, FF, FFs, qtype).ids; }
 
 }  // namespace moe
 
@@ -111,14 +114,14 @@ size_t moe_expert_blob_bytes(const moe_expert_desc* d) {
 size_t moe_layer_workspace_bytes(const moe_layer_desc* d, int32_t T) {
     if (check_layer(d) != MOE_OK || T < 0) return 0;
     if (T <= kSmallT)
-        return small_layout(T, d->top_k, d->expert.ff, d->shared_ff).total;
+        return small_layout(T, d->top_k, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype).total;
     return large_layout(T, d->top_k, d->n_experts, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype)
         .total;
 }
 
 size_t moe_expert_workspace_bytes(const moe_expert_desc* d, int32_t T) {
     if (check_expert(d, "expert") != MOE_OK || T < 0) return 0;
-    if (T <= kSmallT) return small_layout(T, 1, d->ff, 0).total;
+    if (T <= kSmallT) return small_layout(T, 1, d->hidden, d->ff, 0, d->qtype).total;
     return large_layout(T, 1, 1, d->hidden, d->ff, 0, d->qtype).total;
 }
 
@@ -144,14 +147,24 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
                             size_t ws_bytes, hipStream_t s, bool identity, StageMarks* marks = nullptr) {
     char* wsb = (char*)ws;
     if (T <= kSmallT) {
-        const SmallLayout L = small_layout(T, k, ed.ff, FFs);
+        const SmallLayout L = small_layout(T, k, ed.hidden, ed.ff, FFs, ed.qtype);
         if (ws_bytes < L.total)
             return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
-        const GemvShape g = gemv_shape(ed.hidden, ed.ff, FFs, ed.qtype, ed.zero_point, T, k);
-        if (g.lds_bytes > 128 * 1024)
-            return fail(MOE_ERR_UNSUPPORTED, "decode tile needs %zu bytes of LDS", g.lds_bytes);
-        hipError_t e = launch_decode_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm,
-                                           identity ? 1 : 0, ids_out, w_out, L, wsb, y, s, marks);
+        hipError_t e;
+        if (T == 1) {
+            const GemvShape g = gemv_shape(ed.hidden, ed.ff, FFs, ed.qtype, ed.zero_point, T, k);
+            if (g.lds_bytes > 128 * 1024)
+                return fail(MOE_ERR_UNSUPPORTED, "decode tile needs %zu bytes of LDS", g.lds_bytes);
+            e = launch_decode_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm, identity ? 1 : 0,
+                                    ids_out, w_out, L, wsb, y, s, marks);
+        } else {
+            const WindowShape g = window_shape(ed.hidden, ed.ff, FFs, ed.qtype, x_dtype, T, k);
+            if (g.lds_bytes > 150 * 1024)
+                return fail(MOE_ERR_UNSUPPORTED, "verify window needs %zu bytes of LDS", g.lds_bytes);
+            e = launch_window_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm, identity ? 1 : 0,
+                                    ed.qtype, ed.zero_point, ed.hidden, ed.ff, FFs, ids_out, w_out, L, wsb, y, s,
+                                    marks);
+        }
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
         return MOE_OK;
     }

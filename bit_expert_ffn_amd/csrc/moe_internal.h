@@ -21,13 +21,12 @@ constexpr int kBlockBytes = 18;
 
 inline int codes_per_block(int qtype) { return qtype == 1 ? 64 : (qtype == 2 ? 32 : 0); }
 
-// Synchronisation area of the fused decode kernel, at offset 0 of the
-// workspace: 64-byte lines holding groups_done, error, the top exit counter,
-// one counter per group and the first-level exit counters.  It must be zero
-// before the first call on a workspace; every call leaves it zero again.
-// Synchronisation area of the fused decode kernel: 4 + groups + 16 lines of 64
-// bytes (flags, per-group counters, exit counters), then kReadyReplicas
-// replicas of the per-group ready flags, kReadyStride bytes apart.
+// Synchronisation area of the one-token decode kernel: 4 + groups + 16 lines
+// of 64 bytes (flags, per-group counters, load counters), then kReadyReplicas
+// replicas of the per-group ready flags, kReadyStride bytes apart.  The
+// verify-window kernel lays out its own lines over the same area
+// (window_sync_bytes).  The area must be zero before the first call on a
+// workspace; every call leaves it zero again.
 constexpr int kReadyReplicas = 16;
 constexpr int kReadyStride = 4096;
 __host__ __device__ inline size_t decode_sync_lines_bytes(int max_groups_total) { return (size_t)64 * (4 + max_groups_total + 16); }
@@ -38,14 +37,15 @@ __host__ __device__ inline size_t decode_sync_bytes(int max_groups_total) {
 
 // Workspace layout for the GEMV path (T <= kSmallT), byte offsets.
 struct SmallLayout {
-    // The first three regions sit at the same offsets for every T <= kSmallT
+    // The first four regions sit at the same offsets for every T <= kSmallT
     // (sized for kSmallT tokens), and the matrix-core layout starts after
     // them, so that calls of any size can share one workspace: the sync
-    // words, and `a`, whose words are never 0 once written and are returned
-    // to 0 by each call that wrote them.
+    // words, `a` and d, whose words are never 0 once written and are
+    // returned to 0 by each call that wrote them.
     size_t sync;
     size_t a;                // [T*k][FF] SwiGLU output per (expert, token) pair, packed bf16 hi | lo << 16
     size_t as;               // [T][FFs] the shared expert's
+    size_t d;                // [8k + 8][H] verify windows: down output per slot, then per token of the shared expert
     size_t ids, w;           // [T][k] routing when the caller passes no output
     size_t total;
 };
@@ -75,8 +75,24 @@ struct GemvShape {
     int grid;
 };
 
-SmallLayout small_layout(int T, int k, int FF, int FFs);
-size_t small_fixed_bytes(int k, int FF, int FFs);   // sync + a + as: where every layout's own regions start
+// Verify windows (2 <= T <= kSmallT): work items and workgroups of the
+// window kernel.
+constexpr int kWinGuWorkgroups = 256;
+constexpr int kWinDnWorkgroups = 256;
+struct WindowShape {
+    int gu_passes, tiles_gu, tiles_gu_s;     // gate/up: passes per tile; tiles per routed / shared expert
+    int dn_passes, chunk_rows, n_chunks;     // down: passes per routed item; H rows per chunk; chunks
+    int sh_passes, sh_rows, sh_items;        // down of the shared expert: passes, rows and items per chunk
+    int n_gu_wg, n_dn_wg;
+    int x_off, stage_words;
+    size_t lds_bytes;
+    int grid;
+};
+WindowShape window_shape(int H, int FF, int FFs, int qtype, int x_dtype, int T, int k);
+size_t window_sync_bytes(int k, int n_chunks);
+
+SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype);
+size_t small_fixed_bytes(int k, int H, int FF, int FFs, int qtype);   // sync + a + as + d: where every layout's own regions start
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype);
 GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k);
 
@@ -103,6 +119,11 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
                                const void* x, int x_dtype, const float* logits, int T, int E, int k, int renorm,
                                int identity, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
                                hipStream_t s, StageMarks* marks = nullptr);
+hipError_t launch_window_layer(const WindowShape& g, const void* const* table, const void* single,
+                               const void* shared, const void* x, int x_dtype, const float* logits, int T, int E,
+                               int k, int renorm, int identity, int qtype, float z, int H, int FF, int FFs,
+                               int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y, hipStream_t s,
+                               StageMarks* marks = nullptr);
 hipError_t launch_prefill_layer(const void* const* table, const void* single, const void* shared, int qtype, float z,
                                 int H, int FF, int FFs, const void* x, int x_dtype, const float* logits, int T, int E,
                                 int k, int renorm, int identity, int* ids_out, float* w_out, const LargeLayout& L,

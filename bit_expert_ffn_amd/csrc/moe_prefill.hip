@@ -60,7 +60,7 @@ constexpr int kDnCols = 512;               // outputs per down workgroup (64 per
 
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype) {
     LargeLayout L{};
-    size_t off = small_fixed_bytes(k, FF, FFs);   // the decode path's sync words and `a` stay untouched
+    size_t off = small_fixed_bytes(k, H, FF, FFs, qtype);   // the decode path's sync words and `a` stay untouched
     auto take = [&](size_t b) {
         size_t o = off;
         off = (off + b + 255) & ~(size_t)255;

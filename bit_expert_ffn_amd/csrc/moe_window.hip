@@ -1,0 +1,865 @@
+// Verify-window layer (2 <= T <= 8 tokens): one fused kernel per layer.
+//
+// A speculative verify window scores a few draft tokens at once, and under a
+// skewed expert popularity those tokens share experts (Strata, "The plan:
+// three destinations per expert": an expert chosen by several tokens of the
+// window is read once).  Here the tokens that chose an expert form groups of
+// up to two, and each group's weights are read once for its tokens.  (A
+// group of every token of the expert would make the work items of hot
+// experts several times heavier than the rest; the re-read of an expert by
+// its second group is mostly served by the caches.)
+//
+// Work items, in the order every workgroup derives them from the routing:
+//   gate/up items  (group, tile of FF rows): the codes of every pass of the
+//                  tile are loaded once and held in registers while the
+//                  group's tokens go through them one at a time; the SwiGLU
+//                  output rows are published as never-zero packed words;
+//   down items     (group, chunk of H rows): the group's `a` rows are
+//                  arranged into dot-pair slices in LDS once, the down codes of the chunk are held in
+//                  registers, and the tokens go through them one at a time; the
+//                  result of each (slot, row) is published as a never-zero
+//                  fp32 word.
+// The shared expert's groups hold the window's tokens two at a time; its down
+// items cover a chunk in several sub-ranges of rows.
+//
+// Workgroups [0, n_gu_wg) take the gate/up items (item i by workgroup
+// i % n_gu_wg), the others the down items, so a down workgroup only ever waits
+// for gate/up work of workgroups dispatched before it.  Each gate/up tile
+// bumps its group's counter; the tile that completes the group raises the
+// group's ready flag, and the down items of that group start from it (no wait
+// for other groups).  Each down item then bumps its chunk's counter; the item
+// that completes a chunk combines it: y[t][h] = shared + sum_j w[t][j] d, the
+// slots summed in rank order, so the output does not depend on timing.
+//
+// Every piece of shared state is returned to zero by its last user: the last
+// down item of a group clears the group's counters, flag and `a` rows; the
+// combining item clears its chunk's counter and the d words it read.  The
+// bounded waits flag an error if a bound is ever reached.
+#include "moe_gemv_common.h"
+
+namespace moe {
+
+constexpr int kWinPairs = kSmallT * kMaxK;   // (token, slot) pairs of a window
+constexpr long kWinSpin = 1l << 22;
+constexpr int kWinMaxPass = 8;               // passes per item (rows = P * passes)
+// Tokens of one expert per group: a hot expert's tokens are split over
+// several groups, so that no work item holds many more tokens than others
+// (its weights are read once per group; the re-reads of one call are mostly
+// served by the caches).
+constexpr int kWinGroup = 2;
+constexpr int kWinShared = (kSmallT + kWinGroup - 1) / kWinGroup;   // groups of the shared expert, at most
+
+struct WindowParams {
+    const void* const* table;
+    const uint8_t* single;      // one expert's blob when table == nullptr (moe_expert_ffn)
+    const uint8_t* shared;
+    const void* x;              // [T][H] bf16 or fp32
+    const float* logits;        // [T][E]
+    int T, E, k, renorm, identity;
+    int H, FF, FFs;
+    float z;
+    int* ids_out;               // [T][k] or null
+    float* w_out;               // [T][k] or null
+    uint32_t* a;                // [T*k][FF] by sorted pair (expert, token), packed bf16 hi | lo << 16
+    uint32_t* as;               // [T][FFs] the shared expert's
+    uint32_t* d;                // [8k + 8][H] fp32 bits: slot t*k + j, then 8k + t for the shared expert
+    float* y;                   // [T][H]
+    int* sync;                  // window sync lines, see win_* below
+    int gu_passes, tiles_gu, tiles_gu_s;
+    int dn_passes, chunk_rows, n_chunks;
+    int sh_passes, sh_rows, sh_items;
+    int n_gu_wg, n_dn_wg;
+    int x_off;                  // gate/up: LDS word offset of the activation slices
+    int stage_words;            // down: LDS words reserved for the staged `a` rows
+};
+
+// Sync lines (16 ints each): line 1 the error flag; per group g (routed
+// groups g < 8k, the shared expert's groups from 8k on) its gate/up tile
+// count, its ready flag and its down item count; then one counter per chunk.
+__device__ __forceinline__ int* win_error(int* s) { return s + 16; }
+__device__ __forceinline__ int* win_gu_count(int* s, int g) { return s + 16 * (2 + 3 * g); }
+__device__ __forceinline__ int* win_ready(int* s, int g) { return s + 16 * (3 + 3 * g); }
+__device__ __forceinline__ int* win_dn_count(int* s, int g) { return s + 16 * (4 + 3 * g); }
+__device__ __forceinline__ int* win_chunk(int* s, int k, int c) { return s + 16 * (2 + 3 * (kSmallT * k + kWinShared) + c); }
+
+__device__ __forceinline__ void win_flag_error(const WindowParams& p) {
+    __hip_atomic_store(win_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct WinLDS {
+    int id[kWinPairs];
+    float w[kWinPairs];
+    alignas(16) int key[kWinPairs + 4];   // expert << 8 | slot, padded with INT_MAX
+    int sorted[kWinPairs];          // sorted position -> slot
+    int group_first[kWinPairs + 1]; // first sorted position of each group; [n_groups] = T * k
+    int n_groups;
+    int flag_combine, flag_reset;
+};
+
+// Routing of the T tokens (wave w takes tokens w and w + 4), then the groups:
+// pairs sorted by (expert, token), each run of one expert cut into groups of
+// at most kWinGroup pairs.
+// `scratch` is the dynamic LDS, free until the roles start (128 keys per wave).
+__device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, uint64_t* scratch) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int k = p.k, n = p.T * k;
+    for (int t = wv; t < p.T; t += kGemvThreads / 64) {
+        int id = 0;
+        float wt = 1.f;
+        if (!p.identity) wave_topk(p.logits + (size_t)t * p.E, p.E, k, p.renorm, lane, scratch + 128 * wv, &id, &wt);
+        if (lane < k) {
+            R.id[t * k + lane] = id;
+            R.w[t * k + lane] = wt;
+            R.key[t * k + lane] = id << 8 | (t * k + lane);
+        }
+    }
+    if (tid < 4) R.key[n + tid] = 0x7FFFFFFF;
+    __syncthreads();
+    // Keys are distinct (a token selects an expert at most once), so each
+    // pair's count of smaller keys is its sorted position.
+    if (tid < n) {
+        const int mine = R.key[tid];
+        int rank = 0;
+        for (int j = 0; j < n; j += 4) {
+            const int4 q = *reinterpret_cast<const int4*>(&R.key[j]);
+            rank += (q.x < mine) + (q.y < mine) + (q.z < mine) + (q.w < mine);
+        }
+        R.sorted[rank] = tid;
+    }
+    __syncthreads();
+    if (wv == 0) {
+        // A group starts at every kWinGroup-th pair of a run of one expert.
+        int base = 0, carry = 0;   // carry: the run start in effect at the end of the previous 64 pairs
+        for (int r0 = 0; r0 < n; r0 += 64) {
+            const int r = r0 + lane;
+            const bool run_start = r < n && (r == 0 || R.id[R.sorted[r - 1]] != R.id[R.sorted[r]]);
+            const uint64_t m = __ballot(run_start);
+            const uint64_t upto = m & (lane == 63 ? ~0ull : ((2ull << lane) - 1));
+            const int rs = upto ? r0 + 63 - __clzll(upto) : carry;
+            const bool start = r < n && (r - rs) % kWinGroup == 0;
+            const uint64_t gm = __ballot(start);
+            if (start) R.group_first[base + lanes_below(gm)] = r;
+            base += __popcll(gm);
+            carry = __builtin_amdgcn_readlane(rs, 63);
+        }
+        if (lane == 0) {
+            R.n_groups = base;
+            R.group_first[base] = n;
+        }
+    }
+    __syncthreads();
+}
+
+// One gate/up item: group (or the shared expert) and tile.
+struct GuItem {
+    const uint8_t* blob;
+    uint32_t* out;
+    int g, first, n_e, rows, f0;
+    bool sh;
+};
+
+__device__ __forceinline__ GuItem gu_item(const WindowParams& p, const WinLDS& R, int item, int n_routed, int Rr) {
+    GuItem it;
+    it.sh = item >= n_routed;
+    int tile;
+    if (!it.sh) {
+        it.g = item / p.tiles_gu;
+        tile = item - it.g * p.tiles_gu;
+        it.first = R.group_first[it.g];
+        it.n_e = R.group_first[it.g + 1] - it.first;
+        it.blob = p.table ? table_blob(p.table, R.id[R.sorted[it.first]]) : p.single;
+        it.rows = p.FF;
+        it.out = p.a;
+    } else {   // shared group sg: tokens kWinGroup * sg ..
+        const int i2 = item - n_routed, sg = i2 / p.tiles_gu_s;
+        it.g = kSmallT * p.k + sg;
+        tile = i2 - sg * p.tiles_gu_s;
+        it.first = kWinGroup * sg;
+        it.n_e = min(kWinGroup, p.T - it.first);
+        it.blob = p.shared;
+        it.rows = p.FFs;
+        it.out = p.as;
+    }
+    it.f0 = tile * Rr;
+    return it;
+}
+
+// Every pass's codes and scales of the item's tile at once, from clamped rows
+// (the last tile's overhang re-reads its last row): all loads in flight
+// together, and no branch per pass.
+struct GuCodes {
+    uint4 cg[kWinMaxPass], cu[kWinMaxPass];
+    uint16_t sg[kWinMaxPass], su[kWinMaxPass];
+};
+
+__device__ __forceinline__ void gu_load(const GuItem& it, int nblk, int P, int rp, int b, GuCodes& c) {
+    const size_t plane = (size_t)it.rows * nblk;
+    const uint8_t* gcode = it.blob;
+    const uint8_t* gscale = it.blob + plane * 16;
+    const uint8_t* ucode = it.blob + plane * 18;
+    const uint8_t* uscale = ucode + plane * 16;
+#pragma unroll
+    for (int m = 0; m < kWinMaxPass; ++m) {
+        const int f = min(it.f0 + m * P + rp, it.rows - 1);
+        const size_t blk = (size_t)f * nblk + b;
+        c.cg[m] = ldg_u4(gcode + blk * 16);
+        c.cu[m] = ldg_u4(ucode + blk * 16);
+        c.sg[m] = ldg_u16(gscale + blk * 2);
+        c.su[m] = ldg_u16(uscale + blk * 2);
+    }
+}
+
+// The item's tokens through the held codes, one at a time (its slice in
+// registers), two per round of partial sums; then SwiGLU, the published `a`
+// rows, and the tile counted.
+template <int QT, int NTERM>
+__device__ __forceinline__ void gu_compute(const WindowParams& p, const WinLDS& R, const GuItem& it, GuCodes& c,
+                                           float* lds, int nblk, int P, int rp, int b, bool active) {
+    constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
+    const int tid = threadIdx.x;
+    const int Rr = P * kWinMaxPass;
+    // With an even count of block columns, lanes 2j and 2j + 1 (columns b and
+    // b + 1 of one row) add their partials first: ncol columns per (row,
+    // token), padded to ncp.
+    const bool pairs = (nblk & 1) == 0;
+    const int ncol = pairs ? nblk / 2 : nblk;
+    const int ncp = (ncol + 3) & ~3;
+    const uint32_t* xsl = reinterpret_cast<const uint32_t*>(lds) + p.x_off;
+    for (int t0 = 0; t0 < it.n_e; t0 += 2) {
+        const int nt = min(2, it.n_e - t0);
+#pragma unroll 1
+        for (int i = 0; i < nt; ++i) {
+            // Opaque to the compiler per token: the codes' shifted copies are
+            // then formed at their use, not hoisted out of this loop.
+#pragma unroll
+            for (int m = 0; m < kWinMaxPass; ++m) {
+                pin_u4(c.cg[m]);
+                pin_u4(c.cu[m]);
+            }
+            const int tok = it.sh ? it.first + t0 + i : R.sorted[it.first + t0 + i] / p.k;
+            XSlice<QT, NTERM> xs[1];
+            if (p.x_off >= 0) {
+                slice_from_lds<QT, NTERM>(xs[0], xsl + (tok * nblk + b) * SW);
+            } else {   // slices too large for LDS: straight from the activations
+                if constexpr (NTERM == 1)
+                    load_slice_bf16<QT, 1>(xs[0], (const uint16_t*)p.x + (size_t)tok * p.H + b * QK, nullptr, p.z);
+                else
+                    load_slice_f32<QT>(xs[0], (const float*)p.x + (size_t)tok * p.H + b * QK, p.z);
+            }
+            // The partials' addresses are formed here, not hoisted out of the
+            // token loop (where holding them would spill registers).
+            int pb = (rp * 2 + i) * ncp + (pairs ? (b >> 1) : b);
+            asm volatile("" : "+v"(pb));
+#pragma unroll
+            for (int m = 0; m < kWinMaxPass; ++m) {
+                const int f = it.f0 + m * P + rp;
+                if (active && f < it.rows) {
+                    float og[1], ou[1];
+                    block_dot<QT, NTERM, 1>(c.cg[m], scale_at_use(c.sg[m]), xs, 1, og);
+                    block_dot<QT, NTERM, 1>(c.cu[m], scale_at_use(c.su[m]), xs, 1, ou);
+                    if (pairs) {
+                        og[0] += dpp_xor1_f32(og[0]);
+                        ou[0] += dpp_xor1_f32(ou[0]);
+                    }
+                    if (!pairs || (b & 1) == 0) {
+                        // part[((mat * Rr + rr) * 2 + i) * ncp + col] with rr = m * P + rp
+                        float* q = lds + pb + m * P * 2 * ncp;
+                        q[0] = og[0];
+                        q[Rr * 2 * ncp] = ou[0];
+                    }
+                }
+            }
+        }
+        lds_barrier();
+        for (int i = tid; i < Rr * 2; i += kGemvThreads) {
+            const int rr = i >> 1, t = i & 1;
+            const int f = it.f0 + rr;
+            if (f >= it.rows || t >= nt) continue;
+            const float gv = sum_columns4(lds + ((0 * Rr + rr) * 2 + t) * ncp, ncol);
+            const float uv = sum_columns4(lds + ((1 * Rr + rr) * 2 + t) * ncp, ncol);
+            const float av = gv / (1.f + expf(-gv)) * uv;
+            const int orow = it.first + t0 + t;   // routed: sorted pair; shared: token
+            __hip_atomic_store(it.out + (size_t)orow * it.rows + f, pack_a(av), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        lds_barrier();   // the partials are reused by the next pair
+    }
+    // Every `a` store of the tile has completed before it is counted (this
+    // also waits for the next item's codes, loaded while this one ran).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(win_gu_count(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == (it.sh ? p.tiles_gu_s : p.tiles_gu) - 1)
+            __hip_atomic_store(win_ready(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Items blockIdx.x, + n_gu_wg, ...: the next item's codes are loaded before
+// the current one is computed (two buffers in turn), so that its loads
+// overlap the compute.  With no next item, the current one's are read again.
+template <int QT, int NTERM>
+__device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLDS& R, float* lds) {
+    constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
+    const int tid = threadIdx.x;
+    const int n_routed = R.n_groups * p.tiles_gu;
+    const int n_items = n_routed + (p.FFs ? (p.T + kWinGroup - 1) / kWinGroup * p.tiles_gu_s : 0);
+    const int nblk = p.H / QK;
+    const int P = kGemvThreads / nblk;
+    const bool active = tid < P * nblk;
+    const int rp = active ? tid / nblk : 0, b = active ? tid - (tid / nblk) * nblk : 0;
+    const int Rr = P * kWinMaxPass;
+    int item = blockIdx.x;
+    if (item >= n_items) return;
+    GuItem ia = gu_item(p, R, item, n_routed, Rr), ib;
+    GuCodes ca, cb;
+    gu_load(ia, nblk, P, rp, b, ca);
+    if (p.x_off >= 0) {
+        // Every token's activation slice of every block column, once per
+        // workgroup, while the first item's weights are on their way.
+        uint32_t* xsl = reinterpret_cast<uint32_t*>(lds) + p.x_off;
+        for (int s = tid; s < p.T * nblk; s += kGemvThreads) {
+            const int t = s / nblk, bb = s - t * nblk;
+            XSlice<QT, NTERM> x1;
+            if constexpr (NTERM == 1)
+                load_slice_bf16<QT, 1>(x1, (const uint16_t*)p.x + (size_t)t * p.H + bb * QK, nullptr, p.z);
+            else
+                load_slice_f32<QT>(x1, (const float*)p.x + (size_t)t * p.H + bb * QK, p.z);
+            slice_to_lds<QT, NTERM>(x1, xsl + s * SW);
+        }
+    }
+    __syncthreads();
+    while (true) {
+        int next = item + p.n_gu_wg;
+        ib = gu_item(p, R, next < n_items ? next : item, n_routed, Rr);
+        gu_load(ib, nblk, P, rp, b, cb);
+        gu_compute<QT, NTERM>(p, R, ia, ca, lds, nblk, P, rp, b, active);
+        if (next >= n_items) break;
+        item = next;
+        next = item + p.n_gu_wg;
+        ia = gu_item(p, R, next < n_items ? next : item, n_routed, Rr);
+        gu_load(ia, nblk, P, rp, b, ca);
+        gu_compute<QT, NTERM>(p, R, ib, cb, lds, nblk, P, rp, b, active);
+        if (next >= n_items) break;
+        item = next;
+    }
+}
+
+// A published fp32 word, read agent-coherently; 0 means not visible yet.
+__device__ __forceinline__ float load_published(const WindowParams& p, const uint32_t* w) {
+    uint32_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    long spins = 0;
+    while (v == 0u) {
+        if (++spins > kWinSpin) {
+            win_flag_error(p);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return __uint_as_float(v);
+}
+
+// Four published fp32 words, read agent-coherently.
+typedef uint32_t win_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ win_u32x4 load_coherent4(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, kCpolSc1);
+}
+
+__device__ __forceinline__ uint32_t min4(win_u32x4 v) { return min(min(v[0], v[1]), min(v[2], v[3])); }
+
+// Read again, until no word is 0, four words that showed a 0 (written, but
+// not yet visible here).
+__device__ __forceinline__ win_u32x4 reload_published4(const WindowParams& p, __amdgpu_buffer_rsrc_t rsrc,
+                                                    uint32_t off) {
+    win_u32x4 v = load_coherent4(rsrc, off);
+    long spins = 0;
+    while (min4(v) == 0u) {
+        if (++spins > kWinSpin) {
+            win_flag_error(p);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v = load_coherent4(rsrc, off);
+    }
+    return v;
+}
+
+__device__ __forceinline__ float4 as_float4(win_u32x4 v) {
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+
+// Pairwise sum of v[0..N) in natural order: ((v0 + v1) + (v2 + v3)) + ...,
+// the association that row_sum_f32 leaves in lane 0 for N = 16 (each of its
+// DPP steps adds lanes i and i ^ 1, i ^ 2, then the mirrored halves, and
+// every single addition is commutative).
+template <int N>
+__device__ __forceinline__ float pairwise_sum(const float* v) {
+    if constexpr (N == 1) return v[0];
+    else return pairwise_sum<N / 2>(v) + pairwise_sum<N / 2>(v + N / 2);
+}
+
+// Sum over slots [j0, j0 + 16) of w[t][j] * d[t * k + j] for 4 consecutive
+// rows h.. (0 past k), pairwise in slot order; all 16 loads in flight
+// together, then one check (a word still 0 is read again).
+__device__ __forceinline__ void slot_sums16(const WindowParams& p, const WinLDS& R, __amdgpu_buffer_rsrc_t rsrc, int t,
+                                            int h, int j0, float (&out)[4]) {
+    const int k = p.k;
+    win_u32x4 raw[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int jj = j0 + j < k ? j0 + j : 0;   // past k: slot 0 again, unused
+        raw[j] = load_coherent4(rsrc, 4u * (uint32_t)((t * k + jj) * p.H + h));
+    }
+    uint32_t m = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = min(m, min4(raw[j]));
+    if (m == 0u) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (j0 + j < k && min4(raw[j]) == 0u)
+                raw[j] = reload_published4(p, rsrc, 4u * (uint32_t)((t * k + j0 + j) * p.H + h));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = j0 + j < k ? R.w[t * k + j0 + j] * __uint_as_float(raw[j][e]) : 0.f;
+        out[e] = pairwise_sum<16>(v);
+    }
+}
+
+// y rows [c0, c1) of every token: shared + sum_j w[t][j] d[t * k + j], the
+// slot terms added as the one-token kernel adds them (lane j of a group of 16
+// or 32 lanes holds slot j's term, 0 past k, and a DPP tree sums the group:
+// pairwise in slot order), so a token's output is the same alone and inside a
+// window; the shared term is added last.  Each thread takes 4 consecutive
+// rows of one token.  The d words read are cleared for the next call.
+__device__ __forceinline__ void combine_chunk(const WindowParams& p, const WinLDS& R, int c0, int c1) {
+    const int nr4 = (c1 - c0) / 4, k = p.k;
+    const int nq = p.T * nr4;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.d, 0, (kSmallT * k + kSmallT) * p.H * 4, kRsrcWord3);
+    for (int qd = threadIdx.x; qd < nq; qd += kGemvThreads) {
+        const int t = qd / nr4, h = c0 + 4 * (qd - t * nr4);
+        float acc[4];
+        slot_sums16(p, R, rsrc, t, h, 0, acc);
+        if (k > 16) {
+            float hi[4];
+            slot_sums16(p, R, rsrc, t, h, 16, hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = acc[e] + hi[e];
+        }
+        if (p.FFs) {
+            const uint32_t off = 4u * (uint32_t)((kSmallT * k + t) * p.H + h);
+            win_u32x4 sv = load_coherent4(rsrc, off);
+            if (min4(sv) == 0u) sv = reload_published4(p, rsrc, off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(sv[e]) + acc[e];
+        }
+        *reinterpret_cast<float4*>(p.y + (size_t)t * p.H + h) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < k; ++j) *reinterpret_cast<uint4*>(p.d + (size_t)(t * k + j) * p.H + h) = zero;
+        if (p.FFs) *reinterpret_cast<uint4*>(p.d + (size_t)(kSmallT * k + t) * p.H + h) = zero;
+    }
+}
+
+// One down item: group (or the shared expert) and chunk (or sub-range).
+struct DnItem {
+    const uint8_t* dcode;
+    const uint8_t* dscale;
+    const uint32_t* a_src;
+    int g, ch, h0, nrows, first, n_e, K, group_items;
+    bool sh;
+};
+
+template <int QK>
+__device__ __forceinline__ DnItem dn_item(const WindowParams& p, const WinLDS& R, int item, int n_routed) {
+    DnItem it;
+    it.sh = item >= n_routed;
+    const uint8_t* blob;
+    if (!it.sh) {
+        it.g = item / p.n_chunks;
+        it.ch = item - it.g * p.n_chunks;
+        it.h0 = it.ch * p.chunk_rows;
+        it.nrows = min(p.chunk_rows, p.H - it.h0);
+        it.first = R.group_first[it.g];
+        it.n_e = R.group_first[it.g + 1] - it.first;
+        blob = p.table ? table_blob(p.table, R.id[R.sorted[it.first]]) : p.single;
+        it.K = p.FF;
+        it.a_src = p.a + (size_t)it.first * p.FF;
+        it.group_items = p.n_chunks;
+    } else {
+        const int per_sg = p.n_chunks * p.sh_items;
+        const int sg = (item - n_routed) / per_sg;
+        const int i2 = item - n_routed - sg * per_sg;
+        it.ch = i2 / p.sh_items;
+        const int sub = i2 - it.ch * p.sh_items;
+        const int c0 = it.ch * p.chunk_rows, c1 = min(c0 + p.chunk_rows, p.H);
+        it.h0 = c0 + sub * p.sh_rows;
+        it.nrows = min(p.sh_rows, c1 - it.h0);   // <= 0: an empty sub-range, still counted
+        it.g = kSmallT * p.k + sg;
+        it.first = kWinGroup * sg;
+        it.n_e = min(kWinGroup, p.T - it.first);
+        blob = p.shared;
+        it.K = p.FFs;
+        it.a_src = p.as + (size_t)it.first * p.FFs;
+        it.group_items = per_sg;
+    }
+    const int nb = it.K / QK;
+    it.dcode = blob + (size_t)2 * it.K * (p.H / QK) * kBlockBytes;   // after gate and up
+    it.dscale = it.dcode + (size_t)p.H * nb * 16;
+    return it;
+}
+
+struct DnCodes {
+    uint4 c[kWinMaxPass];
+    uint16_t sc[kWinMaxPass];
+};
+
+// Thread (rp, b) of an item: row rp of each pass of P = 256 / nb rows, block
+// column b.
+struct DnLane {
+    int nb, P, rp, b;
+    bool active;
+};
+
+__device__ __forceinline__ DnLane dn_lane(int K, int QK) {
+    DnLane l;
+    l.nb = K / QK;
+    l.P = kGemvThreads / l.nb;
+    const int tid = threadIdx.x;
+    l.active = tid < l.P * l.nb;
+    l.rp = l.active ? tid / l.nb : 0;
+    l.b = l.active ? tid - l.rp * l.nb : 0;
+    return l;
+}
+
+// Every pass's down codes at once, from clamped rows (an item of fewer passes
+// re-reads its last row): all loads in flight together, no branch per pass.
+__device__ __forceinline__ void dn_load(const WindowParams& p, const DnItem& it, const DnLane& l, DnCodes& c) {
+    const int rlast = max(it.nrows, 1) - 1;
+#pragma unroll
+    for (int m = 0; m < kWinMaxPass; ++m) {
+        const int r = min(l.rp + m * l.P, rlast);
+        const size_t blk = (size_t)(min(it.h0 + r, p.H - 1)) * l.nb + l.b;
+        c.c[m] = ldg_u4(it.dcode + blk * 16);
+        c.sc[m] = ldg_u16(it.dscale + blk * 2);
+    }
+}
+
+// Wait for the group's gate/up and take its `a` rows.
+template <int QK>
+__device__ __forceinline__ void dn_begin(const WindowParams& p, const DnItem& it, float* lds) {
+    if (threadIdx.x == 0) {
+        long spins = 0;
+        while (__hip_atomic_load(win_ready(p.sync, it.g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+            if (++spins > kWinSpin) {
+                win_flag_error(p);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __syncthreads();
+    if (p.stage_words) {
+        // Each slice (token i, block column b) once, arranged into dot pairs
+        // of its hi and lo terms in LDS for every thread of column b.
+        constexpr int QT = QK == 64 ? 1 : 2, SW = SliceWords<QT, 2>::N;
+        const int nb = it.K / QK;
+        const __amdgpu_buffer_rsrc_t a_rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)it.a_src, 0, it.n_e * it.K * 4, kRsrcWord3);
+        for (int sl = threadIdx.x; sl < it.n_e * nb; sl += kGemvThreads) {
+            uint32_t w[QK];
+            long spins = 0;
+            // slice sl = i * nb + b starts at word i * K + b * QK = sl * QK
+            while (!load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK))) {
+                if (++spins > kWinSpin) {
+                    win_flag_error(p);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            XSlice<QT, 2> xs;
+            slice_from_packed<QT>(xs, w, p.z);
+            slice_to_lds<QT, 2>(xs, reinterpret_cast<uint32_t*>(lds) + sl * SW);
+        }
+    }
+    __syncthreads();
+}
+
+// Run the item's tokens through the held codes and publish d; count the item,
+// and combine the chunk or clear the group's state when this item is the
+// last of either.
+template <int QT>
+__device__ __forceinline__ void dn_finish(const WindowParams& p, WinLDS& R, const DnItem& it, const DnLane& l,
+                                          DnCodes& c, float* lds, int need_chunk) {
+    constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, 2>::N;
+    const int tid = threadIdx.x;
+    float* part = lds + p.stage_words;
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)it.a_src, 0, it.n_e * it.K * 4, kRsrcWord3);
+    // With the rows staged, this item holds its `a`: count it now (the result
+    // is looked at after the compute below); else after the compute.
+    int old_dn = 0;
+    if (p.stage_words && tid == 0)
+        old_dn = __hip_atomic_fetch_add(win_dn_count(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int nbp = (l.nb + 3) & ~3;
+    for (int t0 = 0; t0 < it.n_e; t0 += 2) {
+        const int nt = min(2, it.n_e - t0);
+        // One token at a time (its slice in registers), two per round of
+        // partial sums.
+#pragma unroll 1
+        for (int i = 0; i < nt; ++i) {
+#pragma unroll
+            for (int m = 0; m < kWinMaxPass; ++m) pin_u4(c.c[m]);
+            const int sl = (t0 + i) * l.nb + l.b;
+            XSlice<QT, 2> xs[1];
+            if (p.stage_words) {
+                slice_from_lds<QT, 2>(xs[0], reinterpret_cast<const uint32_t*>(lds) + sl * SW);
+            } else {
+                // Rows too large for LDS: straight from `a`, again while a word
+                // is still 0.
+                uint32_t w[QK];
+                long spins = 0;
+                while (!load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK))) {
+                    if (++spins > kWinSpin) {
+                        win_flag_error(p);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                slice_from_packed<QT>(xs[0], w, p.z);
+            }
+#pragma unroll
+            for (int m = 0; m < kWinMaxPass; ++m) {
+                const int r = l.rp + m * l.P;
+                if (l.active && r < it.nrows) {   // r < nrows <= P * passes
+                    float o[1];
+                    block_dot<QT, 2, 1>(c.c[m], scale_at_use(c.sc[m]), xs, 1, o);
+                    part[(r * 2 + i) * nbp + l.b] = o[0];
+                }
+            }
+        }
+        lds_barrier();
+        for (int i = tid; i < it.nrows * 2; i += kGemvThreads) {
+            const int r = i >> 1, t = i & 1;
+            if (t >= nt) continue;
+            const float v = sum_columns(part + (r * 2 + t) * nbp, l.nb);
+            const int drow = it.sh ? kSmallT * p.k + it.first + t0 + t : R.sorted[it.first + t0 + t];
+            __hip_atomic_store(p.d + (size_t)drow * p.H + it.h0 + r, nonzero_bits(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        lds_barrier();   // the partials are reused by the next pair
+    }
+    // Every d store of the item has completed before the chunk is counted
+    // (this also waits for the next item's codes, loaded while this one ran).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        if (!p.stage_words)
+            old_dn = __hip_atomic_fetch_add(win_dn_count(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(win_chunk(p.sync, p.k, it.ch), 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        R.flag_combine = old == need_chunk - 1;
+        R.flag_reset = old_dn == it.group_items - 1;
+    }
+    __syncthreads();
+    if (R.flag_combine) {
+        if (tid == 0) __hip_atomic_store(win_chunk(p.sync, p.k, it.ch), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        combine_chunk(p, R, it.ch * p.chunk_rows, min((it.ch + 1) * p.chunk_rows, p.H));
+    }
+    if (R.flag_reset) {
+        // Every item of the group holds its `a` rows: clear them, and the
+        // group's counters and flag.
+        for (int i = tid; i < it.n_e * it.K; i += kGemvThreads)
+            __hip_atomic_store(const_cast<uint32_t*>(it.a_src) + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            __hip_atomic_store(win_gu_count(p.sync, it.g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(win_ready(p.sync, it.g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(win_dn_count(p.sync, it.g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    lds_barrier();   // the flags and the staging area are reused by the next item
+}
+
+// Items blockIdx.x - n_gu_wg, + n_dn_wg, ...: the next item's codes are
+// loaded once the current one's `a` rows are in LDS (the staging waits for
+// every load of the workgroup), before its compute.
+template <int QT>
+__device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, float* lds) {
+    constexpr int QK = QTraits<QT>::QK;
+    const int n_routed = R.n_groups * p.n_chunks;
+    const int n_sg = p.FFs ? (p.T + kWinGroup - 1) / kWinGroup : 0;
+    const int n_items = n_routed + n_sg * p.n_chunks * p.sh_items;
+    const int need_chunk = R.n_groups + n_sg * p.sh_items;
+    int item = blockIdx.x - p.n_gu_wg;
+    if (item >= n_items) return;
+    DnItem ia = dn_item<QK>(p, R, item, n_routed), ib;
+    DnLane la = dn_lane(ia.K, QK), lb;
+    DnCodes ca, cb;
+    dn_load(p, ia, la, ca);
+    while (true) {
+        int next = item + p.n_dn_wg;
+        dn_begin<QK>(p, ia, lds);
+        ib = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
+        lb = dn_lane(ib.K, QK);
+        dn_load(p, ib, lb, cb);
+        dn_finish<QT>(p, R, ia, la, ca, lds, need_chunk);
+        if (next >= n_items) break;
+        item = next;
+        next = item + p.n_dn_wg;
+        dn_begin<QK>(p, ib, lds);
+        ia = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
+        la = dn_lane(ia.K, QK);
+        dn_load(p, ia, la, ca);
+        dn_finish<QT>(p, R, ib, lb, cb, lds, need_chunk);
+        if (next >= n_items) break;
+        item = next;
+    }
+}
+
+template <int QT, int NTERM>
+__global__ void __launch_bounds__(kGemvThreads, 2) window_layer_kernel(WindowParams p) {
+    extern __shared__ __align__(16) float lds[];
+    __shared__ WinLDS R;
+    route_window(p, R, reinterpret_cast<uint64_t*>(lds));
+    if (blockIdx.x == 0) {
+        for (int q = threadIdx.x; q < p.T * p.k; q += kGemvThreads) {
+            if (p.ids_out) p.ids_out[q] = R.id[q];
+            if (p.w_out) p.w_out[q] = R.w[q];
+        }
+    }
+    if ((int)blockIdx.x < p.n_gu_wg) gateup_window<QT, NTERM>(p, R, lds);
+    else down_window<QT>(p, R, lds);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------------------------
+constexpr size_t kWinLdsMax = 100 * 1024;   // dynamic LDS beyond which slices and `a` are read from memory
+
+WindowShape window_shape(int H, int FF, int FFs, int qtype, int x_dtype, int T, int k) {
+    WindowShape g{};
+    const int qk = codes_per_block(qtype);
+    const int nblk = H / qk, P = kGemvThreads / nblk;
+    const int nb_r = FF / qk, P_r = kGemvThreads / nb_r;
+    // Activation slice words per block column (SliceWords): dot pairs of one
+    // (bf16) or two (fp32) terms, the per-q offsets and z * sum x.
+    const int nterm = x_dtype == 1 ? 1 : 2;
+    const int sw = (nterm * qk / 2 + (qk == 64 ? 3 : 1) + 1 + 3) & ~3;
+    const size_t x_bytes = (size_t)T * nblk * sw * 4;
+    g.gu_passes = kWinMaxPass;
+    const int rows_gu = P * g.gu_passes;
+    g.tiles_gu = (FF + rows_gu - 1) / rows_gu;
+    g.tiles_gu_s = FFs ? (FFs + rows_gu - 1) / rows_gu : 0;
+    const int ncol = nblk % 2 == 0 ? nblk / 2 : nblk;
+    const size_t part_gu = (size_t)2 * rows_gu * 2 * ((ncol + 3) & ~3) * 4;
+    g.x_off = (int)(part_gu / 4);
+    // Every token's slices in LDS unless that would pass the budget; then each
+    // token's slice is read from the activations where it is used.
+    const bool x_lds = part_gu + x_bytes <= kWinLdsMax;
+    if (!x_lds) g.x_off = -1;
+    const size_t lds_gu = part_gu + (x_lds ? x_bytes : 0);
+    // Down: chunks of 8 passes of the routed experts' rows; the shared
+    // expert covers a chunk in sub-ranges of at most 8 passes.
+    g.dn_passes = kWinMaxPass;
+    g.chunk_rows = P_r * g.dn_passes;
+    g.n_chunks = (H + g.chunk_rows - 1) / g.chunk_rows;
+    size_t part_dn = (size_t)g.chunk_rows * 2 * ((nb_r + 3) & ~3) * 4;
+    if (FFs) {
+        const int nb_s = FFs / qk, P_s = kGemvThreads / nb_s;
+        const int ps = (g.chunk_rows + P_s - 1) / P_s;
+        g.sh_passes = ps > kWinMaxPass ? kWinMaxPass : ps;
+        g.sh_rows = P_s * g.sh_passes;
+        g.sh_items = (g.chunk_rows + g.sh_rows - 1) / g.sh_rows;
+        const size_t pss = (size_t)g.sh_rows * 2 * ((nb_s + 3) & ~3) * 4;
+        part_dn = pss > part_dn ? pss : part_dn;
+    }
+    // One group's `a` rows as arranged slices (hi and lo dot pairs, the
+    // per-q offsets and z * sum: SliceWords), unless they would pass the
+    // budget; then each thread reads its slices from `a`.
+    const int sw2 = (qk + (qk == 64 ? 3 : 1) + 1 + 3) & ~3;
+    const long slices = (long)(T < kWinGroup ? T : kWinGroup) * ((FF > FFs ? FF : FFs) / qk);
+    g.stage_words = (int)(slices * sw2);
+    if ((size_t)g.stage_words * 4 + part_dn > kWinLdsMax) g.stage_words = 0;
+    const size_t lds_dn = (size_t)g.stage_words * 4 + part_dn;
+    g.lds_bytes = lds_gu > lds_dn ? lds_gu : lds_dn;
+    const size_t topk_scratch = (size_t)kGemvThreads / 64 * 128 * 8;   // the routing's, before any of the above
+    if (g.lds_bytes < topk_scratch) g.lds_bytes = topk_scratch;
+    const int n_sg = FFs ? (T + kWinGroup - 1) / kWinGroup : 0;
+    const int max_gu = T * k * g.tiles_gu + n_sg * g.tiles_gu_s;
+    const int max_dn = T * k * g.n_chunks + n_sg * g.n_chunks * g.sh_items;
+    g.n_gu_wg = max_gu < kWinGuWorkgroups ? max_gu : kWinGuWorkgroups;
+    g.n_dn_wg = max_dn < kWinDnWorkgroups ? max_dn : kWinDnWorkgroups;
+    g.grid = g.n_gu_wg + g.n_dn_wg;
+    return g;
+}
+
+size_t window_sync_bytes(int k, int n_chunks) { return (size_t)64 * (2 + 3 * (kSmallT * k + kWinShared) + n_chunks); }
+
+template <int QT, int NTERM>
+static hipError_t launch_window_t(const WindowShape& g, const WindowParams& p, hipStream_t s) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)window_layer_kernel<QT, NTERM>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((window_layer_kernel<QT, NTERM>), dim3(g.grid), dim3(kGemvThreads), g.lds_bytes, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_window_layer(const WindowShape& g, const void* const* table, const void* single,
+                               const void* shared, const void* x, int x_dtype, const float* logits, int T, int E,
+                               int k, int renorm, int identity, int qtype, float z, int H, int FF, int FFs,
+                               int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y, hipStream_t s,
+                               StageMarks* marks) {
+    WindowParams p{};
+    p.table = table;
+    p.single = (const uint8_t*)single;
+    p.shared = (const uint8_t*)shared;
+    p.x = x;
+    p.logits = logits;
+    p.T = T;
+    p.E = E;
+    p.k = k;
+    p.renorm = renorm;
+    p.identity = identity;
+    p.H = H;
+    p.FF = FF;
+    p.FFs = FFs;
+    p.z = z;
+    p.ids_out = ids_out;
+    p.w_out = w_out;
+    p.a = (uint32_t*)(ws + L.a);
+    p.as = (uint32_t*)(ws + L.as);
+    p.d = (uint32_t*)(ws + L.d);
+    p.y = y;
+    p.sync = (int*)(ws + L.sync);
+    p.gu_passes = g.gu_passes;
+    p.tiles_gu = g.tiles_gu;
+    p.tiles_gu_s = g.tiles_gu_s;
+    p.dn_passes = g.dn_passes;
+    p.chunk_rows = g.chunk_rows;
+    p.n_chunks = g.n_chunks;
+    p.sh_passes = g.sh_passes;
+    p.sh_rows = g.sh_rows;
+    p.sh_items = g.sh_items;
+    p.n_gu_wg = g.n_gu_wg;
+    p.n_dn_wg = g.n_dn_wg;
+    p.x_off = g.x_off;
+    p.stage_words = g.stage_words;
+    stage_mark(marks, s);
+    hipError_t e;
+    const bool bf = x_dtype == 1;
+    if (qtype == 1)
+        e = bf ? launch_window_t<1, 1>(g, p, s) : launch_window_t<1, 2>(g, p, s);
+    else
+        e = bf ? launch_window_t<2, 1>(g, p, s) : launch_window_t<2, 2>(g, p, s);
+    stage_mark(marks, s);
+    return e;
+}
+
+}  // namespace moe

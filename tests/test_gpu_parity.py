@@ -307,15 +307,24 @@ def test_k_equals_e_and_single_expert():
     assert max_err_over_rms(y.cpu().numpy(), oracle.expert_ffn(blobs[0], 2, 7.5, H, FF, x)) <= TOL
 
 
-def _decode_fixed_bytes(k, ff, shared_ff, small_t=8):
-    """Bytes at the start of a layer workspace that the decode kernel keeps
-    between calls: its sync words (64-byte lines, then 16 replicas of the ready
-    flags) sized for small_t tokens, then the `a` words of small_t * k pairs and
-    of small_t shared-expert rows, each region 256-byte aligned."""
+def _decode_fixed_bytes(k, hidden, ff, shared_ff, qk, small_t=8):
+    """Bytes at the start of a layer workspace that the decode kernels keep
+    between calls, each region 256-byte aligned: the sync words (the larger of
+    the one-token kernel's 64-byte lines plus 16 replicas of its ready flags,
+    and the window kernel's lines: 2, then 3 per group of small_t * k + 4,
+    then one per chunk of 8 passes of down rows), then the `a` words of
+    small_t * k pairs and of small_t shared-expert rows, then the window
+    kernel's d words for small_t * k + small_t rows of hidden."""
     al = lambda v: (v + 255) // 256 * 256
     lines = 64 * (4 + small_t * k + small_t + 16)
-    sync = (lines + 4095) // 4096 * 4096 + 16 * 4096
-    return al(al(sync) + small_t * k * ff * 4) + al(small_t * shared_ff * 4)
+    sync1 = (lines + 4095) // 4096 * 4096 + 16 * 4096
+    chunk_rows = (256 // (ff // qk)) * 8
+    n_chunks = (hidden + chunk_rows - 1) // chunk_rows
+    syncw = 64 * (2 + 3 * (small_t * k + 4) + n_chunks)
+    off = al(max(sync1, syncw))
+    off = al(off + small_t * k * ff * 4)
+    off = al(off + small_t * shared_ff * 4)
+    return al(off + (small_t * k + small_t) * hidden * 4)
 
 
 def test_workspace_shared_state_returns_to_zero():
@@ -328,7 +337,7 @@ def test_workspace_shared_state_returns_to_zero():
     desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k, shared_ff=w.shared_ff)
     sizes = (1, 3, 8, 20, 1, 8, 2)
     ws = moe.workspace(max(moe.layer_workspace_bytes(desc, T) for T in sizes), DEV)
-    fixed = _decode_fixed_bytes(w.top_k, w.ff, w.shared_ff)
+    fixed = _decode_fixed_bytes(w.top_k, w.hidden, w.ff, w.shared_ff, 64 if w.qtype == 1 else 32)
     assert fixed <= moe.layer_workspace_bytes(desc, 1)
     for i, T in enumerate(sizes):
         x, logits = wl.device_inputs(w, 0, 50 + i, device=DEV, tokens=T)
@@ -370,4 +379,4 @@ def test_graph_replays_match_eager():
         # eager work between replays
         moe.layer_forward(desc, arena.tables[0], *inputs[1], ws=moe.workspace(moe.layer_workspace_bytes(desc, 1), DEV))
         torch.cuda.synchronize()
-    assert int((ws[:_decode_fixed_bytes(w.top_k, w.ff, 0)] != 0).sum().item()) == 0
+    assert int((ws[:_decode_fixed_bytes(w.top_k, w.hidden, w.ff, 0, 64 if w.qtype == 1 else 32)] != 0).sum().item()) == 0
