@@ -75,15 +75,13 @@ struct GemvShape {
     int grid;
 };
 
-// Verify windows (2 <= T <= kSmallT): work items and workgroups of the
-// window kernel.
-constexpr int kWinGuWorkgroups = 256;
-constexpr int kWinDnWorkgroups = 256;
+// Verify windows (2 <= T <= kSmallT): work items of the window kernel (its
+// grid is set at launch from the GPU's capacity).
 struct WindowShape {
     int gu_passes, tiles_gu, tiles_gu_s;     // gate/up: passes per tile; tiles per routed / shared expert
     int dn_passes, chunk_rows, n_chunks;     // down: passes per routed item; H rows per chunk; chunks
     int sh_passes, sh_rows, sh_items;        // down of the shared expert: passes, rows and items per chunk
-    int n_gu_wg, n_dn_wg;
+    int max_items;           // the larger of the gate/up and down item counts, at most
     int x_off, stage_words;
     size_t lds_bytes;
     int grid;

@@ -22,17 +22,23 @@
 // The shared expert's groups hold the window's tokens two at a time; its down
 // items cover a chunk in several sub-ranges of rows.
 //
-// Workgroups [0, n_gu_wg) take the gate/up items (item i by workgroup
-// i % n_gu_wg), the others the down items, so a down workgroup only ever waits
-// for gate/up work of workgroups dispatched before it.  Each gate/up tile
-// bumps its group's counter; the tile that completes the group raises the
-// group's ready flag, and the down items of that group start from it (no wait
-// for other groups).  Each down item then bumps its chunk's counter; the item
-// that completes a chunk combines it: y[t][h] = shared + sum_j w[t][j] d, the
-// slots summed in rank order, so the output does not depend on timing.
+// Workgroup w takes the gate/up items w, w + G, ... and then the down items
+// w, w + G, ... (G = the grid).  G is at most the number of workgroups the GPU
+// holds at once (two per CU where registers and LDS allow), so that every
+// workgroup is resident: a down item waits for gate/up items of other
+// workgroups, which never wait, so every wait ends.  (If other work holds
+// part of the GPU, the waits last until it leaves room.)  Each gate/up tile
+// bumps its group's counter, and the down items of a group start once its
+// counter is complete (no wait for other groups).  Each down item then bumps
+// its chunk's counter; the item that completes a chunk combines it (its
+// workgroup looks at the count once the next item's `a` is in LDS, so the
+// count's round trip overlaps other work): y[t][h] = shared + sum_j w[t][j] d,
+// the slots summed in rank order, so the output does not depend on timing.
+// Readers of `a` and d read again any word still 0, so no count waits for the
+// stores before it.
 //
 // Every piece of shared state is returned to zero by its last user: the last
-// down item of a group clears the group's counters, flag and `a` rows; the
+// down item of a group clears the group's counters and `a` rows; the
 // combining item clears its chunk's counter and the d words it read.  The
 // bounded waits flag an error if a bound is ever reached.
 #include "moe_gemv_common.h"
@@ -68,19 +74,19 @@ struct WindowParams {
     int gu_passes, tiles_gu, tiles_gu_s;
     int dn_passes, chunk_rows, n_chunks;
     int sh_passes, sh_rows, sh_items;
-    int n_gu_wg, n_dn_wg;
+    int n_wg;                   // the grid
     int x_off;                  // gate/up: LDS word offset of the activation slices
     int stage_words;            // down: LDS words reserved for the staged `a` rows
 };
 
 // Sync lines (16 ints each): line 1 the error flag; per group g (routed
 // groups g < 8k, the shared expert's groups from 8k on) its gate/up tile
-// count, its ready flag and its down item count; then one counter per chunk.
+// count (complete at tiles_gu) and its down item count; then one counter per
+// chunk.
 __device__ __forceinline__ int* win_error(int* s) { return s + 16; }
-__device__ __forceinline__ int* win_gu_count(int* s, int g) { return s + 16 * (2 + 3 * g); }
-__device__ __forceinline__ int* win_ready(int* s, int g) { return s + 16 * (3 + 3 * g); }
-__device__ __forceinline__ int* win_dn_count(int* s, int g) { return s + 16 * (4 + 3 * g); }
-__device__ __forceinline__ int* win_chunk(int* s, int k, int c) { return s + 16 * (2 + 3 * (kSmallT * k + kWinShared) + c); }
+__device__ __forceinline__ int* win_gu_count(int* s, int g) { return s + 16 * (2 + 2 * g); }
+__device__ __forceinline__ int* win_dn_count(int* s, int g) { return s + 16 * (3 + 2 * g); }
+__device__ __forceinline__ int* win_chunk(int* s, int k, int c) { return s + 16 * (2 + 2 * (kSmallT * k + kWinShared) + c); }
 
 __device__ __forceinline__ void win_flag_error(const WindowParams& p) {
     __hip_atomic_store(win_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -92,6 +98,7 @@ struct WinLDS {
     alignas(16) int key[kWinPairs + 4];   // expert << 8 | slot, padded with INT_MAX
     int sorted[kWinPairs];          // sorted position -> slot
     int group_first[kWinPairs + 1]; // first sorted position of each group; [n_groups] = T * k
+    int gorder[kWinPairs];          // groups in work order: full groups (kWinGroup tokens) first
     int n_groups;
     int flag_combine, flag_reset;
 };
@@ -146,6 +153,27 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
             R.n_groups = base;
             R.group_first[base] = n;
         }
+        __builtin_amdgcn_wave_barrier();
+        // Work order: the groups with kWinGroup tokens (the heaviest items)
+        // first, each class in group order, so that round-robin items put
+        // at most about one heavy item on each workgroup.
+        const int ng = base;
+        int n_full = 0;
+        for (int g0 = 0; g0 < ng; g0 += 64) {
+            const int g = g0 + lane;
+            n_full += __popcll(__ballot(g < ng && R.group_first[g + 1] - R.group_first[g] == kWinGroup));
+        }
+        int fb = 0, pb = n_full;
+        for (int g0 = 0; g0 < ng; g0 += 64) {
+            const int g = g0 + lane;
+            const bool full = g < ng && R.group_first[g + 1] - R.group_first[g] == kWinGroup;
+            const bool part = g < ng && !full;
+            const uint64_t mf = __ballot(full), mp = __ballot(part);
+            if (full) R.gorder[fb + lanes_below(mf)] = g;
+            if (part) R.gorder[pb + lanes_below(mp)] = g;
+            fb += __popcll(mf);
+            pb += __popcll(mp);
+        }
     }
     __syncthreads();
 }
@@ -163,8 +191,9 @@ __device__ __forceinline__ GuItem gu_item(const WindowParams& p, const WinLDS& R
     it.sh = item >= n_routed;
     int tile;
     if (!it.sh) {
-        it.g = item / p.tiles_gu;
-        tile = item - it.g * p.tiles_gu;
+        const int gi = item / p.tiles_gu;
+        it.g = R.gorder[gi];
+        tile = item - gi * p.tiles_gu;
         it.first = R.group_first[it.g];
         it.n_e = R.group_first[it.g + 1] - it.first;
         it.blob = p.table ? table_blob(p.table, R.id[R.sorted[it.first]]) : p.single;
@@ -284,22 +313,18 @@ __device__ __forceinline__ void gu_compute(const WindowParams& p, const WinLDS& 
         }
         lds_barrier();   // the partials are reused by the next pair
     }
-    // Every `a` store of the tile has completed before it is counted (this
-    // also waits for the next item's codes, loaded while this one ran).
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(win_gu_count(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (it.sh ? p.tiles_gu_s : p.tiles_gu) - 1)
-            __hip_atomic_store(win_ready(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    // Count the tile without waiting, for its stores or for the count: a
+    // reader that sees the group complete before a word of `a` has landed
+    // reads the word again (it is still 0).
+    if (tid == 0) atomic_add_detached(win_gu_count(p.sync, it.g), 1);
 }
 
-// Items blockIdx.x, + n_gu_wg, ...: the next item's codes are loaded before
+// Items blockIdx.x, + n_wg, ...: the next item's codes are loaded before
 // the current one is computed (two buffers in turn), so that its loads
 // overlap the compute.  With no next item, the current one's are read again.
 template <int QT, int NTERM>
-__device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLDS& R, float* lds) {
+// x_done: activation slices already arranged in LDS.
+__device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLDS& R, float* lds, int x_done) {
     constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
     const int tid = threadIdx.x;
     const int n_routed = R.n_groups * p.tiles_gu;
@@ -318,7 +343,7 @@ __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLD
         // Every token's activation slice of every block column, once per
         // workgroup, while the first item's weights are on their way.
         uint32_t* xsl = reinterpret_cast<uint32_t*>(lds) + p.x_off;
-        for (int s = tid; s < p.T * nblk; s += kGemvThreads) {
+        for (int s = x_done + tid; s < p.T * nblk; s += kGemvThreads) {
             const int t = s / nblk, bb = s - t * nblk;
             XSlice<QT, NTERM> x1;
             if constexpr (NTERM == 1)
@@ -330,13 +355,13 @@ __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLD
     }
     __syncthreads();
     while (true) {
-        int next = item + p.n_gu_wg;
+        int next = item + p.n_wg;
         ib = gu_item(p, R, next < n_items ? next : item, n_routed, Rr);
         gu_load(ib, nblk, P, rp, b, cb);
         gu_compute<QT, NTERM>(p, R, ia, ca, lds, nblk, P, rp, b, active);
         if (next >= n_items) break;
         item = next;
-        next = item + p.n_gu_wg;
+        next = item + p.n_wg;
         ia = gu_item(p, R, next < n_items ? next : item, n_routed, Rr);
         gu_load(ia, nblk, P, rp, b, ca);
         gu_compute<QT, NTERM>(p, R, ib, cb, lds, nblk, P, rp, b, active);
@@ -479,8 +504,9 @@ __device__ __forceinline__ DnItem dn_item(const WindowParams& p, const WinLDS& R
     it.sh = item >= n_routed;
     const uint8_t* blob;
     if (!it.sh) {
-        it.g = item / p.n_chunks;
-        it.ch = item - it.g * p.n_chunks;
+        const int gi = item / p.n_chunks;
+        it.g = R.gorder[gi];
+        it.ch = item - gi * p.n_chunks;
         it.h0 = it.ch * p.chunk_rows;
         it.nrows = min(p.chunk_rows, p.H - it.h0);
         it.first = R.group_first[it.g];
@@ -553,7 +579,8 @@ template <int QK>
 __device__ __forceinline__ void dn_begin(const WindowParams& p, const DnItem& it, float* lds) {
     if (threadIdx.x == 0) {
         long spins = 0;
-        while (__hip_atomic_load(win_ready(p.sync, it.g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+        const int need = it.sh ? p.tiles_gu_s : p.tiles_gu;
+        while (__hip_atomic_load(win_gu_count(p.sync, it.g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
             if (++spins > kWinSpin) {
                 win_flag_error(p);
                 break;
@@ -592,16 +619,15 @@ __device__ __forceinline__ void dn_begin(const WindowParams& p, const DnItem& it
 // and combine the chunk or clear the group's state when this item is the
 // last of either.
 template <int QT>
-__device__ __forceinline__ void dn_finish(const WindowParams& p, WinLDS& R, const DnItem& it, const DnLane& l,
-                                          DnCodes& c, float* lds, int need_chunk) {
+__device__ __forceinline__ void dn_finish(const WindowParams& p, const WinLDS& R, const DnItem& it, const DnLane& l,
+                                          DnCodes& c, float* lds, int& old_chunk, int& old_dn) {
     constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, 2>::N;
     const int tid = threadIdx.x;
     float* part = lds + p.stage_words;
     const __amdgpu_buffer_rsrc_t a_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)it.a_src, 0, it.n_e * it.K * 4, kRsrcWord3);
-    // With the rows staged, this item holds its `a`: count it now (the result
-    // is looked at after the compute below); else after the compute.
-    int old_dn = 0;
+    // With the rows staged, this item holds its `a`: count it now; else after
+    // the compute.
     if (p.stage_words && tid == 0)
         old_dn = __hip_atomic_fetch_add(win_dn_count(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int nbp = (l.nb + 3) & ~3;
@@ -652,16 +678,23 @@ __device__ __forceinline__ void dn_finish(const WindowParams& p, WinLDS& R, cons
         }
         lds_barrier();   // the partials are reused by the next pair
     }
-    // Every d store of the item has completed before the chunk is counted
-    // (this also waits for the next item's codes, loaded while this one ran).
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // Count the item in its chunk (and, without staged rows, in its group);
+    // the counts are looked at in dn_settle.
     if (tid == 0) {
         if (!p.stage_words)
             old_dn = __hip_atomic_fetch_add(win_dn_count(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int old = __hip_atomic_fetch_add(win_chunk(p.sync, p.k, it.ch), 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        R.flag_combine = old == need_chunk - 1;
+        old_chunk = __hip_atomic_fetch_add(win_chunk(p.sync, p.k, it.ch), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// After an item's counts have returned (thread 0 holds them): combine its
+// chunk if the item completed it; clear its group's state if the item was the
+// group's last to take its `a` rows.
+__device__ __forceinline__ void dn_settle(const WindowParams& p, WinLDS& R, const DnItem& it, int old_chunk, int old_dn,
+                                          int need_chunk) {
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        R.flag_combine = old_chunk == need_chunk - 1;
         R.flag_reset = old_dn == it.group_items - 1;
     }
     __syncthreads();
@@ -671,19 +704,18 @@ __device__ __forceinline__ void dn_finish(const WindowParams& p, WinLDS& R, cons
     }
     if (R.flag_reset) {
         // Every item of the group holds its `a` rows: clear them, and the
-        // group's counters and flag.
+        // group's counters.
         for (int i = tid; i < it.n_e * it.K; i += kGemvThreads)
             __hip_atomic_store(const_cast<uint32_t*>(it.a_src) + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (tid == 0) {
             __hip_atomic_store(win_gu_count(p.sync, it.g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(win_ready(p.sync, it.g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(win_dn_count(p.sync, it.g), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    lds_barrier();   // the flags and the staging area are reused by the next item
+    __syncthreads();   // the flags are written again by the next settle
 }
 
-// Items blockIdx.x - n_gu_wg, + n_dn_wg, ...: the next item's codes are
+// Items blockIdx.x, + n_wg, ...: the next item's codes are
 // loaded once the current one's `a` rows are in LDS (the staging waits for
 // every load of the workgroup), before its compute.
 template <int QT>
@@ -693,28 +725,39 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
     const int n_sg = p.FFs ? (p.T + kWinGroup - 1) / kWinGroup : 0;
     const int n_items = n_routed + n_sg * p.n_chunks * p.sh_items;
     const int need_chunk = R.n_groups + n_sg * p.sh_items;
-    int item = blockIdx.x - p.n_gu_wg;
+    int item = blockIdx.x;
     if (item >= n_items) return;
     DnItem ia = dn_item<QK>(p, R, item, n_routed), ib;
     DnLane la = dn_lane(ia.K, QK), lb;
     DnCodes ca, cb;
     dn_load(p, ia, la, ca);
+    // Counts of the previous item (thread 0), settled after the next item's
+    // `a` rows are in LDS.
+    int oc_a = 0, od_a = 0, oc_b = 0, od_b = 0;
     while (true) {
-        int next = item + p.n_dn_wg;
+        int next = item + p.n_wg;
         dn_begin<QK>(p, ia, lds);
+        if (item != (int)blockIdx.x) dn_settle(p, R, ib, oc_b, od_b, need_chunk);
         ib = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         lb = dn_lane(ib.K, QK);
         dn_load(p, ib, lb, cb);
-        dn_finish<QT>(p, R, ia, la, ca, lds, need_chunk);
-        if (next >= n_items) break;
+        dn_finish<QT>(p, R, ia, la, ca, lds, oc_a, od_a);
+        if (next >= n_items) {
+            dn_settle(p, R, ia, oc_a, od_a, need_chunk);
+            break;
+        }
         item = next;
-        next = item + p.n_dn_wg;
+        next = item + p.n_wg;
         dn_begin<QK>(p, ib, lds);
+        dn_settle(p, R, ia, oc_a, od_a, need_chunk);
         ia = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         la = dn_lane(ia.K, QK);
         dn_load(p, ia, la, ca);
-        dn_finish<QT>(p, R, ib, lb, cb, lds, need_chunk);
-        if (next >= n_items) break;
+        dn_finish<QT>(p, R, ib, lb, cb, lds, oc_b, od_b);
+        if (next >= n_items) {
+            dn_settle(p, R, ib, oc_b, od_b, need_chunk);
+            break;
+        }
         item = next;
     }
 }
@@ -723,15 +766,51 @@ template <int QT, int NTERM>
 __global__ void __launch_bounds__(kGemvThreads, 2) window_layer_kernel(WindowParams p) {
     extern __shared__ __align__(16) float lds[];
     __shared__ WinLDS R;
+    constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
+    const int tid = threadIdx.x;
+    const int nblk = p.H / QK, n_x = p.T * nblk;
+    // bf16 activations: the words of the first two slices of each thread are
+    // loaded before the routing, so that they arrive while it runs; the slices
+    // are arranged once it is done.
+    const bool pre = NTERM == 1 && p.x_off >= 0;
+    uint32_t xr[2][QK / 2];
+    if (pre) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int sx = min(tid + kGemvThreads * i, n_x - 1);
+            const int t = sx / nblk, bb = sx - t * nblk;
+            const uint4* src = reinterpret_cast<const uint4*>((const uint16_t*)p.x + (size_t)t * p.H + bb * QK);
+#pragma unroll
+            for (int v = 0; v < QK / 8; ++v) {
+                const uint4 u = ldg_u4(src + v);
+                xr[i][4 * v + 0] = u.x;
+                xr[i][4 * v + 1] = u.y;
+                xr[i][4 * v + 2] = u.z;
+                xr[i][4 * v + 3] = u.w;
+            }
+        }
+    }
     route_window(p, R, reinterpret_cast<uint64_t*>(lds));
+    if (pre) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int sx = tid + kGemvThreads * i;
+            if (sx < n_x) {
+                XSlice<QT, 1> x1;
+                arrange_pairs<QT>(xr[i], x1.pr[0]);
+                finish_slice<QT, 1>(x1, p.z);
+                slice_to_lds<QT, 1>(x1, reinterpret_cast<uint32_t*>(lds) + p.x_off + sx * SW);
+            }
+        }
+    }
     if (blockIdx.x == 0) {
         for (int q = threadIdx.x; q < p.T * p.k; q += kGemvThreads) {
             if (p.ids_out) p.ids_out[q] = R.id[q];
             if (p.w_out) p.w_out[q] = R.w[q];
         }
     }
-    if ((int)blockIdx.x < p.n_gu_wg) gateup_window<QT, NTERM>(p, R, lds);
-    else down_window<QT>(p, R, lds);
+    gateup_window<QT, NTERM>(p, R, lds, pre ? 2 * kGemvThreads : 0);
+    down_window<QT>(p, R, lds);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -790,25 +869,59 @@ WindowShape window_shape(int H, int FF, int FFs, int qtype, int x_dtype, int T, 
     const int n_sg = FFs ? (T + kWinGroup - 1) / kWinGroup : 0;
     const int max_gu = T * k * g.tiles_gu + n_sg * g.tiles_gu_s;
     const int max_dn = T * k * g.n_chunks + n_sg * g.n_chunks * g.sh_items;
-    g.n_gu_wg = max_gu < kWinGuWorkgroups ? max_gu : kWinGuWorkgroups;
-    g.n_dn_wg = max_dn < kWinDnWorkgroups ? max_dn : kWinDnWorkgroups;
-    g.grid = g.n_gu_wg + g.n_dn_wg;
+    g.max_items = max_gu > max_dn ? max_gu : max_dn;
+    g.grid = 0;   // set at launch from the GPU's capacity
     return g;
 }
 
-size_t window_sync_bytes(int k, int n_chunks) { return (size_t)64 * (2 + 3 * (kSmallT * k + kWinShared) + n_chunks); }
+size_t window_sync_bytes(int k, int n_chunks) { return (size_t)64 * (2 + 2 * (kSmallT * k + kWinShared) + n_chunks); }
 
 template <int QT, int NTERM>
 static hipError_t launch_window_t(const WindowShape& g, const WindowParams& p, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)window_layer_kernel<QT, NTERM>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL((window_layer_kernel<QT, NTERM>), dim3(g.grid), dim3(kGemvThreads), g.lds_bytes, s, p);
+    // (the grid is p.n_wg, see window_grid; window_capacity has allowed the LDS)
+    hipLaunchKernelGGL((window_layer_kernel<QT, NTERM>), dim3(p.n_wg), dim3(kGemvThreads), g.lds_bytes, s, p);
     return hipGetLastError();
+}
+
+// Workgroups the current GPU holds at once for this instantiation and LDS
+// size (the kernel's registers and LDS decide), times its CUs; at most the
+// largest item count.  Cached per instantiation and LDS size.
+template <int QT, int NTERM>
+static hipError_t window_capacity(size_t lds_bytes, int* out) {
+    static int dev_cached = -1, n_cu = 0;
+    static size_t lds_cached = 0;
+    static int per_cu = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev != dev_cached || lds_bytes != lds_cached) {
+        e = hipFuncSetAttribute((const void*)window_layer_kernel<QT, NTERM>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                150 * 1024);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)window_layer_kernel<QT, NTERM>,
+                                                         kGemvThreads, lds_bytes);
+        if (e != hipSuccess) return e;
+        dev_cached = dev;
+        lds_cached = lds_bytes;
+    }
+    *out = per_cu * n_cu;
+    return hipSuccess;
+}
+
+static hipError_t window_grid(const WindowShape& g, int qtype, int x_dtype, int* grid) {
+    int cap = 0;
+    hipError_t e;
+    const bool bf = x_dtype == 1;
+    if (qtype == 1)
+        e = bf ? window_capacity<1, 1>(g.lds_bytes, &cap) : window_capacity<1, 2>(g.lds_bytes, &cap);
+    else
+        e = bf ? window_capacity<2, 1>(g.lds_bytes, &cap) : window_capacity<2, 2>(g.lds_bytes, &cap);
+    if (e != hipSuccess) return e;
+    if (cap < 1) return hipErrorInvalidConfiguration;
+    *grid = g.max_items < cap ? g.max_items : cap;
+    return hipSuccess;
 }
 
 hipError_t launch_window_layer(const WindowShape& g, const void* const* table, const void* single,
@@ -847,12 +960,13 @@ hipError_t launch_window_layer(const WindowShape& g, const void* const* table, c
     p.sh_passes = g.sh_passes;
     p.sh_rows = g.sh_rows;
     p.sh_items = g.sh_items;
-    p.n_gu_wg = g.n_gu_wg;
-    p.n_dn_wg = g.n_dn_wg;
+    int grid = 0;
+    hipError_t e = window_grid(g, qtype, x_dtype, &grid);
+    if (e != hipSuccess) return e;
+    p.n_wg = grid;
     p.x_off = g.x_off;
     p.stage_words = g.stage_words;
     stage_mark(marks, s);
-    hipError_t e;
     const bool bf = x_dtype == 1;
     if (qtype == 1)
         e = bf ? launch_window_t<1, 1>(g, p, s) : launch_window_t<1, 2>(g, p, s);
