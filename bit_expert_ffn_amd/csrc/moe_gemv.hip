@@ -3,28 +3,27 @@
 
 namespace moe {
 // ---------------------------------------------------------------------------------------------
-// Fused decode / verify layer: one kernel per layer.
+// Fused one-token decode layer: one kernel per layer.
 //
-// Every workgroup first recomputes the routing and the expert-major buckets of
-// the <= 8 tokens from the logits (a few KB, served from L2).  Workgroups
-// [0, n_gu) run gate/up + SwiGLU tiles and publish their rows of `a` with
-// agent-coherent stores; each tile then bumps its group's counter, and the tile
-// that completes a group raises the group's ready flag in each of n_ready
-// replicas (4 KB apart).  Workgroups [n_gu, grid) own a tile of H output rows:
-// they issue the loads of their down-projection weights for every selected
-// expert at once, wait until every group's flag in their replica (tile %
-// n_ready) is raised, read `a`, and finish the down projection and the
-// weighted combine for their rows (no second pass).  Polling one replica per
-// 16 workgroups keeps the pollers off the lines that the counters and flags
-// are written on.  Workgroups are dispatched in index order on each XCD, so
-// every gate/up workgroup is running or done before any down workgroup on the
-// same XCD starts waiting; the wait is bounded anyway and flags an error if
-// the bound is ever reached.  The last down workgroup to leave returns every
-// counter and flag to zero for the next call.  Same-address atomics serialise
-// (about 12 ns each), so counters are per group, on separate 64-byte lines,
-// and the exit count is two-level.
+// Every workgroup first recomputes the routing of the token from its logits
+// (a few KB, served from L2); the token's k slots are the groups, in rank
+// order.  Workgroups [0, n_gu) run gate/up + SwiGLU tiles and publish their
+// rows of `a` as never-zero packed words with agent-coherent stores; each
+// tile then bumps its group's counter, and the tile that completes a group
+// raises the group's ready flag in each of n_ready replicas (4 KB apart).
+// Workgroups [n_gu, n_gu + tiles_dn) own a tile of H output rows: they issue
+// the loads of their down-projection weights for every selected expert once
+// the first gate/up tile is done, wait until every group's flag in their
+// replica (tile % n_ready) is raised, copy `a` into LDS (reading again any word
+// still 0), and finish the down projection and the weighted combine for their
+// rows.  Polling one replica per 16 workgroups keeps the pollers off the lines
+// that the counters and flags are written on.  Workgroups are dispatched in
+// index order, so every gate/up workgroup is running or done before any down
+// workgroup starts waiting; the wait is bounded anyway and flags an error if
+// the bound is ever reached.  The last workgroup waits until every down
+// workgroup holds its `a` and returns the counters, flags and `a` words to
+// zero for the next call.
 // ---------------------------------------------------------------------------------------------
-constexpr int kMaxPairs = kSmallT * kMaxK;   // 256
 constexpr size_t kDecodeLdsBudget = 112 * 1024;   // dynamic LDS of the fused decode kernel
 constexpr int kMaxRowsDn = 12;               // H rows per down workgroup
 constexpr int kRowsPerThread = 6;            // down rows one thread prefetches
@@ -65,12 +64,11 @@ __device__ __forceinline__ int* sync_ready(int* s, int r, int g, int n_ctr) {
 }
 
 struct RouteLDS {
-    int id[kMaxPairs];
-    float w[kMaxPairs];
-    int pair_tok[kMaxPairs], pair_exp[kMaxPairs], slot_pair[kMaxPairs];
-    int group_first[kMaxPairs], group_n[kMaxPairs], group_of_pair[kMaxPairs];
-    int rank[kMaxPairs], pos[kMaxPairs], cnt[kMaxPairs];
-    int slot_src[kMaxPairs];   // slot (t, j) -> group * NT + token-in-group of its pair
+    int id[kMaxK];
+    float w[kMaxK];
+    int pair_tok[kMaxK], pair_exp[kMaxK], slot_pair[kMaxK];
+    int group_first[kMaxK], group_n[kMaxK], group_of_pair[kMaxK];
+    int slot_src[kMaxK];   // slot j -> group * NT + token-in-group of its pair
     uint64_t topk[kGemvThreads / 64][128];   // each wave's top-k scratch
     int n_groups;
     int flag;
@@ -81,88 +79,27 @@ __device__ __forceinline__ const uint8_t* expert_blob(const DecodeParams& p, int
     return (const uint8_t*)((const __attribute__((address_space(1))) uint64_t*)p.table)[e];
 }
 
-// Routing of the T tokens (wave w takes tokens w, w + 4) and the buckets: pairs
-// (token, slot) sorted by (expert, token); runs of <= NT pairs of one expert
-// form a group.
-template <int NT>
+// Routing of the token: its k slots are its pairs and groups, in rank order
+// (group numbering changes no arithmetic).
 __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int k = p.k, T = p.T;
-    if (T == 1) {
-        // One token: each of its k slots is its own pair and group, in rank
-        // order (group numbering changes no arithmetic).
-        if (wv == 0) {
-            int id = 0;
-            float wt = 1.f;
-            if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, R.topk[0], &id, &wt);
-            if (lane < k) {
-                R.id[lane] = id;
-                R.w[lane] = wt;
-                R.slot_pair[lane] = lane;
-                R.pair_tok[lane] = 0;
-                R.pair_exp[lane] = id;
-                R.group_first[lane] = lane;
-                R.group_n[lane] = 1;
-                R.group_of_pair[lane] = lane;
-                R.slot_src[lane] = lane * NT;
-            }
-            if (lane == 0) R.n_groups = k;
-        }
-        __syncthreads();
-        return;
-    }
-    for (int t = wv; t < T; t += kGemvThreads / 64) {
+    const int k = p.k;
+    if (wv == 0) {
         int id = 0;
         float wt = 1.f;
-        if (!p.identity) wave_topk(p.logits + (size_t)t * p.E, p.E, k, p.renorm, lane, R.topk[wv], &id, &wt);
+        if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, R.topk[0], &id, &wt);
         if (lane < k) {
-            R.id[t * k + lane] = id;
-            R.w[t * k + lane] = wt;
+            R.id[lane] = id;
+            R.w[lane] = wt;
+            R.slot_pair[lane] = lane;
+            R.pair_tok[lane] = 0;
+            R.pair_exp[lane] = id;
+            R.group_first[lane] = lane;
+            R.group_n[lane] = 1;
+            R.group_of_pair[lane] = lane;
+            R.slot_src[lane] = lane;
         }
-    }
-    __syncthreads();
-    const int n = T * k;
-    for (int q = tid; q < n; q += kGemvThreads) {
-        const int e = R.id[q], t = q / k;
-        int rank = 0, pos = 0, cnt = 0;
-        for (int t2 = 0; t2 < T; ++t2) {
-#pragma unroll 4
-            for (int j2 = 0; j2 < k; ++j2) {
-                const int er = R.id[t2 * k + j2];
-                rank += (er < e) || (er == e && t2 < t);
-                pos += (er == e && t2 < t);
-                cnt += (er == e);
-            }
-        }
-        R.rank[q] = rank;
-        R.pos[q] = pos;
-        R.cnt[q] = cnt;
-        R.pair_tok[rank] = t;
-        R.pair_exp[rank] = e;
-        R.slot_pair[q] = rank;
-    }
-    __syncthreads();
-    for (int q = tid; q < n; q += kGemvThreads) {
-        const int pos = R.pos[q], rq = R.rank[q];
-        int g = -1;   // groups start at pairs with pos % NT == 0; count those up to this pair
-#pragma unroll 4
-        for (int r = 0; r < n; ++r) g += (R.pos[r] % NT == 0) && (R.rank[r] <= rq);
-        R.group_of_pair[rq] = g;
-        if (pos % NT == 0) {
-            R.group_first[g] = rq;
-            R.group_n[g] = min(NT, R.cnt[q] - pos);
-        }
-    }
-    if (tid == 0) {
-        int ng = 0;
-        for (int r = 0; r < n; ++r) ng += (R.pos[r] % NT == 0);
-        R.n_groups = ng;
-    }
-    __syncthreads();
-    for (int q = tid; q < n; q += kGemvThreads) {
-        const int pr = R.slot_pair[q];
-        const int gg = R.group_of_pair[pr];
-        R.slot_src[q] = gg * NT + (pr - R.group_first[gg]);
+        if (lane == 0) R.n_groups = k;
     }
     __syncthreads();
 }
@@ -640,8 +577,9 @@ __device__ void janitor_role(const DecodeParams& p, RouteLDS& R) {
         __hip_atomic_store(p.as + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int QT, int NT, int NTERM>
-__global__ void __launch_bounds__(kGemvThreads, NT == 1 ? 3 : 2) decode_layer_kernel(DecodeParams p) {
+template <int QT, int NTERM>
+__global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodeParams p) {
+    constexpr int NT = 1;   // one token
     extern __shared__ __align__(16) float lds[];   // 16-byte aligned: float4 reads
     __shared__ RouteLDS R;
     const int tid = threadIdx.x;
@@ -661,7 +599,7 @@ __global__ void __launch_bounds__(kGemvThreads, NT == 1 ? 3 : 2) decode_layer_ke
             slice_to_lds<QT, NTERM>(xsl, reinterpret_cast<uint32_t*>(lds) + p.x_off + b * SliceWords<QT, NTERM>::N);
         }
     }
-    route_and_bucket<NT>(p, R);
+    route_and_bucket(p, R);
     if (wg == 0) {
         for (int q = tid; q < p.T * p.k; q += kGemvThreads) {
             if (p.ids_out) p.ids_out[q] = R.id[q];
@@ -679,7 +617,7 @@ __global__ void __launch_bounds__(kGemvThreads, NT == 1 ? 3 : 2) decode_layer_ke
 GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     GemvShape g{};
     const int qk = codes_per_block(qtype);
-    const int NT = T == 1 ? 1 : kGroup;
+    const int NT = 1;   // one token (T == 1)
     g.H = H;
     g.FF = FF;
     g.FFs = FFs;
@@ -738,22 +676,17 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     return g;
 }
 
-template <int QT, int NT, int NTERM>
+template <int QT, int NTERM>
 static hipError_t launch_decode_t(const GemvShape& g, DecodeParams& p, hipStream_t s) {
-    static bool attr_set = false;   // allow the dynamic LDS the largest windows need
+    static bool attr_set = false;   // allow the dynamic LDS the largest shapes need
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)decode_layer_kernel<QT, NT, NTERM>,
+        hipError_t e = hipFuncSetAttribute((const void*)decode_layer_kernel<QT, NTERM>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((decode_layer_kernel<QT, NT, NTERM>), dim3(g.grid), dim3(kGemvThreads), g.lds_bytes, s, p);
+    hipLaunchKernelGGL((decode_layer_kernel<QT, NTERM>), dim3(g.grid), dim3(kGemvThreads), g.lds_bytes, s, p);
     return hipGetLastError();
-}
-
-template <int QT, int NT>
-static hipError_t launch_decode(const GemvShape& g, DecodeParams& p, int x_dtype, hipStream_t s) {
-    return x_dtype == 1 ? launch_decode_t<QT, NT, 1>(g, p, s) : launch_decode_t<QT, NT, 2>(g, p, s);
 }
 
 hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, const void* single, const void* shared,
@@ -794,10 +727,11 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
     p.x_off = g.x_off;
     stage_mark(marks, s);
     hipError_t e;
-    if (T == 1)
-        e = g.qtype == 1 ? launch_decode<1, 1>(g, p, x_dtype, s) : launch_decode<2, 1>(g, p, x_dtype, s);
+    const bool bf = x_dtype == 1;
+    if (g.qtype == 1)
+        e = bf ? launch_decode_t<1, 1>(g, p, s) : launch_decode_t<1, 2>(g, p, s);
     else
-        e = g.qtype == 1 ? launch_decode<1, kGroup>(g, p, x_dtype, s) : launch_decode<2, kGroup>(g, p, x_dtype, s);
+        e = bf ? launch_decode_t<2, 1>(g, p, s) : launch_decode_t<2, 2>(g, p, s);
     stage_mark(marks, s);
     return e;
 }

@@ -11,7 +11,6 @@ namespace moe {
 constexpr int kMaxE = 1024;        // logits per token held by one wave (16 per lane)
 constexpr int kMaxK = 32;          // selected experts per token
 constexpr int kSmallT = 8;         // decode / verify window limit of the GEMV path
-constexpr int kGroup = 2;          // tokens of one expert processed together on the GEMV path
 constexpr int kGemvThreads = 256;  // workgroup size of the GEMV kernels
 constexpr int kMaxBlocksPerRow = 256;
 

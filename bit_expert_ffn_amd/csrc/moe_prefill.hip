@@ -52,7 +52,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kRowsPerTile = 128;          // (token, slot) rows per tile
-constexpr int kPrefillThreads = 256;       // 4 waves
 constexpr int kGuThreads = 512;            // gate/up workgroup: 8 waves
 constexpr int kGuFeatures = 256;           // features per gate/up workgroup (32 per wave)
 constexpr int kDnThreads = 512;            // down workgroup: 8 waves
