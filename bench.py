@@ -465,7 +465,8 @@ def main():
         "bytes_per_step": int(bytes_steps / K), "distinct_experts_per_layer": round(uniq_tot / (K * w.layers), 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "decode_layer_kernel (one launch per layer)", "launch_us": round(layer_ms * 1e3, 3),
+                     "kernel": ("decode_layer_kernel" if w.tokens == 1 else "window_layer_kernel") + " (one launch per layer)",
+                     "launch_us": round(layer_ms * 1e3, 3),
                      "bytes_per_launch": int(bytes_layer), "eager_launch_us": round(eager_layer_ms * 1e3, 3)},
         "wall_s": round(t_wall, 4),
     }

@@ -23,7 +23,7 @@
 // items cover a chunk in several sub-ranges of rows.
 //
 // Workgroup w takes the gate/up items w, w + G, ... and then the down items
-// w, w + G, ... (G = the grid).  G is at most the number of workgroups the GPU
+// G - 1 - w, 2G - 1 - w, ... (G = the grid).  G is at most the number of workgroups the GPU
 // holds at once (two per CU where registers and LDS allow), so that every
 // workgroup is resident: a down item waits for gate/up items of other
 // workgroups, which never wait, so every wait ends.  (If other work holds
@@ -715,7 +715,7 @@ __device__ __forceinline__ void dn_settle(const WindowParams& p, WinLDS& R, cons
     __syncthreads();   // the flags are written again by the next settle
 }
 
-// Items blockIdx.x, + n_wg, ...: the next item's codes are
+// Items n_wg - 1 - blockIdx.x, + n_wg, ...: the next item's codes are
 // loaded once the current one's `a` rows are in LDS (the staging waits for
 // every load of the workgroup), before its compute.
 template <int QT>
@@ -725,7 +725,10 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
     const int n_sg = p.FFs ? (p.T + kWinGroup - 1) / kWinGroup : 0;
     const int n_items = n_routed + n_sg * p.n_chunks * p.sh_items;
     const int need_chunk = R.n_groups + n_sg * p.sh_items;
-    int item = blockIdx.x;
+    // Down items go to the workgroups in reverse order: those with the most
+    // gate/up items (the low indices) get the fewest down items.
+    const int first_item = p.n_wg - 1 - (int)blockIdx.x;
+    int item = first_item;
     if (item >= n_items) return;
     DnItem ia = dn_item<QK>(p, R, item, n_routed), ib;
     DnLane la = dn_lane(ia.K, QK), lb;
@@ -737,7 +740,7 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
     while (true) {
         int next = item + p.n_wg;
         dn_begin<QK>(p, ia, lds);
-        if (item != (int)blockIdx.x) dn_settle(p, R, ib, oc_b, od_b, need_chunk);
+        if (item != first_item) dn_settle(p, R, ib, oc_b, od_b, need_chunk);
         ib = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         lb = dn_lane(ib.K, QK);
         dn_load(p, ib, lb, cb);
