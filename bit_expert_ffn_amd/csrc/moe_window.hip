@@ -323,8 +323,7 @@ __device__ __forceinline__ void gu_compute(const WindowParams& p, const WinLDS& 
 // the current one is computed (two buffers in turn), so that its loads
 // overlap the compute.  With no next item, the current one's are read again.
 template <int QT, int NTERM>
-// x_done: activation slices already arranged in LDS.
-__device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLDS& R, float* lds, int x_done) {
+__device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLDS& R, float* lds) {
     constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
     const int tid = threadIdx.x;
     const int n_routed = R.n_groups * p.tiles_gu;
@@ -343,7 +342,7 @@ __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLD
         // Every token's activation slice of every block column, once per
         // workgroup, while the first item's weights are on their way.
         uint32_t* xsl = reinterpret_cast<uint32_t*>(lds) + p.x_off;
-        for (int s = x_done + tid; s < p.T * nblk; s += kGemvThreads) {
+        for (int s = tid; s < p.T * nblk; s += kGemvThreads) {
             const int t = s / nblk, bb = s - t * nblk;
             XSlice<QT, NTERM> x1;
             if constexpr (NTERM == 1)
@@ -769,50 +768,14 @@ template <int QT, int NTERM>
 __global__ void __launch_bounds__(kGemvThreads, 2) window_layer_kernel(WindowParams p) {
     extern __shared__ __align__(16) float lds[];
     __shared__ WinLDS R;
-    constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
-    const int tid = threadIdx.x;
-    const int nblk = p.H / QK, n_x = p.T * nblk;
-    // bf16 activations: the words of the first two slices of each thread are
-    // loaded before the routing, so that they arrive while it runs; the slices
-    // are arranged once it is done.
-    const bool pre = NTERM == 1 && p.x_off >= 0;
-    uint32_t xr[2][QK / 2];
-    if (pre) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int sx = min(tid + kGemvThreads * i, n_x - 1);
-            const int t = sx / nblk, bb = sx - t * nblk;
-            const uint4* src = reinterpret_cast<const uint4*>((const uint16_t*)p.x + (size_t)t * p.H + bb * QK);
-#pragma unroll
-            for (int v = 0; v < QK / 8; ++v) {
-                const uint4 u = ldg_u4(src + v);
-                xr[i][4 * v + 0] = u.x;
-                xr[i][4 * v + 1] = u.y;
-                xr[i][4 * v + 2] = u.z;
-                xr[i][4 * v + 3] = u.w;
-            }
-        }
-    }
     route_window(p, R, reinterpret_cast<uint64_t*>(lds));
-    if (pre) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int sx = tid + kGemvThreads * i;
-            if (sx < n_x) {
-                XSlice<QT, 1> x1;
-                arrange_pairs<QT>(xr[i], x1.pr[0]);
-                finish_slice<QT, 1>(x1, p.z);
-                slice_to_lds<QT, 1>(x1, reinterpret_cast<uint32_t*>(lds) + p.x_off + sx * SW);
-            }
-        }
-    }
     if (blockIdx.x == 0) {
         for (int q = threadIdx.x; q < p.T * p.k; q += kGemvThreads) {
             if (p.ids_out) p.ids_out[q] = R.id[q];
             if (p.w_out) p.w_out[q] = R.w[q];
         }
     }
-    gateup_window<QT, NTERM>(p, R, lds, pre ? 2 * kGemvThreads : 0);
+    gateup_window<QT, NTERM>(p, R, lds);
     down_window<QT>(p, R, lds);
 }
 
