@@ -335,14 +335,47 @@ __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLD
     const int Rr = P * kWinMaxPass;
     int item = blockIdx.x;
     if (item >= n_items) return;
+    // Every token's activation slice of every block column, once per
+    // workgroup, while the first item's weights are on their way: the words of
+    // a thread's first two slices (bf16) are loaded before the weights, so
+    // that arranging them waits for them alone.
+    const bool pre = NTERM == 1 && p.x_off >= 0;
+    const int n_x = p.T * nblk;
+    uint32_t xr[2][QK / 2];
+    if (pre) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int sx = min(tid + kGemvThreads * i, n_x - 1);
+            const int t = sx / nblk, bb = sx - t * nblk;
+            const uint4* src = reinterpret_cast<const uint4*>((const uint16_t*)p.x + (size_t)t * p.H + bb * QK);
+#pragma unroll
+            for (int v = 0; v < QK / 8; ++v) {
+                const uint4 u = ldg_u4(src + v);
+                xr[i][4 * v + 0] = u.x;
+                xr[i][4 * v + 1] = u.y;
+                xr[i][4 * v + 2] = u.z;
+                xr[i][4 * v + 3] = u.w;
+            }
+        }
+    }
     GuItem ia = gu_item(p, R, item, n_routed, Rr), ib;
     GuCodes ca, cb;
     gu_load(ia, nblk, P, rp, b, ca);
     if (p.x_off >= 0) {
-        // Every token's activation slice of every block column, once per
-        // workgroup, while the first item's weights are on their way.
         uint32_t* xsl = reinterpret_cast<uint32_t*>(lds) + p.x_off;
-        for (int s = tid; s < p.T * nblk; s += kGemvThreads) {
+        if (pre) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int sx = tid + kGemvThreads * i;
+                if (sx < n_x) {
+                    XSlice<QT, NTERM> x1;
+                    arrange_pairs<QT>(xr[i], x1.pr[0]);
+                    finish_slice<QT, NTERM>(x1, p.z);
+                    slice_to_lds<QT, NTERM>(x1, xsl + sx * SW);
+                }
+            }
+        }
+        for (int s = tid + (pre ? 2 * kGemvThreads : 0); s < n_x; s += kGemvThreads) {
             const int t = s / nblk, bb = s - t * nblk;
             XSlice<QT, NTERM> x1;
             if constexpr (NTERM == 1)
