@@ -184,6 +184,7 @@ struct GuItem {
     uint32_t* out;
     int g, first, n_e, rows, f0;
     bool sh;
+    bool none;   // no item: its loads read one chunk (the buffers' turn needs loads, not these bytes)
 };
 
 __device__ __forceinline__ GuItem gu_item(const WindowParams& p, const WinLDS& R, int item, int n_routed, int Rr) {
@@ -210,6 +211,7 @@ __device__ __forceinline__ GuItem gu_item(const WindowParams& p, const WinLDS& R
         it.out = p.as;
     }
     it.f0 = tile * Rr;
+    it.none = false;
     return it;
 }
 
@@ -230,7 +232,7 @@ __device__ __forceinline__ void gu_load(const GuItem& it, int nblk, int P, int r
 #pragma unroll
     for (int m = 0; m < kWinMaxPass; ++m) {
         const int f = min(it.f0 + m * P + rp, it.rows - 1);
-        const size_t blk = (size_t)f * nblk + b;
+        const size_t blk = it.none ? 0 : (size_t)f * nblk + b;
         c.cg[m] = ldg_u4(gcode + blk * 16);
         c.cu[m] = ldg_u4(ucode + blk * 16);
         c.sg[m] = ldg_u16(gscale + blk * 2);
@@ -321,7 +323,7 @@ __device__ __forceinline__ void gu_compute(const WindowParams& p, const WinLDS& 
 
 // Items blockIdx.x, + n_wg, ...: the next item's codes are loaded before
 // the current one is computed (two buffers in turn), so that its loads
-// overlap the compute.  With no next item, the current one's are read again.
+// overlap the compute.  With no next item, one chunk is read.
 template <int QT, int NTERM>
 __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLDS& R, float* lds) {
     constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
@@ -389,12 +391,14 @@ __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLD
     while (true) {
         int next = item + p.n_wg;
         ib = gu_item(p, R, next < n_items ? next : item, n_routed, Rr);
+        ib.none = next >= n_items;
         gu_load(ib, nblk, P, rp, b, cb);
         gu_compute<QT, NTERM>(p, R, ia, ca, lds, nblk, P, rp, b, active);
         if (next >= n_items) break;
         item = next;
         next = item + p.n_wg;
         ia = gu_item(p, R, next < n_items ? next : item, n_routed, Rr);
+        ia.none = next >= n_items;
         gu_load(ia, nblk, P, rp, b, ca);
         gu_compute<QT, NTERM>(p, R, ib, cb, lds, nblk, P, rp, b, active);
         if (next >= n_items) break;
@@ -528,6 +532,7 @@ struct DnItem {
     const uint32_t* a_src;
     int g, ch, h0, nrows, first, n_e, K, group_items;
     bool sh;
+    bool none;   // no item: its loads read one chunk
 };
 
 template <int QK>
@@ -567,6 +572,7 @@ __device__ __forceinline__ DnItem dn_item(const WindowParams& p, const WinLDS& R
     const int nb = it.K / QK;
     it.dcode = blob + (size_t)2 * it.K * (p.H / QK) * kBlockBytes;   // after gate and up
     it.dscale = it.dcode + (size_t)p.H * nb * 16;
+    it.none = false;
     return it;
 }
 
@@ -600,7 +606,7 @@ __device__ __forceinline__ void dn_load(const WindowParams& p, const DnItem& it,
 #pragma unroll
     for (int m = 0; m < kWinMaxPass; ++m) {
         const int r = min(l.rp + m * l.P, rlast);
-        const size_t blk = (size_t)(min(it.h0 + r, p.H - 1)) * l.nb + l.b;
+        const size_t blk = it.none ? 0 : (size_t)(min(it.h0 + r, p.H - 1)) * l.nb + l.b;
         c.c[m] = ldg_u4(it.dcode + blk * 16);
         c.sc[m] = ldg_u16(it.dscale + blk * 2);
     }
@@ -774,6 +780,7 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
         dn_begin<QK>(p, ia, lds);
         if (item != first_item) dn_settle(p, R, ib, oc_b, od_b, need_chunk);
         ib = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
+        ib.none = next >= n_items;
         lb = dn_lane(ib.K, QK);
         dn_load(p, ib, lb, cb);
         dn_finish<QT>(p, R, ia, la, ca, lds, oc_a, od_a);
@@ -786,6 +793,7 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
         dn_begin<QK>(p, ib, lds);
         dn_settle(p, R, ia, oc_a, od_a, need_chunk);
         ia = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
+        ia.none = next >= n_items;
         la = dn_lane(ia.K, QK);
         dn_load(p, ia, la, ca);
         dn_finish<QT>(p, R, ib, lb, cb, lds, oc_b, od_b);
