@@ -224,6 +224,29 @@ def test_layer_ragged_windows(T):
     _layer_parity(wl.WORKLOADS["verify_t8"], [1], [4], tokens=T)
 
 
+def test_window_most_pairs_and_shared_groups():
+    """The window kernel at its largest pair count (8 tokens x 32 slots = 256
+    pairs over 48 experts, so most experts are split into several groups of
+    two) and with a shared expert over an odd window (its last group holds
+    one token), against the oracle."""
+    rng = np.random.default_rng(21)
+    H, FF, FFs, E = 128, 64, 96, 48
+    blobs = [random_expert(rng, 2, H, FF, 0.02)[0] for _ in range(E)]
+    shared = random_expert(rng, 2, H, FFs, 0.02)[0]
+    dev = [torch.from_numpy(b).to(DEV) for b in blobs]
+    table = torch.tensor([t.data_ptr() for t in dev], dtype=torch.int64, device=DEV)
+    sh = torch.from_numpy(shared).to(DEV)
+    for T, k, use_shared in [(8, 32, False), (5, 6, True), (7, 32, True)]:
+        x = rng.normal(size=(T, H)).astype(np.float32)
+        logits = rng.normal(size=(T, E)).astype(np.float32)
+        desc = moe.layer_desc(H, FF, 2, 7.5, E, k, shared_ff=FFs if use_shared else 0)
+        y = moe.layer_forward(desc, table, torch.from_numpy(x).to(DEV), torch.from_numpy(logits).to(DEV),
+                              shared=sh if use_shared else None)
+        y_ref, _, _ = oracle.layer_forward(blobs, k, 2, 7.5, H, FF, x, logits,
+                                           shared=shared if use_shared else None, shared_ff=FFs if use_shared else 0)
+        assert max_err_over_rms(y.cpu().numpy(), y_ref) <= TOL, (T, k, use_shared)
+
+
 # --- invariants of the GEMV path ----------------------------------------------------------------
 
 def test_batch_invariance_and_determinism():
