@@ -6,36 +6,38 @@
 // window is read once).  Here the tokens that chose an expert form groups of
 // up to two, and each group's weights are read once for its tokens.  (A
 // group of every token of the expert would make the work items of hot
-// experts several times heavier than the rest; the re-read of an expert by
-// its second group is mostly served by the caches.)
+// experts several times heavier than the rest, which costs more time than
+// the re-reads of hot experts by their later groups.)
 //
-// Work items, in the order every workgroup derives them from the routing:
+// Work items, in the order every workgroup derives them from the routing
+// (groups of two tokens first):
 //   gate/up items  (group, tile of FF rows): the codes of every pass of the
 //                  tile are loaded once and held in registers while the
 //                  group's tokens go through them one at a time; the SwiGLU
 //                  output rows are published as never-zero packed words;
 //   down items     (group, chunk of H rows): the group's `a` rows are
-//                  arranged into dot-pair slices in LDS once, the down codes of the chunk are held in
-//                  registers, and the tokens go through them one at a time; the
-//                  result of each (slot, row) is published as a never-zero
-//                  fp32 word.
+//                  arranged into dot-pair slices in LDS once, the down codes
+//                  of the chunk are held in registers, and the tokens go
+//                  through them one at a time; the result of each (slot, row)
+//                  is published as a never-zero fp32 word.
 // The shared expert's groups hold the window's tokens two at a time; its down
 // items cover a chunk in several sub-ranges of rows.
 //
 // Workgroup w takes the gate/up items w, w + G, ... and then the down items
-// G - 1 - w, 2G - 1 - w, ... (G = the grid).  G is at most the number of workgroups the GPU
-// holds at once (two per CU where registers and LDS allow), so that every
-// workgroup is resident: a down item waits for gate/up items of other
-// workgroups, which never wait, so every wait ends.  (If other work holds
-// part of the GPU, the waits last until it leaves room.)  Each gate/up tile
-// bumps its group's counter, and the down items of a group start once its
-// counter is complete (no wait for other groups).  Each down item then bumps
-// its chunk's counter; the item that completes a chunk combines it (its
-// workgroup looks at the count once the next item's `a` is in LDS, so the
-// count's round trip overlaps other work): y[t][h] = shared + sum_j w[t][j] d,
-// the slots summed in rank order, so the output does not depend on timing.
-// Readers of `a` and d read again any word still 0, so no count waits for the
-// stores before it.
+// G - 1 - w, 2G - 1 - w, ... (G = the grid; reversed, so that the workgroups
+// with the most gate/up items get the fewest down items).  G is at most the
+// number of workgroups the GPU holds at once (two per CU where registers and
+// LDS allow), so that every workgroup is resident: a down item waits for
+// gate/up items of other workgroups, which never wait, so every wait ends.
+// (If other work holds part of the GPU, the waits last until it leaves room.)
+// Each gate/up tile bumps its group's counter, and the down items of a group
+// start once its counter is complete (no wait for other groups).  Each down
+// item then bumps its chunk's counter; the item that completes a chunk
+// combines it (its workgroup looks at the count once the next item's `a` is in
+// LDS, so the count's round trip overlaps other work): y[t][h] = shared +
+// sum_j w[t][j] d, the slots summed in rank order, so the output does not
+// depend on timing.  Readers of `a` and d read again any word still 0, so no
+// count waits for the stores before it.
 //
 // Every piece of shared state is returned to zero by its last user: the last
 // down item of a group clears the group's counters and `a` rows; the
@@ -50,8 +52,7 @@ constexpr long kWinSpin = 1l << 22;
 constexpr int kWinMaxPass = 8;               // passes per item (rows = P * passes)
 // Tokens of one expert per group: a hot expert's tokens are split over
 // several groups, so that no work item holds many more tokens than others
-// (its weights are read once per group; the re-reads of one call are mostly
-// served by the caches).
+// (its weights are read once per group).
 constexpr int kWinGroup = 2;
 constexpr int kWinShared = (kSmallT + kWinGroup - 1) / kWinGroup;   // groups of the shared expert, at most
 
