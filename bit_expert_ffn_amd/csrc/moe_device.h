@@ -206,13 +206,15 @@ __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k
     // compiler from moving them across each other.
     __builtin_amdgcn_wave_barrier();
     const uint64_t mine = lane < n ? scratch[lane] : 0ull;
-    // Lanes n.. hold key 0, which is larger than no key: the count may run on
-    // to a multiple of 8.
+    // Every lane reads the candidates from LDS, 8 at a time (the same address
+    // for all lanes: broadcast reads); positions n.. hold no candidate.
     int rank = 0;
-    const int n8 = (n + 7) & ~7;
-    for (int j = 0; j < n8; j += 8) {
+    for (int j = 0; j < n; j += 8) {
+        uint64_t c[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) rank += readlane_u64(mine, j + u) > mine;
+        for (int u = 0; u < 8; ++u) c[u] = scratch[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += (j + u < n) && c[u] > mine;
     }
     __builtin_amdgcn_wave_barrier();
     scratch[lane < n && rank < k ? rank : 64 + lane] = mine;
