@@ -32,17 +32,17 @@
 // (If other work holds part of the GPU, the waits last until it leaves room.)
 // Each gate/up tile bumps its group's counter, and the down items of a group
 // start once its counter is complete (no wait for other groups).  Each down
-// item then bumps its chunk's counter; the item that completes a chunk
-// combines it (its workgroup looks at the count once the next item's `a` is in
-// LDS, so the count's round trip overlaps other work): y[t][h] = shared +
+// item then bumps its chunk's counter once its d words are visible.  When a
+// chunk's count is complete, up to eight workgroups that are done with their
+// own items combine it, each a part of its rows: y[t][h] = shared +
 // sum_j w[t][j] d, the slots summed in rank order, so the output does not
-// depend on timing.  Readers of `a` and d read again any word still 0, so no
-// count waits for the stores before it.
+// depend on timing.  Readers of `a` and d read again any word still 0, so a
+// count that runs ahead of the words costs a reload, not a wrong value.
 //
 // Every piece of shared state is returned to zero by its last user: the last
-// down item of a group clears the group's counters and `a` rows; the
-// combining item clears its chunk's counter and the d words it read.  The
-// bounded waits flag an error if a bound is ever reached.
+// down item of a group clears the group's counters and `a` rows; each
+// combining part clears the d words it read, and the last part of a chunk its
+// counters.  The bounded waits flag an error if a bound is ever reached.
 #include "moe_gemv_common.h"
 
 namespace moe {
@@ -55,6 +55,7 @@ constexpr int kWinMaxPass = 8;               // passes per item (rows = P * pass
 // (its weights are read once per group).
 constexpr int kWinGroup = 2;
 constexpr int kWinShared = (kSmallT + kWinGroup - 1) / kWinGroup;   // groups of the shared expert, at most
+constexpr int kWinCombineParts = 8;          // workgroups that combine one chunk, at most
 
 struct WindowParams {
     const void* const* table;
@@ -82,12 +83,15 @@ struct WindowParams {
 
 // Sync lines (16 ints each): line 1 the error flag; per group g (routed
 // groups g < 8k, the shared expert's groups from 8k on) its gate/up tile
-// count (complete at tiles_gu) and its down item count; then one counter per
-// chunk.
+// count (complete at tiles_gu) and its down item count; then per chunk its
+// down item count, then per chunk the count of its combined parts.
 __device__ __forceinline__ int* win_error(int* s) { return s + 16; }
 __device__ __forceinline__ int* win_gu_count(int* s, int g) { return s + 16 * (2 + 2 * g); }
 __device__ __forceinline__ int* win_dn_count(int* s, int g) { return s + 16 * (3 + 2 * g); }
 __device__ __forceinline__ int* win_chunk(int* s, int k, int c) { return s + 16 * (2 + 2 * (kSmallT * k + kWinShared) + c); }
+__device__ __forceinline__ int* win_combined(int* s, int k, int n_chunks, int c) {
+    return s + 16 * (2 + 2 * (kSmallT * k + kWinShared) + n_chunks + c);
+}
 
 __device__ __forceinline__ void win_flag_error(const WindowParams& p) {
     __hip_atomic_store(win_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -101,7 +105,7 @@ struct WinLDS {
     int group_first[kWinPairs + 1]; // first sorted position of each group; [n_groups] = T * k
     int gorder[kWinPairs];          // groups in work order: full groups (kWinGroup tokens) first
     int n_groups;
-    int flag_combine, flag_reset;
+    int flag_reset;
 };
 
 // Routing of the T tokens (wave w takes tokens w and w + 4), then the groups:
@@ -491,19 +495,20 @@ __device__ __forceinline__ void slot_sums16(const WindowParams& p, const WinLDS&
     }
 }
 
-// y rows [c0, c1) of every token: shared + sum_j w[t][j] d[t * k + j], the
-// slot terms added as the one-token kernel adds them (lane j of a group of 16
-// or 32 lanes holds slot j's term, 0 past k, and a DPP tree sums the group:
-// pairwise in slot order), so a token's output is the same alone and inside a
-// window; the shared term is added last.  Each thread takes 4 consecutive
-// rows of one token.  The d words read are cleared for the next call.
-__device__ __forceinline__ void combine_chunk(const WindowParams& p, const WinLDS& R, int c0, int c1) {
-    const int nr4 = (c1 - c0) / 4, k = p.k;
-    const int nq = p.T * nr4;
+// y rows [h0, h0 + 4 n4) of every token: shared + sum_j w[t][j] d[t * k + j],
+// the slot terms added as the one-token kernel adds them (lane j of a group
+// of 16 or 32 lanes holds slot j's term, 0 past k, and a DPP tree sums the
+// group: pairwise in slot order), so a token's output is the same alone and
+// inside a window; the shared term is added last.  Each thread takes 4
+// consecutive rows of one token.  The d words read are cleared for the next
+// call.
+__device__ __forceinline__ void combine_rows(const WindowParams& p, const WinLDS& R, int h0, int n4) {
+    const int k = p.k;
+    const int nq = p.T * n4;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.d, 0, (kSmallT * k + kSmallT) * p.H * 4, kRsrcWord3);
     for (int qd = threadIdx.x; qd < nq; qd += kGemvThreads) {
-        const int t = qd / nr4, h = c0 + 4 * (qd - t * nr4);
+        const int t = qd / n4, h = h0 + 4 * (qd - t * n4);
         float acc[4];
         slot_sums16(p, R, rsrc, t, h, 0, acc);
         if (k > 16) {
@@ -659,7 +664,7 @@ __device__ __forceinline__ void dn_begin(const WindowParams& p, const DnItem& it
 // last of either.
 template <int QT>
 __device__ __forceinline__ void dn_finish(const WindowParams& p, const WinLDS& R, const DnItem& it, const DnLane& l,
-                                          DnCodes& c, float* lds, int& old_chunk, int& old_dn) {
+                                          DnCodes& c, float* lds, int& old_dn) {
     constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, 2>::N;
     const int tid = threadIdx.x;
     float* part = lds + p.stage_words;
@@ -715,32 +720,29 @@ __device__ __forceinline__ void dn_finish(const WindowParams& p, const WinLDS& R
             __hip_atomic_store(p.d + (size_t)drow * p.H + it.h0 + r, nonzero_bits(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
-        lds_barrier();   // the partials are reused by the next pair
+        // The partials are reused by the next pair.  After the last pair the
+        // barrier also waits for every d store of the workgroup, so the item
+        // is counted only once its words are visible: the combine that the
+        // count may start then finds them on its first read.
+        if (t0 + 2 < it.n_e) lds_barrier();
+        else __syncthreads();
     }
-    // Count the item in its chunk (and, without staged rows, in its group);
-    // the counts are looked at in dn_settle.
+    // Count the item in its chunk (its d words are visible: the barrier above
+    // waited for them) and, without staged rows, in its group; the group
+    // count is looked at in dn_settle.
     if (tid == 0) {
         if (!p.stage_words)
             old_dn = __hip_atomic_fetch_add(win_dn_count(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        old_chunk = __hip_atomic_fetch_add(win_chunk(p.sync, p.k, it.ch), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        atomic_add_detached(win_chunk(p.sync, p.k, it.ch), 1);
     }
 }
 
-// After an item's counts have returned (thread 0 holds them): combine its
-// chunk if the item completed it; clear its group's state if the item was the
-// group's last to take its `a` rows.
-__device__ __forceinline__ void dn_settle(const WindowParams& p, WinLDS& R, const DnItem& it, int old_chunk, int old_dn,
-                                          int need_chunk) {
+// After an item's group count has returned (thread 0 holds it): clear the
+// group's state if the item was the group's last to take its `a` rows.
+__device__ __forceinline__ void dn_settle(const WindowParams& p, WinLDS& R, const DnItem& it, int old_dn) {
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        R.flag_combine = old_chunk == need_chunk - 1;
-        R.flag_reset = old_dn == it.group_items - 1;
-    }
+    if (tid == 0) R.flag_reset = old_dn == it.group_items - 1;
     __syncthreads();
-    if (R.flag_combine) {
-        if (tid == 0) __hip_atomic_store(win_chunk(p.sync, p.k, it.ch), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        combine_chunk(p, R, it.ch * p.chunk_rows, min((it.ch + 1) * p.chunk_rows, p.H));
-    }
     if (R.flag_reset) {
         // Every item of the group holds its `a` rows: clear them, and the
         // group's counters.
@@ -763,7 +765,6 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
     const int n_routed = R.n_groups * p.n_chunks;
     const int n_sg = p.FFs ? (p.T + kWinGroup - 1) / kWinGroup : 0;
     const int n_items = n_routed + n_sg * p.n_chunks * p.sh_items;
-    const int need_chunk = R.n_groups + n_sg * p.sh_items;
     // Down items go to the workgroups in reverse order: those with the most
     // gate/up items (the low indices) get the fewest down items.
     const int first_item = p.n_wg - 1 - (int)blockIdx.x;
@@ -775,34 +776,79 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
     dn_load(p, ia, la, ca);
     // Counts of the previous item (thread 0), settled after the next item's
     // `a` rows are in LDS.
-    int oc_a = 0, od_a = 0, oc_b = 0, od_b = 0;
+    int od_a = 0, od_b = 0;
     while (true) {
         int next = item + p.n_wg;
         dn_begin<QK>(p, ia, lds);
-        if (item != first_item) dn_settle(p, R, ib, oc_b, od_b, need_chunk);
+        if (item != first_item) dn_settle(p, R, ib, od_b);
         ib = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         ib.none = next >= n_items;
         lb = dn_lane(ib.K, QK);
         dn_load(p, ib, lb, cb);
-        dn_finish<QT>(p, R, ia, la, ca, lds, oc_a, od_a);
+        dn_finish<QT>(p, R, ia, la, ca, lds, od_a);
         if (next >= n_items) {
-            dn_settle(p, R, ia, oc_a, od_a, need_chunk);
+            dn_settle(p, R, ia, od_a);
             break;
         }
         item = next;
         next = item + p.n_wg;
         dn_begin<QK>(p, ib, lds);
-        dn_settle(p, R, ia, oc_a, od_a, need_chunk);
+        dn_settle(p, R, ia, od_a);
         ia = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         ia.none = next >= n_items;
         la = dn_lane(ia.K, QK);
         dn_load(p, ia, la, ca);
-        dn_finish<QT>(p, R, ib, lb, cb, lds, oc_b, od_b);
+        dn_finish<QT>(p, R, ib, lb, cb, lds, od_b);
         if (next >= n_items) {
-            dn_settle(p, R, ib, oc_b, od_b, need_chunk);
+            dn_settle(p, R, ib, od_b);
             break;
         }
         item = next;
+    }
+}
+
+// The combine, once a chunk's down items are all counted, split into parts of
+// its rows over several workgroups (each workgroup's loads in flight are
+// bounded, so one workgroup per chunk would take several round trips): part
+// slots s = w, w + G, ... of n_chunks * hp (hp parts per chunk).  A
+// workgroup's own down items are done before it waits, and the items it waits
+// for never wait for it.  The last part of a chunk to see it complete clears
+// the chunk's counters.
+__device__ __forceinline__ void combine_window(const WindowParams& p, const WinLDS& R) {
+    const int n_sg = p.FFs ? (p.T + kWinGroup - 1) / kWinGroup : 0;
+    const int need_chunk = R.n_groups + n_sg * p.sh_items;
+    const int hp = max(1, min(kWinCombineParts, p.n_wg / p.n_chunks));
+    for (int sl = blockIdx.x; sl < p.n_chunks * hp; sl += p.n_wg) {
+        const int c = sl / hp, part = sl - c * hp;
+        const int c0 = c * p.chunk_rows, nr4 = (min(c0 + p.chunk_rows, p.H) - c0) / 4;
+        const int q0 = part * nr4 / hp, q1 = (part + 1) * nr4 / hp;
+        if (threadIdx.x == 0) {
+            long spins = 0;
+            while (__hip_atomic_load(win_chunk(p.sync, p.k, c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                   need_chunk) {
+                if (++spins > kWinSpin) {
+                    win_flag_error(p);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        // Count this part as one that has seen the chunk complete (no part
+        // looks at the chunk's counter after that); the count returns while
+        // the rows are combined.
+        int old = 0;
+        if (threadIdx.x == 0)
+            old = __hip_atomic_fetch_add(win_combined(p.sync, p.k, p.n_chunks, c), 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        combine_rows(p, R, c0 + 4 * q0, q1 - q0);
+        if (threadIdx.x == 0) {
+            if (old == hp - 1) {
+                __hip_atomic_store(win_chunk(p.sync, p.k, c), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(win_combined(p.sync, p.k, p.n_chunks, c), 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
 }
 
@@ -819,6 +865,7 @@ __global__ void __launch_bounds__(kGemvThreads, 2) window_layer_kernel(WindowPar
     }
     gateup_window<QT, NTERM>(p, R, lds);
     down_window<QT>(p, R, lds);
+    combine_window(p, R);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -882,7 +929,9 @@ WindowShape window_shape(int H, int FF, int FFs, int qtype, int x_dtype, int T, 
     return g;
 }
 
-size_t window_sync_bytes(int k, int n_chunks) { return (size_t)64 * (2 + 2 * (kSmallT * k + kWinShared) + n_chunks); }
+size_t window_sync_bytes(int k, int n_chunks) {
+    return (size_t)64 * (2 + 2 * (kSmallT * k + kWinShared) + 2 * n_chunks);
+}
 
 template <int QT, int NTERM>
 static hipError_t launch_window_t(const WindowShape& g, const WindowParams& p, hipStream_t s) {

@@ -335,7 +335,7 @@ def _decode_fixed_bytes(k, hidden, ff, shared_ff, qk, small_t=8):
     between calls, each region 256-byte aligned: the sync words (the larger of
     the one-token kernel's 64-byte lines plus 16 replicas of its ready flags,
     and the window kernel's lines: 2, then 2 per group of small_t * k + 4,
-    then one per chunk of 8 passes of down rows), then the `a` words of
+    then 2 per chunk of 8 passes of down rows), then the `a` words of
     small_t * k pairs and of small_t shared-expert rows, then the window
     kernel's d words for small_t * k + small_t rows of hidden."""
     al = lambda v: (v + 255) // 256 * 256
@@ -343,7 +343,7 @@ def _decode_fixed_bytes(k, hidden, ff, shared_ff, qk, small_t=8):
     sync1 = (lines + 4095) // 4096 * 4096 + 16 * 4096
     chunk_rows = (256 // (ff // qk)) * 8
     n_chunks = (hidden + chunk_rows - 1) // chunk_rows
-    syncw = 64 * (2 + 2 * (small_t * k + 4) + n_chunks)
+    syncw = 64 * (2 + 2 * (small_t * k + 4) + 2 * n_chunks)
     off = al(max(sync1, syncw))
     off = al(off + small_t * k * ff * 4)
     off = al(off + small_t * shared_ff * 4)
