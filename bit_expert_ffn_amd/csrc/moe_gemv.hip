@@ -626,12 +626,14 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     const int nblk_gu = H / qk;
     const int P = kGemvThreads / nblk_gu;
     g.max_groups = T * k;
-    // Enough passes per gate/up workgroup that about 384 of them cover the
-    // routed experts' FF rows (more loads in flight per thread, and every
-    // workgroup of the layer resident at once).
+    // Enough passes per gate/up workgroup that at most about 256 of them (one
+    // per CU) cover the routed experts' FF rows: each gate/up wave then has a
+    // SIMD to itself, where a second workgroup on a CU would double the
+    // slowest tile's compute (Strata decode: 220 tiles of 5 passes run 0.8%
+    // faster than 360 of 3).
     {
         const long rows_all = (long)g.max_groups * FF;
-        int passes = (int)((rows_all + (long)P * 384 - 1) / ((long)P * 384));
+        int passes = (int)((rows_all + (long)P * 256 - 1) / ((long)P * 256));
         g.gu_passes = passes < 1 ? 1 : (passes > kMaxPass ? kMaxPass : passes);
     }
     g.tile_rows_gu = P * g.gu_passes;
