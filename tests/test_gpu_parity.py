@@ -247,6 +247,25 @@ def test_window_most_pairs_and_shared_groups():
         assert max_err_over_rms(y.cpu().numpy(), y_ref) <= TOL, (T, k, use_shared)
 
 
+def test_window_more_chunks_than_workgroups():
+    """A wide layer (H = 4608, FF = 8192, 4-bit) whose down rows fall into
+    more chunks (576 of 8 rows) than the window kernel has workgroups, so
+    that workgroups combine several chunks one after another, against the
+    oracle."""
+    rng = np.random.default_rng(33)
+    H, FF, E = 4608, 8192, 2
+    blobs = [random_expert(rng, 2, H, FF, 0.02)[0] for _ in range(E)]
+    dev = [torch.from_numpy(b).to(DEV) for b in blobs]
+    table = torch.tensor([t.data_ptr() for t in dev], dtype=torch.int64, device=DEV)
+    for T, k in [(2, 1), (3, 2)]:
+        x = rng.normal(size=(T, H)).astype(np.float32)
+        logits = rng.normal(size=(T, E)).astype(np.float32)
+        desc = moe.layer_desc(H, FF, 2, 7.5, E, k)
+        y = moe.layer_forward(desc, table, torch.from_numpy(x).to(DEV), torch.from_numpy(logits).to(DEV))
+        y_ref, _, _ = oracle.layer_forward(blobs, k, 2, 7.5, H, FF, x, logits)
+        assert max_err_over_rms(y.cpu().numpy(), y_ref) <= TOL, (T, k)
+
+
 # --- invariants of the GEMV path ----------------------------------------------------------------
 
 def test_batch_invariance_and_determinism():
