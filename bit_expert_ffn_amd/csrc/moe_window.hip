@@ -56,6 +56,7 @@ constexpr int kWinMaxPass = 8;               // passes per item (rows = P * pass
 constexpr int kWinGroup = 2;
 constexpr int kWinShared = (kSmallT + kWinGroup - 1) / kWinGroup;   // groups of the shared expert, at most
 constexpr int kWinCombineParts = 8;          // workgroups that combine one chunk, at most
+constexpr int kWinItemCost = 4;              // a gate/up item's fixed work, in passes (an estimate)
 
 struct WindowParams {
     const void* const* table;
@@ -73,7 +74,6 @@ struct WindowParams {
     uint32_t* d;                // [8k + 8][H] fp32 bits: slot t*k + j, then 8k + t for the shared expert
     float* y;                   // [T][H]
     int* sync;                  // window sync lines, see win_* below
-    int gu_passes, tiles_gu, tiles_gu_s;
     int dn_passes, chunk_rows, n_chunks;
     int sh_passes, sh_rows, sh_items;
     int n_wg;                   // the grid
@@ -105,14 +105,41 @@ struct WinLDS {
     int group_first[kWinPairs + 1]; // first sorted position of each group; [n_groups] = T * k
     int gorder[kWinPairs];          // groups in work order: full groups (kWinGroup tokens) first
     int n_groups;
+    int gu_passes, tiles_gu, tiles_gu_s;   // this call's gate/up tiling (gu_tiling)
     int flag_reset;
 };
+
+// Gate/up passes per tile for this call's groups: the count p of passes
+// (at most kWinMaxPass) that makes the busiest workgroup's share, rounds of
+// items times (p + kWinItemCost), the smallest (the larger p on a tie: fewer
+// items).  kWinItemCost prices an item's fixed work (its row sums, SwiGLU,
+// stores and count) in passes; without it the smallest tiles would win.
+// With 63 groups of the Strata shape on 512 workgroups, 7 passes give 1,008
+// items in 2 rounds (22) where 8 give 882 items, also in 2 rounds (24); with
+// 65 groups 8 passes stay (2 rounds against 3).  Every workgroup derives the
+// same tiling from the same routing.  One wave: lane i < kWinMaxPass prices
+// kWinMaxPass - i passes.
+__device__ __forceinline__ void gu_tiling(const WindowParams& p, WinLDS& R, int n_groups, int P, int lane) {
+    const int n_sg = p.FFs ? (p.T + kWinGroup - 1) / kWinGroup : 0;
+    const int gp = kWinMaxPass - min(lane, kWinMaxPass - 1);
+    const int rows = P * gp;
+    const int t = (p.FF + rows - 1) / rows, ts = p.FFs ? (p.FFs + rows - 1) / rows : 0;
+    const int items = n_groups * t + n_sg * ts;
+    const uint32_t cost = (uint32_t)min((items + p.n_wg - 1) / p.n_wg * (gp + kWinItemCost), 1 << 25);
+    // (cost, lane): the lowest cost, then the most passes
+    const uint32_t best = wave_min_u32(lane < kWinMaxPass ? cost * 64u + (uint32_t)lane : 0xFFFFFFFFu);
+    if (lane == (int)(best & 63u)) {
+        R.gu_passes = gp;
+        R.tiles_gu = t;
+        R.tiles_gu_s = ts;
+    }
+}
 
 // Routing of the T tokens (wave w takes tokens w and w + 4), then the groups:
 // pairs sorted by (expert, token), each run of one expert cut into groups of
 // at most kWinGroup pairs.
 // `scratch` is the dynamic LDS, free until the roles start (128 keys per wave).
-__device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, uint64_t* scratch) {
+__device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, uint64_t* scratch, int P_gu) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k, n = p.T * k;
     for (int t = wv; t < p.T; t += kGemvThreads / 64) {
@@ -179,6 +206,7 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
             fb += __popcll(mf);
             pb += __popcll(mp);
         }
+        gu_tiling(p, R, ng, P_gu, lane);
     }
     __syncthreads();
 }
@@ -197,18 +225,20 @@ __device__ __forceinline__ GuItem gu_item(const WindowParams& p, const WinLDS& R
     it.sh = item >= n_routed;
     int tile;
     if (!it.sh) {
-        const int gi = item / p.tiles_gu;
+        const int tg = __builtin_amdgcn_readfirstlane(R.tiles_gu);   // uniform: scalar arithmetic
+        const int gi = item / tg;
         it.g = R.gorder[gi];
-        tile = item - gi * p.tiles_gu;
+        tile = item - gi * tg;
         it.first = R.group_first[it.g];
         it.n_e = R.group_first[it.g + 1] - it.first;
         it.blob = p.table ? table_blob(p.table, R.id[R.sorted[it.first]]) : p.single;
         it.rows = p.FF;
         it.out = p.a;
     } else {   // shared group sg: tokens kWinGroup * sg ..
-        const int i2 = item - n_routed, sg = i2 / p.tiles_gu_s;
+        const int ts = __builtin_amdgcn_readfirstlane(R.tiles_gu_s);
+        const int i2 = item - n_routed, sg = i2 / ts;
         it.g = kSmallT * p.k + sg;
-        tile = i2 - sg * p.tiles_gu_s;
+        tile = i2 - sg * ts;
         it.first = kWinGroup * sg;
         it.n_e = min(kWinGroup, p.T - it.first);
         it.blob = p.shared;
@@ -228,7 +258,7 @@ struct GuCodes {
     uint16_t sg[kWinMaxPass], su[kWinMaxPass];
 };
 
-__device__ __forceinline__ void gu_load(const GuItem& it, int nblk, int P, int rp, int b, GuCodes& c) {
+__device__ __forceinline__ void gu_load(const GuItem& it, int nblk, int P, int gp, int rp, int b, GuCodes& c) {
     const size_t plane = (size_t)it.rows * nblk;
     const uint8_t* gcode = it.blob;
     const uint8_t* gscale = it.blob + plane * 16;
@@ -236,7 +266,7 @@ __device__ __forceinline__ void gu_load(const GuItem& it, int nblk, int P, int r
     const uint8_t* uscale = ucode + plane * 16;
 #pragma unroll
     for (int m = 0; m < kWinMaxPass; ++m) {
-        const int f = min(it.f0 + m * P + rp, it.rows - 1);
+        const int f = min(it.f0 + min(m, gp - 1) * P + rp, it.rows - 1);
         const size_t blk = it.none ? 0 : (size_t)f * nblk + b;
         c.cg[m] = ldg_u4(gcode + blk * 16);
         c.cu[m] = ldg_u4(ucode + blk * 16);
@@ -250,10 +280,10 @@ __device__ __forceinline__ void gu_load(const GuItem& it, int nblk, int P, int r
 // rows, and the tile counted.
 template <int QT, int NTERM>
 __device__ __forceinline__ void gu_compute(const WindowParams& p, const WinLDS& R, const GuItem& it, GuCodes& c,
-                                           float* lds, int nblk, int P, int rp, int b, bool active) {
+                                           float* lds, int nblk, int P, int gp, int rp, int b, bool active) {
     constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
     const int tid = threadIdx.x;
-    const int Rr = P * kWinMaxPass;
+    const int Rr = P * gp;
     // With an even count of block columns, lanes 2j and 2j + 1 (columns b and
     // b + 1 of one row) add their partials first: ncol columns per (row,
     // token), padded to ncp.
@@ -289,7 +319,7 @@ __device__ __forceinline__ void gu_compute(const WindowParams& p, const WinLDS& 
 #pragma unroll
             for (int m = 0; m < kWinMaxPass; ++m) {
                 const int f = it.f0 + m * P + rp;
-                if (active && f < it.rows) {
+                if (active && m < gp && f < it.rows) {
                     float og[1], ou[1];
                     block_dot<QT, NTERM, 1>(c.cg[m], scale_at_use(c.sg[m]), xs, 1, og);
                     block_dot<QT, NTERM, 1>(c.cu[m], scale_at_use(c.su[m]), xs, 1, ou);
@@ -333,13 +363,15 @@ template <int QT, int NTERM>
 __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLDS& R, float* lds) {
     constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, NTERM>::N;
     const int tid = threadIdx.x;
-    const int n_routed = R.n_groups * p.tiles_gu;
-    const int n_items = n_routed + (p.FFs ? (p.T + kWinGroup - 1) / kWinGroup * p.tiles_gu_s : 0);
+    const int n_routed = __builtin_amdgcn_readfirstlane(R.n_groups * R.tiles_gu);
+    const int n_items =
+        n_routed + (p.FFs ? (p.T + kWinGroup - 1) / kWinGroup * __builtin_amdgcn_readfirstlane(R.tiles_gu_s) : 0);
     const int nblk = p.H / QK;
     const int P = kGemvThreads / nblk;
     const bool active = tid < P * nblk;
     const int rp = active ? tid / nblk : 0, b = active ? tid - (tid / nblk) * nblk : 0;
-    const int Rr = P * kWinMaxPass;
+    const int gp = __builtin_amdgcn_readfirstlane(R.gu_passes);
+    const int Rr = P * gp;
     int item = blockIdx.x;
     if (item >= n_items) return;
     // Every token's activation slice of every block column, once per
@@ -367,7 +399,7 @@ __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLD
     }
     GuItem ia = gu_item(p, R, item, n_routed, Rr), ib;
     GuCodes ca, cb;
-    gu_load(ia, nblk, P, rp, b, ca);
+    gu_load(ia, nblk, P, gp, rp, b, ca);
     if (p.x_off >= 0) {
         uint32_t* xsl = reinterpret_cast<uint32_t*>(lds) + p.x_off;
         if (pre) {
@@ -397,15 +429,15 @@ __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLD
         int next = item + p.n_wg;
         ib = gu_item(p, R, next < n_items ? next : item, n_routed, Rr);
         ib.none = next >= n_items;
-        gu_load(ib, nblk, P, rp, b, cb);
-        gu_compute<QT, NTERM>(p, R, ia, ca, lds, nblk, P, rp, b, active);
+        gu_load(ib, nblk, P, gp, rp, b, cb);
+        gu_compute<QT, NTERM>(p, R, ia, ca, lds, nblk, P, gp, rp, b, active);
         if (next >= n_items) break;
         item = next;
         next = item + p.n_wg;
         ia = gu_item(p, R, next < n_items ? next : item, n_routed, Rr);
         ia.none = next >= n_items;
-        gu_load(ia, nblk, P, rp, b, ca);
-        gu_compute<QT, NTERM>(p, R, ib, cb, lds, nblk, P, rp, b, active);
+        gu_load(ia, nblk, P, gp, rp, b, ca);
+        gu_compute<QT, NTERM>(p, R, ib, cb, lds, nblk, P, gp, rp, b, active);
         if (next >= n_items) break;
         item = next;
     }
@@ -620,10 +652,10 @@ __device__ __forceinline__ void dn_load(const WindowParams& p, const DnItem& it,
 
 // Wait for the group's gate/up and take its `a` rows.
 template <int QK>
-__device__ __forceinline__ void dn_begin(const WindowParams& p, const DnItem& it, float* lds) {
+__device__ __forceinline__ void dn_begin(const WindowParams& p, const WinLDS& R, const DnItem& it, float* lds) {
     if (threadIdx.x == 0) {
         long spins = 0;
-        const int need = it.sh ? p.tiles_gu_s : p.tiles_gu;
+        const int need = __builtin_amdgcn_readfirstlane(it.sh ? R.tiles_gu_s : R.tiles_gu);
         while (__hip_atomic_load(win_gu_count(p.sync, it.g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
             if (++spins > kWinSpin) {
                 win_flag_error(p);
@@ -779,7 +811,7 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
     int od_a = 0, od_b = 0;
     while (true) {
         int next = item + p.n_wg;
-        dn_begin<QK>(p, ia, lds);
+        dn_begin<QK>(p, R, ia, lds);
         if (item != first_item) dn_settle(p, R, ib, od_b);
         ib = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         ib.none = next >= n_items;
@@ -792,7 +824,7 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
         }
         item = next;
         next = item + p.n_wg;
-        dn_begin<QK>(p, ib, lds);
+        dn_begin<QK>(p, R, ib, lds);
         dn_settle(p, R, ia, od_a);
         ia = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         ia.none = next >= n_items;
@@ -856,7 +888,7 @@ template <int QT, int NTERM>
 __global__ void __launch_bounds__(kGemvThreads, 2) window_layer_kernel(WindowParams p) {
     extern __shared__ __align__(16) float lds[];
     __shared__ WinLDS R;
-    route_window(p, R, reinterpret_cast<uint64_t*>(lds));
+    route_window(p, R, reinterpret_cast<uint64_t*>(lds), kGemvThreads / (p.H / QTraits<QT>::QK));
     if (blockIdx.x == 0) {
         for (int q = threadIdx.x; q < p.T * p.k; q += kGemvThreads) {
             if (p.ids_out) p.ids_out[q] = R.id[q];
@@ -883,6 +915,8 @@ WindowShape window_shape(int H, int FF, int FFs, int qtype, int x_dtype, int T, 
     const int nterm = x_dtype == 1 ? 1 : 2;
     const int sw = (nterm * qk / 2 + (qk == 64 ? 3 : 1) + 1 + 3) & ~3;
     const size_t x_bytes = (size_t)T * nblk * sw * 4;
+    // The largest gate/up tiling: it sizes the partials and bounds the items
+    // (the kernel picks the pass count of each call from its groups, gu_tiling).
     g.gu_passes = kWinMaxPass;
     const int rows_gu = P * g.gu_passes;
     g.tiles_gu = (FF + rows_gu - 1) / rows_gu;
@@ -1008,9 +1042,6 @@ hipError_t launch_window_layer(const WindowShape& g, const void* const* table, c
     p.d = (uint32_t*)(ws + L.d);
     p.y = y;
     p.sync = (int*)(ws + L.sync);
-    p.gu_passes = g.gu_passes;
-    p.tiles_gu = g.tiles_gu;
-    p.tiles_gu_s = g.tiles_gu_s;
     p.dn_passes = g.dn_passes;
     p.chunk_rows = g.chunk_rows;
     p.n_chunks = g.n_chunks;
