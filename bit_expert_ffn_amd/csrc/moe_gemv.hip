@@ -26,7 +26,9 @@ namespace moe {
 // ---------------------------------------------------------------------------------------------
 constexpr size_t kDecodeLdsBudget = 112 * 1024;   // dynamic LDS of the fused decode kernel
 constexpr int kMaxRowsDn = 12;               // H rows per down workgroup
-constexpr int kRowsPerThread = 6;            // down rows one thread prefetches
+// Down rows one thread prefetches: as many as the registers hold without
+// spilling (2-bit blocks decode into more registers than 4-bit ones).
+__host__ __device__ constexpr int rows_per_thread(int qtype) { return qtype == 1 ? 6 : 10; }
 constexpr long kSpinLimit = 1l << 22;
 constexpr int kLoadFan = 16;                 // counters of the down workgroups done loading `a`
 
@@ -389,10 +391,11 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
             dcode = p.shared + gu_s;
         }
         const uint8_t* dscale = dcode + (size_t)p.H * nb * 16;
-        uint4 c[kRowsPerThread];
-        uint16_t sc[kRowsPerThread];
+        constexpr int RPT = rows_per_thread(QT);
+        uint4 c[RPT];
+        uint16_t sc[RPT];
 #pragma unroll
-        for (int i = 0; i < kRowsPerThread; ++i) {
+        for (int i = 0; i < RPT; ++i) {
             const int r = min(rs + i * S, nrows - 1);
             const size_t blk = (size_t)(h0 + r) * nb + b;
             c[i] = ldg_u4(dcode + blk * 16);
@@ -475,7 +478,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
         }
         if (act) {
 #pragma unroll
-            for (int i = 0; i < kRowsPerThread; ++i) {
+            for (int i = 0; i < RPT; ++i) {
                 const int r = rs + i * S;
                 if (r < nrows) {
                     float o[NT];
@@ -651,13 +654,13 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     const size_t per_row =
         ((size_t)g.max_groups * ((nb_r + 3) & ~3) + (size_t)g.shared_groups * ((nb_s + 3) & ~3) + g.max_groups +
          g.shared_groups) * NT * 4;
-    // One thread prefetches at most kRowsPerThread rows of its unit; with few
+    // One thread prefetches at most rows_per_thread rows of its unit; with few
     // units, S = 256 / units threads share a unit's rows.
     int s_min = (int)(kGemvThreads / units);
     s_min = s_min < 1 ? 1 : s_min;
     int rows = (H + 255) / 256;
     rows = rows < 1 ? 1 : (rows > kMaxRowsDn ? kMaxRowsDn : rows);
-    if (rows > kRowsPerThread * s_min) rows = kRowsPerThread * s_min;
+    if (rows > rows_per_thread(qtype) * s_min) rows = rows_per_thread(qtype) * s_min;
     // One token: the `a` words are staged in LDS ahead of the partials.
     const long words = (long)g.max_groups * FF + FFs;
     g.stage_words = (T == 1 && words <= kStageMaxWords) ? (int)words : 0;
