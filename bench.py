@@ -47,6 +47,63 @@ def algorithmic_bytes_per_layer(w, ids_np):
             + w.tokens * w.experts * 4 + w.tokens * w.hidden * 4), uniq
 
 
+def gpu_clocks():
+    """Current shader (sclk) and memory (mclk) clocks in MHz of the first GPU,
+    read from the amdgpu sysfs DPM tables (the level marked '*'), else from
+    rocm-smi; None where neither is readable."""
+    import glob
+    import re
+    out = {}
+    for name in ("sclk", "mclk"):
+        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{name}")):
+            try:
+                for line in open(f):
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                        if m:
+                            out[name + "_mhz"] = int(m.group(1))
+            except OSError:
+                pass
+            if name + "_mhz" in out:
+                break
+    if len(out) < 2:
+        try:
+            import subprocess
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+            d = json.loads(r.stdout)
+            card = d[sorted(d)[0]]
+            for key, v in card.items():
+                k = key.lower()
+                for name in ("sclk", "mclk"):
+                    if f"({name})" in k and name + "_mhz" not in out:
+                        m = re.search(r"(\d+)", str(v))
+                        if m:
+                            out[name + "_mhz"] = int(m.group(1))
+        except Exception:
+            pass
+    return {"sclk_mhz": out.get("sclk_mhz"), "mclk_mhz": out.get("mclk_mhz"), "sampled": "after the timed repeats"}
+
+
+def host_cores():
+    """Host CPUs: os.cpu_count() and the CPUs this process may run on."""
+    return {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+class one_core:
+    """Runs the enclosed code pinned to one CPU (the first this process may
+    use), restoring the affinity afterwards."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.cpu = min(self.saved)
+        os.sched_setaffinity(0, {self.cpu})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+        return False
+
+
 def kernel_source_hash():
     import glob
     import hashlib
@@ -99,7 +156,8 @@ def cpu_baseline(w, x_host, l_host, budget_s=12.0):
     tok = steps * w.tokens
     return {"value": tok / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} full step(s) x {w.layers} layers x {w.tokens} token(s) of the same workload, "
-                      f"float64 oracle single-threaded, {t_total:.1f} s"}, ref
+                      f"float64 oracle single-threaded, pinned to one CPU, {t_total:.1f} s",
+            "host": host_cores()}, ref
 
 
 def prefill_flops(w, n_slots, T):
@@ -158,7 +216,8 @@ def prefill_cpu_baseline(w, x0, l0, got, n=64):
     return ({"value": len(sample) / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
              "sample": f"{len(sample)} of the {w.tokens} prompt tokens of layer 0 (tokens routed to the hottest "
                        f"expert {hot} and the coldest expert {cold}, then the first tokens), float64 oracle "
-                       f"single-threaded, {t_total:.1f} s"},
+                       f"single-threaded, pinned to one CPU, {t_total:.1f} s",
+             "host": host_cores()},
             err, len(sample))
 
 
@@ -225,28 +284,33 @@ def bench_prefill(args, w):
             for l in range(w.layers):
                 layer(s, l)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # The K timed steps, run `repeats` times, each run bracketed by HIP events
+    # on the launch stream and a device synchronisation; value = the median
+    # run.  Per-kernel durations come from the boundary events of every run.
+    reps_ms = []
+    dur = np.zeros((args.repeats, K, w.layers, nk))
     t_wall = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for i, s in enumerate(range(W, nsteps)):
+    for rep in range(args.repeats):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for i, s in enumerate(range(W, nsteps)):
+                for l in range(w.layers):
+                    layer(s, l, evs[i][l])
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        reps_ms.append(ev0.elapsed_time(ev1))
+        for i in range(K):
             for l in range(w.layers):
-                layer(s, l, evs[i][l])
-            log(f"step {i + 1}/{K} enqueued")
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_total = ev0.elapsed_time(ev1)
+                for j in range(nk):
+                    dur[rep, i, l, j] = evs[i][l][j].elapsed_time(evs[i][l][j + 1])
+        log(f"repeat {rep + 1}/{args.repeats}: {reps_ms[-1] / K:.3f} ms per step")
+    t_wall = (time.perf_counter() - t_wall) / args.repeats
+    clocks = gpu_clocks()
+    ms_total = float(np.median(reps_ms))
     ms_step = ms_total / K
     tok_s = K * w.tokens / (ms_total / 1e3)
-
-    # Per-kernel durations over the timed region, from the boundary events.
-    dur = np.zeros((K, w.layers, nk))
-    for i in range(K):
-        for l in range(w.layers):
-            for j in range(nk):
-                dur[i, l, j] = evs[i][l][j].elapsed_time(evs[i][l][j + 1])
-    avg_ms = dur.mean(axis=(0, 1))
+    avg_ms = dur.mean(axis=(0, 1, 2))
     n_slots = w.tokens * w.top_k
     gu, dn = prefill_flops(w, n_slots, w.tokens)
     layer_flops = gu + dn
@@ -291,10 +355,15 @@ def bench_prefill(args, w):
                      "bytes_per_launch": int(dom_bytes)},
         "stages": stages,
         "wall_s": round(t_wall, 4),
+        "repeats": args.repeats, "median_ms_per_step": round(ms_step, 4),
+        "min_ms_per_step": round(min(reps_ms) / K, 4),
+        "max_tokens_per_s": round(K * w.tokens / (min(reps_ms) / 1e3), 1),
+        "repeat_ms": [round(r, 3) for r in reps_ms], "clocks": clocks, "host_cores": host_cores(),
     }
     if not args.no_cpu_baseline:
         got = y_first.cpu().numpy()
-        base, err, n = prefill_cpu_baseline(w, x0, l0, got)
+        with one_core():
+            base, err, n = prefill_cpu_baseline(w, x0, l0, got)
         result["cpu_baseline"] = base
         result["parity_max_err_over_rms"] = err
         result["parity_tokens"] = n
@@ -309,8 +378,12 @@ def main():
     ap.add_argument("--workload", default="strata_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--repeats", type=int, default=5, help="timed repeats of the K steps (value = median)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain fp32 elementwise copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--calibrate-copy64", type=int, default=0, metavar="MIB",
+                    help="run only a copy of MIB MiB read as 64-byte runs, one per 128 bytes of a source twice "
+                         "as large (counter calibration for kernels whose requests are 64 B) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -329,6 +402,17 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "fp32 neg copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                          "launches": 3}), flush=True)
+        return
+    if args.calibrate_copy64:
+        # Reads 16 of every 32 floats (one 64-byte run per 128 bytes) and writes them packed.
+        n = args.calibrate_copy64 * (1 << 20) // 4
+        src = torch.ones((n // 16, 32), dtype=torch.float32, device="cuda")
+        dst = torch.empty((n // 16, 16), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            dst.copy_(src[:, :16])
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "fp32 copy of 64-byte runs", "bytes_read": 4 * n, "bytes_written": 4 * n,
                           "launches": 3}), flush=True)
         return
 
@@ -408,15 +492,22 @@ def main():
 
     replay_warm()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # The K timed steps, replayed `repeats` times; each replay is bracketed by
+    # HIP events on the launch stream and a device synchronisation on both
+    # sides.  value = the median replay; the minimum is reported beside it.
+    reps_ms = []
     t_wall = time.perf_counter()
-    ev0.record(stream)
-    replay_timed()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_total = ev0.elapsed_time(ev1)
+    for _ in range(args.repeats):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        replay_timed()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        reps_ms.append(ev0.elapsed_time(ev1))
+    t_wall = (time.perf_counter() - t_wall) / args.repeats
+    clocks = gpu_clocks()
+    ms_total = float(np.median(reps_ms))
     ms_step = ms_total / K
     tok_s = K * w.tokens / (ms_total / 1e3)
 
@@ -469,9 +560,14 @@ def main():
                      "launch_us": round(layer_ms * 1e3, 3),
                      "bytes_per_launch": int(bytes_layer), "eager_launch_us": round(eager_layer_ms * 1e3, 3)},
         "wall_s": round(t_wall, 4),
+        "repeats": args.repeats, "median_ms_per_step": round(ms_step, 5),
+        "min_ms_per_step": round(min(reps_ms) / K, 5),
+        "max_tokens_per_s": round(K * w.tokens / (min(reps_ms) / 1e3), 2),
+        "repeat_ms": [round(r, 4) for r in reps_ms], "clocks": clocks, "host_cores": host_cores(),
     }
     if not args.no_cpu_baseline:
-        base, ref = cpu_baseline(w, x_host, l_host)
+        with one_core():
+            base, ref = cpu_baseline(w, x_host, l_host)
         result["cpu_baseline"] = base
         got = y[0, w.layers - 1].cpu().numpy()
         rms = float(np.sqrt(np.mean(ref ** 2)))

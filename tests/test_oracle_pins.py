@@ -172,6 +172,31 @@ def test_topk_special_cases():
     assert list(ids[0]) == [2, 1, 0, 3]
 
 
+def test_topk_all_neg_inf_selection_gets_equal_weights():
+    """Reading (ties, -0, NaN): a selection whose top logit is -inf gets equal
+    weights.  Pinned to the limit it extends: k equal finite logits c give
+    exactly 1/k whatever c (every term is exp(0)), so equal weights are the
+    value of the softmax as c -> -inf; with renormalize = 0 the same limit over
+    all E logits gives 1/E."""
+    E = 6
+    for k in (1, 3, 6):
+        l = np.full((2, E), -np.inf, dtype=np.float32)
+        ids, w = oracle.route_topk(l, k)
+        assert list(ids[0]) == list(range(k))            # all tied: lowest indices first
+        assert np.all(w == 1.0 / k)
+        for c in (-1e3, -1e30, float(np.finfo(np.float32).min)):
+            _, wc = oracle.route_topk(np.full((2, E), c, dtype=np.float32), k)
+            assert np.array_equal(wc, w)
+        _, w0 = oracle.route_topk(l, k, renormalize=False)
+        assert np.all(w0 == 1.0 / E)
+    # -inf on top and NaN below: the -inf experts first (by index), then the
+    # NaNs; the whole selection gets equal weights
+    l = np.array([[np.nan, -np.inf, np.nan, -np.inf]], dtype=np.float32)
+    ids, w = oracle.route_topk(l, 3)
+    assert list(ids[0]) == [1, 3, 0]
+    assert np.all(w == 1.0 / 3)
+
+
 def test_topk_rejects_bad_k():
     with pytest.raises(ValueError):
         oracle.route_topk(np.zeros((1, 4), np.float32), 5)
