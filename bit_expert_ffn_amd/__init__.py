@@ -21,8 +21,8 @@ QK = {Q2_64: 64, Q4_32: 32}
 
 # Functions the header declares (the CPU test checks that each is exported).
 EXPORTS = ["moe_expert_blob_bytes", "moe_expert_workspace_bytes", "moe_layer_workspace_bytes", "moe_route_topk",
-           "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed", "moe_dequant_matrix", "moe_validate_table", "moe_status_str",
-           "moe_last_error"]
+           "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed", "moe_dequant_matrix", "moe_validate_table",
+           "moe_max_tokens", "moe_workspace_check", "moe_debug_set_wait_limit", "moe_status_str", "moe_last_error"]
 
 
 class MoeError(RuntimeError):
@@ -71,6 +71,12 @@ def lib():
         L.moe_dequant_matrix.argtypes = [ctypes.POINTER(ExpertDesc), vp, i32, vp, vp]
         L.moe_validate_table.restype = ctypes.c_int
         L.moe_validate_table.argtypes = [vp, i32, vp]
+        L.moe_max_tokens.restype = ctypes.c_int64
+        L.moe_max_tokens.argtypes = [ctypes.POINTER(LayerDesc)]
+        L.moe_workspace_check.restype = ctypes.c_int
+        L.moe_workspace_check.argtypes = [ctypes.POINTER(LayerDesc), vp, sz, vp]
+        L.moe_debug_set_wait_limit.restype = None
+        L.moe_debug_set_wait_limit.argtypes = [ctypes.c_int64]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_last_error.restype = ctypes.c_char_p
@@ -122,6 +128,14 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which temporaries are allocated (and zeroed) on the launch
+    stream, so that the kernels see them ready and the caching allocator does
+    not hand them out while the call runs."""
+    import contextlib
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _xdtype(x):
     if x.dtype == torch.bfloat16:
         return BF16
@@ -139,10 +153,11 @@ def _need_cuda(*ts):
 def route_topk(logits, k, renormalize=True, ids=None, weights=None, stream=None):
     _need_cuda(logits)
     T, E = logits.shape
-    if ids is None:
-        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
-    if weights is None:
-        weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    with _on(stream):
+        if ids is None:
+            ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        if weights is None:
+            weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check(lib().moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(weights),
                                 _stream(stream)))
     return ids, weights
@@ -151,11 +166,12 @@ def route_topk(logits, k, renormalize=True, ids=None, weights=None, stream=None)
 def expert_ffn(desc, blob, x, y=None, ws=None, stream=None):
     _need_cuda(blob, x)
     T = x.shape[0]
-    if y is None:
-        y = torch.empty((T, desc.hidden), dtype=torch.float32, device=x.device)
     need = expert_workspace_bytes(desc, T)
-    if ws is None:
-        ws = workspace(need, x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, desc.hidden), dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = workspace(need, x.device)
     _check(lib().moe_expert_ffn(ctypes.byref(desc), _ptr(blob), _ptr(x), _xdtype(x), T, _ptr(y), _ptr(ws),
                                 ws.numel(), _stream(stream)))
     return y
@@ -165,10 +181,11 @@ def layer_forward(desc, table, x, logits, shared=None, y=None, ids=None, weights
     """table: int64 CUDA tensor of E blob addresses (blob.data_ptr())."""
     _need_cuda(table, x, logits, shared, y, ids, weights, ws)
     T = x.shape[0]
-    if y is None:
-        y = torch.empty((T, desc.expert.hidden), dtype=torch.float32, device=x.device)
-    if ws is None:
-        ws = workspace(layer_workspace_bytes(desc, T), x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, desc.expert.hidden), dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = workspace(layer_workspace_bytes(desc, T), x.device)
     _check(lib().moe_layer_forward(ctypes.byref(desc), _ptr(table), _ptr(shared), _ptr(x), _xdtype(x),
                                    _ptr(logits), T, _ptr(y), _ptr(ids), _ptr(weights), _ptr(ws), ws.numel(),
                                    _stream(stream)))
@@ -182,10 +199,11 @@ def layer_forward_timed(desc, table, x, logits, events, shared=None, y=None, ids
     kernel boundaries on the launch stream.  Returns (y, number of kernels)."""
     _need_cuda(table, x, logits, shared, y, ids, weights, ws)
     T = x.shape[0]
-    if y is None:
-        y = torch.empty((T, desc.expert.hidden), dtype=torch.float32, device=x.device)
-    if ws is None:
-        ws = workspace(layer_workspace_bytes(desc, T), x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, desc.expert.hidden), dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = workspace(layer_workspace_bytes(desc, T), x.device)
     handles = [e.cuda_event for e in events]
     if any(h == 0 for h in handles):
         raise ValueError("record every event once before passing it (torch creates HIP events lazily)")
@@ -200,9 +218,26 @@ def layer_forward_timed(desc, table, x, logits, events, shared=None, y=None, ids
 def dequant_matrix(desc, blob, m, stream=None):
     _need_cuda(blob)
     rows, cols = [(desc.ff, desc.hidden), (desc.ff, desc.hidden), (desc.hidden, desc.ff)][m]
-    out = torch.empty((rows, cols), dtype=torch.float32, device=blob.device)
+    with _on(stream):
+        out = torch.empty((rows, cols), dtype=torch.float32, device=blob.device)
     _check(lib().moe_dequant_matrix(ctypes.byref(desc), _ptr(blob), m, _ptr(out), _stream(stream)))
     return out
+
+
+def max_tokens(desc):
+    return int(lib().moe_max_tokens(ctypes.byref(desc)))
+
+
+def workspace_check(desc, ws, stream=None):
+    """Raises MoeError (MOE_ERR_DEVICE) if a call on `ws` failed; the library
+    then has zero-filled the workspace's shared region."""
+    _need_cuda(ws)
+    _check(lib().moe_workspace_check(ctypes.byref(desc), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def debug_set_wait_limit(polls):
+    """Bound of every kernel wait in polls; 0 forces every wait to give up; < 0 restores the default."""
+    lib().moe_debug_set_wait_limit(int(polls))
 
 
 def validate_table(table, stream=None):

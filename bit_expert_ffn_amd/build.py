@@ -17,17 +17,37 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if out.strip() and verbose:
-        print(out)
+    return r.returncode, out
+
+
+def build(verbose=False):
+    """Each source compiled to an object in parallel (every kernel is
+    self-contained: no relocatable device code), then linked."""
+    from concurrent.futures import ThreadPoolExecutor
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    cflags = [f for f in FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
+        jobs.append((obj, [HIPCC] + cflags + ["-c", os.path.join(CSRC, src), "-o", obj]))
+    if verbose:
+        for _, c in jobs:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(lambda j: _run(j[1]), jobs))
+    for (obj, _), (rc, out) in zip(jobs, results):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {os.path.basename(obj)}:\n" + out)
+        if out.strip() and verbose:
+            print(out)
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + [o for o, _ in jobs] + ["-o", LIB + ".tmp"]
+    rc, out = _run(link)
+    if rc != 0:
+        raise RuntimeError("hipcc link failed:\n" + out)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

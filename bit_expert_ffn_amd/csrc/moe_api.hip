@@ -5,12 +5,33 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/moe_ffn.h"
 #include "moe_internal.h"
 
 namespace moe {
 
 static thread_local char g_err[512] = "";
+
+// Bound of every kernel wait (polls); negative = the default.
+static std::atomic<long> g_wait_polls{-1};
+long wait_polls() {
+    const long v = g_wait_polls.load(std::memory_order_relaxed);
+    return v < 0 ? kDefaultWaitPolls : v;
+}
+
+// The matrix-core path addresses the fp16 activation planes [2][T][H] and the
+// `a` planes [2][rows][FFmax] with 32-bit byte offsets: the largest T whose
+// offsets stay below 2^32 (with a 4 KiB margin for the last chunk's reads).
+static int64_t prefill_max_tokens(int k, int H, int FF, int FFs) {
+    const int64_t lim = ((int64_t)1 << 32) - 4096;
+    const int64_t ffmax = FFs > FF ? FFs : FF;
+    const int64_t per_x = (int64_t)4 * H;                         // 2 planes x 2 bytes
+    const int64_t per_a = (int64_t)4 * ffmax * (k + (FFs ? 1 : 0));   // 2 planes x 2 bytes per row, k (+1) rows
+    const int64_t t1 = lim / per_x, t2 = lim / per_a;
+    return t1 < t2 ? t1 : t2;
+}
 
 static moe_status fail(moe_status s, const char* fmt, ...) {
     va_list ap;
@@ -168,6 +189,10 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
         return MOE_OK;
     }
+    const int64_t t_max = prefill_max_tokens(k, ed.hidden, ed.ff, FFs);
+    if (T > t_max)
+        return fail(MOE_ERR_UNSUPPORTED, "T = %d above %lld, the largest the 32-bit offsets of the matrix-core path "
+                    "address at this shape", T, (long long)t_max);
     const LargeLayout L = large_layout(T, k, E, ed.hidden, ed.ff, FFs, ed.qtype);
     if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
     hipError_t e = launch_prefill_layer(table, single, shared, ed.qtype, ed.zero_point, ed.hidden, ed.ff, FFs, x, x_dtype,
@@ -183,6 +208,9 @@ moe_status moe_expert_ffn(const moe_expert_desc* desc, const void* blob, const v
     if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
     if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown x_dtype %d", x_dtype);
     if (T == 0) return MOE_OK;
+    if (T > kSmallT && T > prefill_max_tokens(1, desc->hidden, desc->ff, 0))
+        return fail(MOE_ERR_UNSUPPORTED, "T = %d above %lld, the largest the matrix-core path addresses", T,
+                    (long long)prefill_max_tokens(1, desc->hidden, desc->ff, 0));
     if (!blob || !x || !y || !ws) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
     if (!aligned(blob, 16) || !aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256))
         return fail(MOE_ERR_INVALID_ARG, "blob, x and y must be 16-byte aligned and ws 256-byte aligned");
@@ -203,6 +231,10 @@ static moe_status layer_forward_checked(const moe_layer_desc* desc, const void* 
     if ((desc->shared_ff > 0) != (shared_blob != nullptr))
         return fail(MOE_ERR_INVALID_ARG, "shared_blob must be non-NULL exactly when shared_ff > 0");
     if (T == 0) return MOE_OK;
+    if (T > kSmallT && T > prefill_max_tokens(desc->top_k, desc->expert.hidden, desc->expert.ff, desc->shared_ff))
+        return fail(MOE_ERR_UNSUPPORTED, "T = %d above %lld, the largest the matrix-core path addresses at this shape",
+                    T, (long long)prefill_max_tokens(desc->top_k, desc->expert.hidden, desc->expert.ff,
+                                                     desc->shared_ff));
     if (!expert_table || !x || !logits || !y || !ws) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, 256) ||
         !aligned(expert_table, 8) || (shared_blob && !aligned(shared_blob, 16)) || (ids_out && !aligned(ids_out, 4)) ||
@@ -257,6 +289,37 @@ moe_status moe_dequant_matrix(const moe_expert_desc* desc, const void* blob, int
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "dequant launch: %s", hipGetErrorString(e));
     return MOE_OK;
 }
+
+int64_t moe_max_tokens(const moe_layer_desc* desc) {
+    if (check_layer(desc) != MOE_OK) return 0;
+    return prefill_max_tokens(desc->top_k, desc->expert.hidden, desc->expert.ff, desc->shared_ff);
+}
+
+moe_status moe_workspace_check(const moe_layer_desc* desc, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_layer(desc);
+    if (st != MOE_OK) return st;
+    if (!ws || !aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "ws must be a 256-byte aligned device pointer");
+    const size_t fixed = small_fixed_bytes(desc->top_k, desc->expert.hidden, desc->expert.ff, desc->shared_ff,
+                                           desc->expert.qtype);
+    if (ws_bytes < fixed) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, fixed);
+    hipStream_t s = (hipStream_t)stream;
+    int word = 0;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess)
+        e = hipMemcpy(&word, (const char*)ws + (size_t)kErrWord * sizeof(int), sizeof(int), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "workspace check: %s", hipGetErrorString(e));
+    if (word == 0) return MOE_OK;
+    // The failed call may have left any of the shared words set: return the
+    // whole fixed region (synchronisation words, `a`, d) to zero.
+    e = hipMemsetAsync(ws, 0, fixed, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "workspace reset: %s", hipGetErrorString(e));
+    return fail(MOE_ERR_DEVICE, "a layer call on this workspace failed (error bits 0x%x:%s%s); its outputs were "
+                "NaN; the workspace is reset", word, (word & kErrTimeout) ? " a bounded wait gave up" : "",
+                (word & kErrBadId) ? " an expert id outside [0, E)" : "");
+}
+
+void moe_debug_set_wait_limit(int64_t polls) { g_wait_polls.store(polls < 0 ? -1 : (long)polls); }
 
 moe_status moe_validate_table(const void* const* expert_table, int32_t E, void* stream) {
     if (!expert_table || E < 1) return fail(MOE_ERR_INVALID_ARG, "NULL table or E < 1");

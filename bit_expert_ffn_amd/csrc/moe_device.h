@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_internal.h"
+
 namespace moe {
 
 // Routing order (Krasis white paper 5.3: the k highest-scoring experts; ties
@@ -77,6 +79,35 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // reused.
 __device__ __forceinline__ void atomic_add_detached(int* p, int v) {
     asm volatile("global_atomic_add %0, %1, off\n\ts_waitcnt expcnt(0)" ::"v"(p), "v"(v) : "memory");
+}
+
+// Error bits of a workspace (see kErrWord), set with a relaxed device-scope OR.
+__device__ __forceinline__ void flag_error(int* err, int bits) {
+    __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_error(const int* err) {
+    return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A bounded wait: polls ready() (sleeping between polls) until it holds or
+// `polls` polls have failed; then flags kErrTimeout and returns false.  A
+// bound of 0 gives up at once, whether or not ready() holds (the debug mode
+// that exercises every failure path without a real stall).
+template <int SLEEP = 1, class F>
+__device__ __forceinline__ bool bounded_wait(F ready, long polls, int* err) {
+    if (polls == 0) {
+        flag_error(err, kErrTimeout);
+        return false;
+    }
+    long n = 0;
+    while (!ready()) {
+        if (++n > polls) {
+            flag_error(err, kErrTimeout);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(SLEEP);
+    }
+    return true;
 }
 
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {

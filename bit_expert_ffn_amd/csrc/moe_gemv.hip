@@ -1,4 +1,7 @@
 // Fused one-token decode layer (see moe_gemv_common.h for the GEMV scheme).
+#include <mutex>
+#include <set>
+
 #include "moe_gemv_common.h"
 
 namespace moe {
@@ -23,13 +26,18 @@ namespace moe {
 // the bound is ever reached.  The last workgroup waits until every down
 // workgroup holds its `a` and returns the counters, flags and `a` words to
 // zero for the next call.
+//
+// Failures.  A bounded wait that gives up ORs kErrTimeout into the
+// workspace's error word, and the down workgroup it belongs to writes NaN
+// into its output rows.  A call that finds the error word already set (a
+// failure that moe_workspace_check has not cleared) writes NaN into every
+// output row and does no other work.
 // ---------------------------------------------------------------------------------------------
 constexpr size_t kDecodeLdsBudget = 112 * 1024;   // dynamic LDS of the fused decode kernel
 constexpr int kMaxRowsDn = 12;               // H rows per down workgroup
 // Down rows one thread prefetches: as many as the registers hold without
 // spilling (2-bit blocks decode into more registers than 4-bit ones).
 __host__ __device__ constexpr int rows_per_thread(int qtype) { return qtype == 1 ? 6 : 10; }
-constexpr long kSpinLimit = 1l << 22;
 constexpr int kLoadFan = 16;                 // counters of the down workgroups done loading `a`
 
 struct DecodeParams {
@@ -47,6 +55,8 @@ struct DecodeParams {
     uint32_t* as;                // [T][FFs] the same for the shared expert
     float* y;                    // [T][H]
     int* sync;                   // DecodeSync words, see sync_* below
+    int* err;                    // the workspace's error word (sync + kErrWord)
+    long polls;                  // bound of every wait
     int gu_passes, tiles_gu, tiles_gu_s, max_groups, shared_groups, n_gu;
     int dn_rows, tiles_dn;
     int n_ready;                 // ready-flag replicas in use: min(kReadyReplicas, tiles_dn)
@@ -56,7 +66,6 @@ struct DecodeParams {
 
 // Word offsets inside the synchronisation area (ints; 16 ints = one 64-byte line).
 __device__ __forceinline__ int* sync_group(int* s, int g) { return s + 16 * (4 + g); }
-__device__ __forceinline__ int* sync_error(int* s) { return s + 16; }
 // Count i of the down workgroups done loading `a` (workgroup tile counts in i = tile % kLoadFan).
 __device__ __forceinline__ int* sync_loaded(int* s, int i, int n_ctr) { return s + 16 * (4 + n_ctr + i); }
 // Ready flag of group g in replica r (replicas kReadyStride bytes apart, after the lines above).
@@ -73,7 +82,7 @@ struct RouteLDS {
     int slot_src[kMaxK];   // slot j -> group * NT + token-in-group of its pair
     uint64_t topk[kGemvThreads / 64][128];   // each wave's top-k scratch
     int n_groups;
-    int flag;
+    int fail;              // this workgroup's output is NaN: an earlier failure, or one of its waits gave up
 };
 
 // Expert e's blob from the device table (a global load of one pointer).
@@ -86,6 +95,7 @@ __device__ __forceinline__ const uint8_t* expert_blob(const DecodeParams& p, int
 __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k;
+    const int prior = tid == 0 ? load_error(p.err) : 0;   // issued ahead of the logits
     if (wv == 0) {
         int id = 0;
         float wt = 1.f;
@@ -101,7 +111,10 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
             R.group_of_pair[lane] = lane;
             R.slot_src[lane] = lane;
         }
-        if (lane == 0) R.n_groups = k;
+        if (lane == 0) {
+            R.n_groups = k;
+            R.fail = prior != 0;
+        }
     }
     __syncthreads();
 }
@@ -244,11 +257,13 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         const int n_ctr = p.max_groups + p.shared_groups;
         if (old == need - 1 && tid < p.n_ready)
             __hip_atomic_store(sync_ready(p.sync, tid, grp, n_ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // The first tile of each group to finish also raises the prefetch hint
-        // (slot n_ctr): from then on the down weights may be loaded.  A hint that
-        // lands late only starts a later call's prefetch early.
+        // The first tile of each group to finish also counts the group in the
+        // prefetch hint (slot n_ctr of every replica): from the first count on,
+        // the down weights may be loaded.  The janitor clears the hint only
+        // once it counts every group, so no count lands after the clear.
         if (old == 0 && tid < p.n_ready)
-            __hip_atomic_store(sync_ready(p.sync, tid, n_ctr, n_ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(sync_ready(p.sync, tid, n_ctr, n_ctr), 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -277,7 +292,7 @@ __device__ __forceinline__ uint32_t stage_src_off(int q, int routed_words, uint3
 
 template <int QK>
 __device__ __forceinline__ void stage_a(const DecodeParams& p, __amdgpu_buffer_rsrc_t rsrc, const uint8_t* a_base,
-                                        uint32_t as_off, int routed_words, uint8_t* dst) {
+                                        uint32_t as_off, int routed_words, uint8_t* dst, int* fail) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     const int tid = threadIdx.x, wv = tid >> 6;
     int lane = tid & 63;
@@ -310,16 +325,15 @@ __device__ __forceinline__ void stage_a(const DecodeParams& p, __amdgpu_buffer_r
             if (q >= n_chunks) break;
             u32x4* slot = reinterpret_cast<u32x4*>(dst + 16 * q);
             u32x4 v = *slot;
-            long spins = 0;
-            while (min(min(v[0], v[1]), min(v[2], v[3])) == 0u) {
-                if (++spins > kSpinLimit) {
-                    __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-                v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)stage_src_off<QK>(q, routed_words, as_off), 0,
-                                                          kCpolSc1);
-            }
+            const bool ok = bounded_wait(
+                [&] {
+                    if (min(min(v[0], v[1]), min(v[2], v[3])) != 0u) return true;
+                    v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)stage_src_off<QK>(q, routed_words, as_off),
+                                                              0, kCpolSc1);
+                    return false;
+                },
+                p.polls, p.err);
+            if (!ok) *fail = 1;
             *slot = v;
         }
     }
@@ -352,11 +366,10 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
     {
         const int rep = tile % p.n_ready;
         const int n_ctr = p.max_groups + p.shared_groups;
-        long spins = 0;
-        while (__hip_atomic_load(sync_ready(p.sync, rep, n_ctr, n_ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   0 &&
-               ++spins < kSpinLimit)
-            __builtin_amdgcn_s_sleep(1);
+        const int* hint = sync_ready(p.sync, rep, n_ctr, n_ctr);
+        if (!bounded_wait([&] { return __hip_atomic_load(hint, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0; },
+                          p.polls, p.err))
+            R.fail = 1;
     }
 
     // Partials part[((group * dn_rows + r) * NT + t) * nbp + b]: a (group, row,
@@ -406,31 +419,28 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
             // groups, then shared groups) in this workgroup's replica; the wave
             // continues when all are raised.
             if (tid < 64) {
-                long spins = 0;
                 const int rep = tile % p.n_ready;
                 const int n_ctr = p.max_groups + p.shared_groups;
                 for (int g0 = 0; g0 < ng + p.shared_groups; g0 += 64) {
                     const int gi = g0 + tid;
                     const bool mine = gi < ng + p.shared_groups;
                     const int ctr = gi < ng ? gi : p.max_groups + (gi - ng);
-                    while (true) {
-                        const bool ready = !mine || __hip_atomic_load(sync_ready(p.sync, rep, ctr, n_ctr),
-                                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-                        if (__all(ready)) break;
-                        if (++spins > kSpinLimit) {
-                            if (tid == 0)
-                                __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
+                    const bool ok = bounded_wait(
+                        [&] {
+                            const bool ready = !mine || __hip_atomic_load(sync_ready(p.sync, rep, ctr, n_ctr),
+                                                                          __ATOMIC_RELAXED,
+                                                                          __HIP_MEMORY_SCOPE_AGENT) != 0;
+                            return (bool)__all(ready);
+                        },
+                        p.polls, p.err);
+                    if (!ok) R.fail = 1;
                 }
             }
             __syncthreads();
             waited = true;
             if (p.stage_words) {
                 stage_a<QK>(p, a_rsrc, reinterpret_cast<const uint8_t*>(p.a), as_off, ng * p.FF,
-                            reinterpret_cast<uint8_t*>(lds));
+                            reinterpret_cast<uint8_t*>(lds), &R.fail);
                 // Every load has landed; saying so leaves the compiler no load
                 // to wait for after the atomic below.
                 __builtin_amdgcn_s_waitcnt(0);
@@ -464,14 +474,8 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
                     }
                 } else {
                     // A word still 0 has not landed yet: read the slice again.
-                    long spins = 0;
-                    while (!load_packed_words<QT>(w, a_rsrc, off)) {
-                        if (++spins > kSpinLimit) {
-                            __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
+                    if (!bounded_wait([&] { return load_packed_words<QT>(w, a_rsrc, off); }, p.polls, p.err))
+                        R.fail = 1;
                 }
                 slice_from_packed<QT>(xs[t], w, p.z);
             }
@@ -526,7 +530,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
                 const int sg = t / NT, st = t - sg * NT;
                 acc = sum_columns(part + sh_off + ((sg * p.dn_rows + r) * NT + st) * nbp_s, nb_s) + v;
             }
-            p.y[(size_t)t * p.H + h0 + r] = acc;
+            p.y[(size_t)t * p.H + h0 + r] = R.fail ? __uint_as_float(0x7FC00000u) : acc;
         }
     }
 }
@@ -541,31 +545,23 @@ template <int NT>
 __device__ void janitor_role(const DecodeParams& p, RouteLDS& R) {
     const int tid = threadIdx.x;
     const int ng = R.n_groups, nsg = p.shared_groups, n_ctr = p.max_groups + p.shared_groups;
-    const int n_flags = p.n_ready * (ng + nsg);
-    for (int i = tid; i < n_flags; i += kGemvThreads) {
-        const int r = i / (ng + nsg), gi = i - r * (ng + nsg);
-        const int ctr = gi < ng ? gi : p.max_groups + (gi - ng);
-        long spins = 0;
-        while (__hip_atomic_load(sync_ready(p.sync, r, ctr, n_ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-            if (++spins > kSpinLimit) {
-                __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
+    // Every ready flag of every replica, and every replica's prefetch hint at
+    // its full count (one per group).
+    for (int i = tid; i < p.n_ready * (ng + nsg + 1); i += kGemvThreads) {
+        const int r = i / (ng + nsg + 1), gi = i - r * (ng + nsg + 1);
+        const bool hint = gi == ng + nsg;
+        const int ctr = hint ? n_ctr : (gi < ng ? gi : p.max_groups + (gi - ng));
+        const int need = hint ? ng + nsg : 1;
+        const int* w = sync_ready(p.sync, r, ctr, n_ctr);
+        bounded_wait<2>([&] { return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need; },
+                        p.polls, p.err);
     }
     const int fan = min(kLoadFan, p.tiles_dn);
     if (tid < fan) {
         const int members = (p.tiles_dn - tid + kLoadFan - 1) / kLoadFan;
-        long spins = 0;
-        while (__hip_atomic_load(sync_loaded(p.sync, tid, n_ctr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               members) {
-            if (++spins > kSpinLimit) {
-                __hip_atomic_store(sync_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
+        const int* w = sync_loaded(p.sync, tid, n_ctr);
+        bounded_wait<2>([&] { return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= members; },
+                        p.polls, p.err);
     }
     __syncthreads();
     for (int i = tid; i < n_ctr; i += kGemvThreads)
@@ -608,6 +604,16 @@ __global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodePar
             if (p.ids_out) p.ids_out[q] = R.id[q];
             if (p.w_out) p.w_out[q] = R.w[q];
         }
+    }
+    if (R.fail) {
+        // The workspace holds an unchecked failure: its shared state may be
+        // stale, so nothing is computed; the down workgroups write NaN rows.
+        if (wg >= p.n_gu && wg - p.n_gu < p.tiles_dn) {
+            const int h0 = (wg - p.n_gu) * p.dn_rows, nrows = min(p.dn_rows, p.H - h0);
+            for (int i = tid; i < p.T * nrows; i += kGemvThreads)
+                p.y[(size_t)(i / nrows) * p.H + h0 + i % nrows] = __uint_as_float(0x7FC00000u);
+        }
+        return;
     }
     if (wg < p.n_gu) gateup_role<QT, NT, NTERM>(p, R, wg, lds);
     else if (wg - p.n_gu < p.tiles_dn) down_role<QT, NT>(p, R, wg - p.n_gu, lds);
@@ -683,12 +689,20 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
 
 template <int QT, int NTERM>
 static hipError_t launch_decode_t(const GemvShape& g, DecodeParams& p, hipStream_t s) {
-    static bool attr_set = false;   // allow the dynamic LDS the largest shapes need
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)decode_layer_kernel<QT, NTERM>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
+    // Allow the dynamic LDS the largest shapes need, once per device.
+    static std::mutex mu;
+    static std::set<int> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (!done.count(dev)) {
+            e = hipFuncSetAttribute((const void*)decode_layer_kernel<QT, NTERM>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+            if (e != hipSuccess) return e;
+            done.insert(dev);
+        }
     }
     hipLaunchKernelGGL((decode_layer_kernel<QT, NTERM>), dim3(g.grid), dim3(kGemvThreads), g.lds_bytes, s, p);
     return hipGetLastError();
@@ -719,6 +733,8 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
     p.as = (uint32_t*)(ws + L.as);
     p.y = y;
     p.sync = (int*)(ws + L.sync);
+    p.err = p.sync + kErrWord;
+    p.polls = wait_polls();
     p.gu_passes = g.gu_passes;
     p.tiles_gu = g.tiles_gu;
     p.tiles_gu_s = g.tiles_gu_s;

@@ -20,6 +20,20 @@ constexpr int kBlockBytes = 18;
 
 inline int codes_per_block(int qtype) { return qtype == 1 ? 64 : (qtype == 2 ? 32 : 0); }
 
+// Error word of a workspace: the int kErrWord ints into the synchronisation
+// area (the first word of its second 64-byte line), in every layout.  Kernels
+// OR cause bits into it; moe_workspace_check reads it and returns the area to
+// zero.  While it is non-zero, every layer call on the workspace writes NaN
+// into its output rows and does no other work.
+constexpr int kErrWord = 16;
+constexpr int kErrTimeout = 1;     // a bounded wait gave up
+constexpr int kErrBadId = 2;       // a caller-supplied expert id outside [0, E) (its slot was skipped)
+// Polls of a bounded wait before it gives up (each poll sleeps about 64
+// cycles after a coherent load); the debug override moe_debug_set_wait_limit
+// replaces it, and a bound of 0 makes every wait give up at its first check.
+constexpr long kDefaultWaitPolls = 1l << 22;
+long wait_polls();
+
 // Synchronisation area of the one-token decode kernel: 4 + groups + 16 lines
 // of 64 bytes (flags, per-group counters, load counters), then kReadyReplicas
 // replicas of the per-group ready flags, kReadyStride bytes apart.  The

@@ -109,6 +109,7 @@ struct PrefillParams {
     uint16_t* a_lo;
     float* ypair;
     float* y;
+    const int* err;           // the workspace's error word
     int max_tiles;
 };
 
@@ -737,10 +738,16 @@ __global__ void __launch_bounds__(kDnThreads, 1) prefill_down_kernel(PrefillPara
 }
 
 // y[t][h] = shared(t)[h] + sum_j w[t][j] * Y[pair(t, j)][h], in this order.
+// While the workspace's error word is set, every output is NaN.
 __global__ void __launch_bounds__(256) prefill_combine_kernel(PrefillParams p) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t n4 = (size_t)p.T * p.H / 4;
     if (i >= n4) return;
+    if (load_error(p.err) != 0) {
+        const float nan = __uint_as_float(0x7FC00000u);
+        *reinterpret_cast<float4*>(p.y + i * 4) = make_float4(nan, nan, nan, nan);
+        return;
+    }
     const int t = (int)(i * 4 / p.H), h = (int)(i * 4 - (size_t)t * p.H);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.shared) acc = *reinterpret_cast<const float4*>(p.ypair + (size_t)(p.T * p.k + t) * p.H + h);
@@ -813,6 +820,7 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     p.a_lo = p.a_hi + P * p.ffmax;
     p.ypair = (float*)(ws + L.ypair);
     p.y = y;
+    p.err = (const int*)ws + kErrWord;   // the GEMV path's synchronisation area starts every workspace
     p.max_tiles = (int)L.max_tiles;
 
     stage_mark(marks, s);

@@ -42,13 +42,22 @@
 // Every piece of shared state is returned to zero by its last user: the last
 // down item of a group clears the group's counters and `a` rows; each
 // combining part clears the d words it read, and the last part of a chunk its
-// counters.  The bounded waits flag an error if a bound is ever reached.
+// counters.
+//
+// Failures.  A bounded wait that gives up ORs kErrTimeout into the
+// workspace's error word, and from then on every value its workgroup
+// publishes (d words, output rows) is NaN, so the failure reaches y.  A call
+// that finds the error word already set (a failure that moe_workspace_check
+// has not cleared) writes NaN into every output row and does no other work.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "moe_gemv_common.h"
 
 namespace moe {
 
 constexpr int kWinPairs = kSmallT * kMaxK;   // (token, slot) pairs of a window
-constexpr long kWinSpin = 1l << 22;
 constexpr int kWinMaxPass = 8;               // passes per item (rows = P * passes)
 // Tokens of one expert per group: a hot expert's tokens are split over
 // several groups, so that no work item holds many more tokens than others
@@ -74,6 +83,8 @@ struct WindowParams {
     uint32_t* d;                // [8k + 8][H] fp32 bits: slot t*k + j, then 8k + t for the shared expert
     float* y;                   // [T][H]
     int* sync;                  // window sync lines, see win_* below
+    int* err;                   // the workspace's error word (sync + kErrWord)
+    long polls;                 // bound of every wait
     int dn_passes, chunk_rows, n_chunks;
     int sh_passes, sh_rows, sh_items;
     int n_wg;                   // the grid
@@ -81,11 +92,10 @@ struct WindowParams {
     int stage_words;            // down: LDS words reserved for the staged `a` rows
 };
 
-// Sync lines (16 ints each): line 1 the error flag; per group g (routed
+// Sync lines (16 ints each): line 1 the error word; per group g (routed
 // groups g < 8k, the shared expert's groups from 8k on) its gate/up tile
 // count (complete at tiles_gu) and its down item count; then per chunk its
 // down item count, then per chunk the count of its combined parts.
-__device__ __forceinline__ int* win_error(int* s) { return s + 16; }
 __device__ __forceinline__ int* win_gu_count(int* s, int g) { return s + 16 * (2 + 2 * g); }
 __device__ __forceinline__ int* win_dn_count(int* s, int g) { return s + 16 * (3 + 2 * g); }
 __device__ __forceinline__ int* win_chunk(int* s, int k, int c) { return s + 16 * (2 + 2 * (kSmallT * k + kWinShared) + c); }
@@ -93,9 +103,6 @@ __device__ __forceinline__ int* win_combined(int* s, int k, int n_chunks, int c)
     return s + 16 * (2 + 2 * (kSmallT * k + kWinShared) + n_chunks + c);
 }
 
-__device__ __forceinline__ void win_flag_error(const WindowParams& p) {
-    __hip_atomic_store(win_error(p.sync), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 struct WinLDS {
     int id[kWinPairs];
@@ -107,7 +114,10 @@ struct WinLDS {
     int n_groups;
     int gu_passes, tiles_gu, tiles_gu_s;   // this call's gate/up tiling (gu_tiling)
     int flag_reset;
+    int fail;               // publish NaN: an earlier failure, or one of this workgroup's waits gave up
 };
+
+constexpr uint32_t kNaNBits = 0x7FC00000u;   // never 0, so a published NaN reads as written
 
 // Gate/up passes per tile for this call's groups: the count p of passes
 // (at most kWinMaxPass) that makes the busiest workgroup's share, rounds of
@@ -142,6 +152,7 @@ __device__ __forceinline__ void gu_tiling(const WindowParams& p, WinLDS& R, int 
 __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, uint64_t* scratch, int P_gu) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k, n = p.T * k;
+    const int prior = tid == 0 ? load_error(p.err) : 0;   // issued ahead of the logits
     for (int t = wv; t < p.T; t += kGemvThreads / 64) {
         int id = 0;
         float wt = 1.f;
@@ -153,6 +164,7 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
         }
     }
     if (tid < 4) R.key[n + tid] = 0x7FFFFFFF;
+    if (tid == 0) R.fail = prior != 0;
     __syncthreads();
     // Keys are distinct (a token selects an expert at most once), so each
     // pair's count of smaller keys is its sorted position.
@@ -443,21 +455,6 @@ __device__ __forceinline__ void gateup_window(const WindowParams& p, const WinLD
     }
 }
 
-// A published fp32 word, read agent-coherently; 0 means not visible yet.
-__device__ __forceinline__ float load_published(const WindowParams& p, const uint32_t* w) {
-    uint32_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    long spins = 0;
-    while (v == 0u) {
-        if (++spins > kWinSpin) {
-            win_flag_error(p);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    return __uint_as_float(v);
-}
-
 // Four published fp32 words, read agent-coherently.
 typedef uint32_t win_u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ win_u32x4 load_coherent4(__amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
@@ -468,18 +465,18 @@ __device__ __forceinline__ uint32_t min4(win_u32x4 v) { return min(min(v[0], v[1
 
 // Read again, until no word is 0, four words that showed a 0 (written, but
 // not yet visible here).
+// A wait that gives up leaves NaN in the words (and the error flagged).
 __device__ __forceinline__ win_u32x4 reload_published4(const WindowParams& p, __amdgpu_buffer_rsrc_t rsrc,
                                                     uint32_t off) {
     win_u32x4 v = load_coherent4(rsrc, off);
-    long spins = 0;
-    while (min4(v) == 0u) {
-        if (++spins > kWinSpin) {
-            win_flag_error(p);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        v = load_coherent4(rsrc, off);
-    }
+    const bool ok = bounded_wait(
+        [&] {
+            if (min4(v) != 0u) return true;
+            v = load_coherent4(rsrc, off);
+            return false;
+        },
+        p.polls, p.err);
+    if (!ok) v = win_u32x4{kNaNBits, kNaNBits, kNaNBits, kNaNBits};
     return v;
 }
 
@@ -556,6 +553,7 @@ __device__ __forceinline__ void combine_rows(const WindowParams& p, const WinLDS
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(sv[e]) + acc[e];
         }
+        if (R.fail) acc[0] = acc[1] = acc[2] = acc[3] = __uint_as_float(kNaNBits);
         *reinterpret_cast<float4*>(p.y + (size_t)t * p.H + h) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
         for (int j = 0; j < k; ++j) *reinterpret_cast<uint4*>(p.d + (size_t)(t * k + j) * p.H + h) = zero;
@@ -652,17 +650,13 @@ __device__ __forceinline__ void dn_load(const WindowParams& p, const DnItem& it,
 
 // Wait for the group's gate/up and take its `a` rows.
 template <int QK>
-__device__ __forceinline__ void dn_begin(const WindowParams& p, const WinLDS& R, const DnItem& it, float* lds) {
+__device__ __forceinline__ void dn_begin(const WindowParams& p, WinLDS& R, const DnItem& it, float* lds) {
     if (threadIdx.x == 0) {
-        long spins = 0;
         const int need = __builtin_amdgcn_readfirstlane(it.sh ? R.tiles_gu_s : R.tiles_gu);
-        while (__hip_atomic_load(win_gu_count(p.sync, it.g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-            if (++spins > kWinSpin) {
-                win_flag_error(p);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
+        const int* cnt = win_gu_count(p.sync, it.g);
+        if (!bounded_wait([&] { return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need; },
+                          p.polls, p.err))
+            R.fail = 1;
     }
     __syncthreads();
     if (p.stage_words) {
@@ -674,15 +668,10 @@ __device__ __forceinline__ void dn_begin(const WindowParams& p, const WinLDS& R,
             __builtin_amdgcn_make_buffer_rsrc((void*)it.a_src, 0, it.n_e * it.K * 4, kRsrcWord3);
         for (int sl = threadIdx.x; sl < it.n_e * nb; sl += kGemvThreads) {
             uint32_t w[QK];
-            long spins = 0;
             // slice sl = i * nb + b starts at word i * K + b * QK = sl * QK
-            while (!load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK))) {
-                if (++spins > kWinSpin) {
-                    win_flag_error(p);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
+            if (!bounded_wait([&] { return load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK)); }, p.polls,
+                              p.err))
+                R.fail = 1;
             XSlice<QT, 2> xs;
             slice_from_packed<QT>(xs, w, p.z);
             slice_to_lds<QT, 2>(xs, reinterpret_cast<uint32_t*>(lds) + sl * SW);
@@ -695,7 +684,7 @@ __device__ __forceinline__ void dn_begin(const WindowParams& p, const WinLDS& R,
 // and combine the chunk or clear the group's state when this item is the
 // last of either.
 template <int QT>
-__device__ __forceinline__ void dn_finish(const WindowParams& p, const WinLDS& R, const DnItem& it, const DnLane& l,
+__device__ __forceinline__ void dn_finish(const WindowParams& p, WinLDS& R, const DnItem& it, const DnLane& l,
                                           DnCodes& c, float* lds, int& old_dn) {
     constexpr int QK = QTraits<QT>::QK, SW = SliceWords<QT, 2>::N;
     const int tid = threadIdx.x;
@@ -723,14 +712,9 @@ __device__ __forceinline__ void dn_finish(const WindowParams& p, const WinLDS& R
                 // Rows too large for LDS: straight from `a`, again while a word
                 // is still 0.
                 uint32_t w[QK];
-                long spins = 0;
-                while (!load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK))) {
-                    if (++spins > kWinSpin) {
-                        win_flag_error(p);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
+                if (!bounded_wait([&] { return load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK)); },
+                                  p.polls, p.err))
+                    R.fail = 1;
                 slice_from_packed<QT>(xs[0], w, p.z);
             }
 #pragma unroll
@@ -749,8 +733,8 @@ __device__ __forceinline__ void dn_finish(const WindowParams& p, const WinLDS& R
             if (t >= nt) continue;
             const float v = sum_columns(part + (r * 2 + t) * nbp, l.nb);
             const int drow = it.sh ? kSmallT * p.k + it.first + t0 + t : R.sorted[it.first + t0 + t];
-            __hip_atomic_store(p.d + (size_t)drow * p.H + it.h0 + r, nonzero_bits(v), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.d + (size_t)drow * p.H + it.h0 + r, R.fail ? kNaNBits : nonzero_bits(v),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // The partials are reused by the next pair.  After the last pair the
         // barrier also waits for every d store of the workgroup, so the item
@@ -846,7 +830,7 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
 // workgroup's own down items are done before it waits, and the items it waits
 // for never wait for it.  The last part of a chunk to see it complete clears
 // the chunk's counters.
-__device__ __forceinline__ void combine_window(const WindowParams& p, const WinLDS& R) {
+__device__ __forceinline__ void combine_window(const WindowParams& p, WinLDS& R) {
     const int n_sg = p.FFs ? (p.T + kWinGroup - 1) / kWinGroup : 0;
     const int need_chunk = R.n_groups + n_sg * p.sh_items;
     const int hp = max(1, min(kWinCombineParts, p.n_wg / p.n_chunks));
@@ -855,15 +839,11 @@ __device__ __forceinline__ void combine_window(const WindowParams& p, const WinL
         const int c0 = c * p.chunk_rows, nr4 = (min(c0 + p.chunk_rows, p.H) - c0) / 4;
         const int q0 = part * nr4 / hp, q1 = (part + 1) * nr4 / hp;
         if (threadIdx.x == 0) {
-            long spins = 0;
-            while (__hip_atomic_load(win_chunk(p.sync, p.k, c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                   need_chunk) {
-                if (++spins > kWinSpin) {
-                    win_flag_error(p);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
+            const int* cnt = win_chunk(p.sync, p.k, c);
+            if (!bounded_wait(
+                    [&] { return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need_chunk; },
+                    p.polls, p.err))
+                R.fail = 1;
         }
         // Count this part as one that has seen the chunk complete (no part
         // looks at the chunk's counter after that); the count returns while
@@ -894,6 +874,13 @@ __global__ void __launch_bounds__(kGemvThreads, 2) window_layer_kernel(WindowPar
             if (p.ids_out) p.ids_out[q] = R.id[q];
             if (p.w_out) p.w_out[q] = R.w[q];
         }
+    }
+    if (R.fail) {
+        // The workspace holds an unchecked failure: its shared state may be
+        // stale, so nothing is computed; every output row is NaN.
+        for (int q = blockIdx.x * kGemvThreads + threadIdx.x; q < p.T * p.H; q += p.n_wg * kGemvThreads)
+            p.y[q] = __uint_as_float(kNaNBits);
+        return;
     }
     gateup_window<QT, NTERM>(p, R, lds);
     down_window<QT>(p, R, lds);
@@ -975,29 +962,30 @@ static hipError_t launch_window_t(const WindowShape& g, const WindowParams& p, h
 }
 
 // Workgroups the current GPU holds at once for this instantiation and LDS
-// size (the kernel's registers and LDS decide), times its CUs; at most the
-// largest item count.  Cached per instantiation and LDS size.
+// size (the kernel's registers and LDS decide), times its CUs.  Cached per
+// (device, LDS size); the cache is shared by every thread of the process.
 template <int QT, int NTERM>
 static hipError_t window_capacity(size_t lds_bytes, int* out) {
-    static int dev_cached = -1, n_cu = 0;
-    static size_t lds_cached = 0;
-    static int per_cu = 0;
+    static std::mutex mu;
+    static std::map<std::pair<int, size_t>, int> cache;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev != dev_cached || lds_bytes != lds_cached) {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({dev, lds_bytes});
+    if (it == cache.end()) {
         e = hipFuncSetAttribute((const void*)window_layer_kernel<QT, NTERM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 150 * 1024);
         if (e != hipSuccess) return e;
+        int n_cu = 0, per_cu = 0;
         e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)window_layer_kernel<QT, NTERM>,
                                                          kGemvThreads, lds_bytes);
         if (e != hipSuccess) return e;
-        dev_cached = dev;
-        lds_cached = lds_bytes;
+        it = cache.emplace(std::make_pair(dev, lds_bytes), per_cu * n_cu).first;
     }
-    *out = per_cu * n_cu;
+    *out = it->second;
     return hipSuccess;
 }
 
@@ -1042,6 +1030,8 @@ hipError_t launch_window_layer(const WindowShape& g, const void* const* table, c
     p.d = (uint32_t*)(ws + L.d);
     p.y = y;
     p.sync = (int*)(ws + L.sync);
+    p.err = p.sync + kErrWord;
+    p.polls = wait_polls();
     p.dn_passes = g.dn_passes;
     p.chunk_rows = g.chunk_rows;
     p.n_chunks = g.n_chunks;

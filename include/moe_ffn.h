@@ -36,10 +36,22 @@
  *     from run to run (no atomics on any value path).  On the decode/verify path
  *     (T <= 8) a token's output is also bitwise independent of the other tokens
  *     in the batch.
- *   - Calls with distinct workspaces may run concurrently on distinct streams;
- *     calls that share a workspace must be ordered (same stream, or events).
+ *   - Concurrency.  The decode and verify-window kernels rely on all of their
+ *     workgroups being resident on the GPU at once (their work items wait on
+ *     each other).  Layer calls on one device must therefore not overlap each
+ *     other, whatever their workspaces, nor other long-running kernels on
+ *     other streams: order them on one stream, or with events.  Calls on
+ *     different devices are independent.  The library's host state (launch
+ *     caches) is per device and thread-safe.
+ *   - Failures inside a call.  Every wait inside a kernel is bounded.  A wait
+ *     that gives up sets a cause bit in the workspace's error word and the
+ *     output rows it served are NaN.  While the word is set, every later layer
+ *     call on that workspace writes NaN into all of its output rows and does
+ *     nothing else, so stale shared state can never give a finite wrong
+ *     result.  moe_workspace_check reports and clears it.
  *   - Workspace: a device buffer of at least the *_workspace_bytes size,
- *     256-byte aligned, ZERO-FILLED ONCE after allocation.  Its leading bytes
+ *     256-byte aligned, ZERO-FILLED ONCE after allocation (and after a failure
+ *     that moe_workspace_check reported, which zero-fills it itself).  Its leading bytes
  *     hold the decode kernel's state (synchronisation words and the hand-off
  *     buffer between its gate/up and down stages), which every call returns
  *     to zero; the rest is scratch.  One workspace may serve calls of any T,
@@ -152,7 +164,8 @@ moe_status moe_expert_ffn(const moe_expert_desc* desc, const void* blob, const v
  * T <= 8 (decode, verify windows) runs the GEMV path: routing, expert-major
  * de-duplicated buckets, dequant-fused gate/up + SwiGLU, down, combine.
  * Larger T (prefill) sorts token slots by expert and runs grouped matrix-core
- * GEMMs over ragged per-expert token counts.
+ * GEMMs over ragged per-expert token counts; T above moe_max_tokens(desc)
+ * returns MOE_ERR_UNSUPPORTED.
  */
 moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expert_table, const void* shared_blob,
                              const void* x, int32_t x_dtype, const float* logits, int32_t T, float* y,
@@ -186,6 +199,38 @@ moe_status moe_dequant_matrix(const moe_expert_desc* desc, const void* blob, int
  * first null entry.
  */
 moe_status moe_validate_table(const void* const* expert_table, int32_t E, void* stream);
+
+/*
+ * The largest T a layer call accepts for this descriptor (0 if it is
+ * invalid): the matrix-core path addresses its activation planes [2][T][H] and
+ * its SwiGLU planes [2][rows][max(FF, shared_ff)] (rows = T*k, plus T with a
+ * shared expert) with 32-bit byte offsets, so
+ *   T_max = min((2^32 - 4096) / (4 H), (2^32 - 4096) / (4 max(FF, shared_ff) (k + [shared_ff > 0]))).
+ * For H 7168, FF 2048, k 8 this is 65,535.
+ */
+int64_t moe_max_tokens(const moe_layer_desc* desc);
+
+/*
+ * Reports and clears a failure of earlier layer calls on a workspace (see
+ * "Failures inside a call" above).  Synchronises `stream`, reads the
+ * workspace's error word and returns MOE_OK if it is clear.  Otherwise it
+ * zero-fills the workspace's shared region (the part every call leaves zero),
+ * synchronises again and returns MOE_ERR_DEVICE; moe_last_error() names the
+ * cause bits (1: a bounded wait gave up; 2: a caller-supplied expert id outside
+ * [0, E), whose slot was skipped).  `desc` is the descriptor the workspace
+ * serves (it sizes the shared region).  Not for use inside graph capture.
+ */
+moe_status moe_workspace_check(const moe_layer_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Debug and testing: the bound of every wait inside the layer kernels, in
+ * polls (each a coherent load and a short sleep).  A negative value restores
+ * the default (2^22).  0 makes every bounded wait give up at its first check,
+ * whether or not it would have ended: every kernel still exits normally, and
+ * the failure path (error word, NaN outputs, moe_workspace_check) can be tested
+ * without a real stall.  Process-wide; takes effect at the next call.
+ */
+void moe_debug_set_wait_limit(int64_t polls);
 
 const char* moe_status_str(moe_status s);
 /* Detail of the last non-OK status returned on the calling thread. */

@@ -125,3 +125,31 @@ def test_layer_forward_timed_rejects_bad_arguments(L):
     assert nk.value == 0
     assert call(None, 0, T=0) == 0                                # nothing to do, no kernel
     assert nk.value == 0
+
+
+def test_max_tokens_and_prefill_limit(L):
+    """moe_max_tokens states the largest T the matrix-core path's 32-bit
+    offsets address; a call above it is rejected on the host."""
+    d = moe.layer_desc(7168, 2048, 2, 7.5, 256, 8)
+    lim = ((1 << 32) - 4096)
+    assert moe.max_tokens(d) == min(lim // (4 * 7168), lim // (4 * 2048 * 8)) == 65535
+    ds = moe.layer_desc(7168, 2048, 2, 7.5, 256, 8, shared_ff=4096)
+    assert moe.max_tokens(ds) == min(lim // (4 * 7168), lim // (4 * 4096 * 9))
+    assert moe.max_tokens(moe.layer_desc(2560, 640, 7, 1.5, 512, 10)) == 0      # invalid descriptor
+    p = ctypes.c_void_p(FAKE)
+    T = moe.max_tokens(d) + 1
+    st = L.moe_layer_forward(ctypes.byref(d), p, None, p, 1, p, T, p, None, None, p, 1 << 62, None)
+    assert st == 2 and b"T = 65536" in L.moe_last_error()
+    e = moe.expert_desc(7168, 2048, 2, 7.5)
+    t1 = min(lim // (4 * 7168), lim // (4 * 2048))
+    assert L.moe_expert_ffn(ctypes.byref(e), p, p, 1, t1 + 1, p, p, 1 << 62, None) == 2
+
+
+def test_workspace_check_rejects_bad_arguments(L):
+    """Argument checks of moe_workspace_check run before any HIP call."""
+    d = moe.layer_desc(2560, 640, 1, 1.5, 512, 10)
+    assert L.moe_workspace_check(ctypes.byref(d), None, 1 << 20, None) == 1           # NULL workspace
+    assert L.moe_workspace_check(ctypes.byref(d), ctypes.c_void_p(FAKE + 64), 1 << 20, None) == 1   # misaligned
+    assert L.moe_workspace_check(ctypes.byref(d), ctypes.c_void_p(FAKE), 256, None) == 3            # too small
+    assert L.moe_workspace_check(None, ctypes.c_void_p(FAKE), 1 << 20, None) == 1
+    L.moe_debug_set_wait_limit(-1)     # host-side state only
