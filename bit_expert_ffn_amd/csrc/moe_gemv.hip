@@ -325,15 +325,17 @@ __device__ __forceinline__ void stage_a(const DecodeParams& p, __amdgpu_buffer_r
             if (q >= n_chunks) break;
             u32x4* slot = reinterpret_cast<u32x4*>(dst + 16 * q);
             u32x4 v = *slot;
-            const bool ok = bounded_wait(
-                [&] {
-                    if (min(min(v[0], v[1]), min(v[2], v[3])) != 0u) return true;
-                    v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)stage_src_off<QK>(q, routed_words, as_off),
-                                                              0, kCpolSc1);
-                    return false;
-                },
-                p.polls, p.err);
-            if (!ok) *fail = 1;
+            long n = 0;
+            while (p.polls == 0 || min(min(v[0], v[1]), min(v[2], v[3])) == 0u) {
+                if (++n > p.polls) {   // a bound of 0 gives up at once
+                    flag_error(p.err, kErrTimeout);
+                    *fail = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)stage_src_off<QK>(q, routed_words, as_off), 0,
+                                                          kCpolSc1);
+            }
             *slot = v;
         }
     }
@@ -367,7 +369,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
         const int rep = tile % p.n_ready;
         const int n_ctr = p.max_groups + p.shared_groups;
         const int* hint = sync_ready(p.sync, rep, n_ctr, n_ctr);
-        if (!bounded_wait([&] { return __hip_atomic_load(hint, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0; },
+        if (!bounded_wait([&]() __attribute__((always_inline)) { return __hip_atomic_load(hint, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0; },
                           p.polls, p.err))
             R.fail = 1;
     }
@@ -426,7 +428,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
                     const bool mine = gi < ng + p.shared_groups;
                     const int ctr = gi < ng ? gi : p.max_groups + (gi - ng);
                     const bool ok = bounded_wait(
-                        [&] {
+                        [&]() __attribute__((always_inline)) {
                             const bool ready = !mine || __hip_atomic_load(sync_ready(p.sync, rep, ctr, n_ctr),
                                                                           __ATOMIC_RELAXED,
                                                                           __HIP_MEMORY_SCOPE_AGENT) != 0;
@@ -474,8 +476,16 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
                     }
                 } else {
                     // A word still 0 has not landed yet: read the slice again.
-                    if (!bounded_wait([&] { return load_packed_words<QT>(w, a_rsrc, off); }, p.polls, p.err))
-                        R.fail = 1;
+                    // (A plain loop: a lambda holding w by reference spills it.)
+                    long n = 0;
+                    while (!load_packed_words<QT>(w, a_rsrc, off) || p.polls == 0) {
+                        if (++n > p.polls) {   // a bound of 0 gives up at once
+                            flag_error(p.err, kErrTimeout);
+                            R.fail = 1;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
                 }
                 slice_from_packed<QT>(xs[t], w, p.z);
             }
@@ -553,14 +563,14 @@ __device__ void janitor_role(const DecodeParams& p, RouteLDS& R) {
         const int ctr = hint ? n_ctr : (gi < ng ? gi : p.max_groups + (gi - ng));
         const int need = hint ? ng + nsg : 1;
         const int* w = sync_ready(p.sync, r, ctr, n_ctr);
-        bounded_wait<2>([&] { return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need; },
+        bounded_wait<2>([&]() __attribute__((always_inline)) { return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need; },
                         p.polls, p.err);
     }
     const int fan = min(kLoadFan, p.tiles_dn);
     if (tid < fan) {
         const int members = (p.tiles_dn - tid + kLoadFan - 1) / kLoadFan;
         const int* w = sync_loaded(p.sync, tid, n_ctr);
-        bounded_wait<2>([&] { return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= members; },
+        bounded_wait<2>([&]() __attribute__((always_inline)) { return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= members; },
                         p.polls, p.err);
     }
     __syncthreads();

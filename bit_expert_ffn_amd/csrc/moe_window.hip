@@ -470,7 +470,7 @@ __device__ __forceinline__ win_u32x4 reload_published4(const WindowParams& p, __
                                                     uint32_t off) {
     win_u32x4 v = load_coherent4(rsrc, off);
     const bool ok = bounded_wait(
-        [&] {
+        [&]() __attribute__((always_inline)) {
             if (min4(v) != 0u) return true;
             v = load_coherent4(rsrc, off);
             return false;
@@ -654,7 +654,7 @@ __device__ __forceinline__ void dn_begin(const WindowParams& p, WinLDS& R, const
     if (threadIdx.x == 0) {
         const int need = __builtin_amdgcn_readfirstlane(it.sh ? R.tiles_gu_s : R.tiles_gu);
         const int* cnt = win_gu_count(p.sync, it.g);
-        if (!bounded_wait([&] { return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need; },
+        if (!bounded_wait([&]() __attribute__((always_inline)) { return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need; },
                           p.polls, p.err))
             R.fail = 1;
     }
@@ -669,9 +669,15 @@ __device__ __forceinline__ void dn_begin(const WindowParams& p, WinLDS& R, const
         for (int sl = threadIdx.x; sl < it.n_e * nb; sl += kGemvThreads) {
             uint32_t w[QK];
             // slice sl = i * nb + b starts at word i * K + b * QK = sl * QK
-            if (!bounded_wait([&] { return load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK)); }, p.polls,
-                              p.err))
-                R.fail = 1;
+            long n = 0;
+            while (!load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK)) || p.polls == 0) {
+                if (++n > p.polls) {   // a bound of 0 gives up at once
+                    flag_error(p.err, kErrTimeout);
+                    R.fail = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
             XSlice<QT, 2> xs;
             slice_from_packed<QT>(xs, w, p.z);
             slice_to_lds<QT, 2>(xs, reinterpret_cast<uint32_t*>(lds) + sl * SW);
@@ -712,9 +718,15 @@ __device__ __forceinline__ void dn_finish(const WindowParams& p, WinLDS& R, cons
                 // Rows too large for LDS: straight from `a`, again while a word
                 // is still 0.
                 uint32_t w[QK];
-                if (!bounded_wait([&] { return load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK)); },
-                                  p.polls, p.err))
-                    R.fail = 1;
+                long n = 0;
+                while (!load_packed_words<QT>(w, a_rsrc, 4u * (uint32_t)(sl * QK)) || p.polls == 0) {
+                    if (++n > p.polls) {   // a bound of 0 gives up at once
+                        flag_error(p.err, kErrTimeout);
+                        R.fail = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
                 slice_from_packed<QT>(xs[0], w, p.z);
             }
 #pragma unroll
@@ -841,7 +853,7 @@ __device__ __forceinline__ void combine_window(const WindowParams& p, WinLDS& R)
         if (threadIdx.x == 0) {
             const int* cnt = win_chunk(p.sync, p.k, c);
             if (!bounded_wait(
-                    [&] { return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need_chunk; },
+                    [&]() __attribute__((always_inline)) { return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need_chunk; },
                     p.polls, p.err))
                 R.fail = 1;
         }
