@@ -22,7 +22,7 @@ QK = {Q2_64: 64, Q4_32: 32}
 # Functions the header declares (the CPU test checks that each is exported).
 EXPORTS = ["moe_expert_blob_bytes", "moe_expert_workspace_bytes", "moe_layer_workspace_bytes", "moe_route_topk",
            "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed", "moe_dequant_matrix", "moe_validate_table",
-           "moe_max_tokens", "moe_workspace_check", "moe_debug_set_wait_limit", "moe_status_str", "moe_last_error"]
+           "moe_layer_forward_noalloc", "moe_max_tokens", "moe_workspace_check", "moe_debug_set_wait_limit", "moe_status_str", "moe_last_error"]
 
 
 class MoeError(RuntimeError):
@@ -71,6 +71,8 @@ def lib():
         L.moe_dequant_matrix.argtypes = [ctypes.POINTER(ExpertDesc), vp, i32, vp, vp]
         L.moe_validate_table.restype = ctypes.c_int
         L.moe_validate_table.argtypes = [vp, i32, vp]
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
+        L.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp, i32, vp, i32, vp, vp, vp, vp]
         L.moe_max_tokens.restype = ctypes.c_int64
         L.moe_max_tokens.argtypes = [ctypes.POINTER(LayerDesc)]
         L.moe_workspace_check.restype = ctypes.c_int
@@ -222,6 +224,18 @@ def dequant_matrix(desc, blob, m, stream=None):
         out = torch.empty((rows, cols), dtype=torch.float32, device=blob.device)
     _check(lib().moe_dequant_matrix(ctypes.byref(desc), _ptr(blob), m, _ptr(out), _stream(stream)))
     return out
+
+
+def layer_forward_noalloc(desc, table, x, logits, shared=None, y=None, ids=None, weights=None, stream=None):
+    """layer_forward (T <= 8) with the library's own device array as workspace."""
+    _need_cuda(table, x, logits, shared, y, ids, weights)
+    T = x.shape[0]
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, desc.expert.hidden), dtype=torch.float32, device=x.device)
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(desc), _ptr(table), _ptr(shared), _ptr(x), _xdtype(x),
+                                           _ptr(logits), T, _ptr(y), _ptr(ids), _ptr(weights), _stream(stream)))
+    return y
 
 
 def max_tokens(desc):

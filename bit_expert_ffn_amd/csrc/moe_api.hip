@@ -6,6 +6,8 @@
 #include <string.h>
 
 #include <atomic>
+#include <map>
+#include <mutex>
 
 #include "../../include/moe_ffn.h"
 #include "moe_internal.h"
@@ -69,6 +71,39 @@ SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype) {
 }
 
 size_t small_fixed_bytes(int k, int H, int FF, int FFs, int qtype) { return small_layout(0, k, H, FF, FFs, qtype).ids; }
+
+// Workspace of moe_layer_forward_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes its name to a
+// kernel (on the host the name is only a stand-in): its device address comes
+// from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static hipError_t scratch_address(void** out) {
+    static std::mutex mu;
+    static std::map<int, void*> addr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = addr.find(dev);
+    if (it == addr.end()) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        it = addr.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return hipSuccess;
+}
+
+// Zero-fill of n16 16-byte words (a kernel rather than a memset node, so that
+// a captured graph replays it correctly).
+__global__ void __launch_bounds__(256) zero_fill_kernel(uint4* p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
 
 }  // namespace moe
 
@@ -288,6 +323,37 @@ moe_status moe_dequant_matrix(const moe_expert_desc* desc, const void* blob, int
                                   (hipStream_t)stream);
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "dequant launch: %s", hipGetErrorString(e));
     return MOE_OK;
+}
+
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const void* const* expert_table,
+                                     const void* shared_blob, const void* x, int32_t x_dtype, const float* logits,
+                                     int32_t T, float* y, int32_t* ids_out, float* w_out, void* stream) {
+    moe_status st = check_layer(desc);
+    if (st != MOE_OK) return st;
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+    if (T > kSmallT)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_layer_forward_noalloc serves T <= %d (decode and verify windows), got %d",
+                    kSmallT, T);
+    const size_t need = moe_layer_workspace_bytes(desc, T);
+    if (need > kScratchBytes)
+        return fail(MOE_ERR_WORKSPACE, "this shape needs %zu bytes of workspace, above the %zu-byte device array of "
+                    "moe_layer_forward_noalloc", need, kScratchBytes);
+    if (T == 0) return layer_forward_checked(desc, expert_table, shared_blob, x, x_dtype, logits, T, y, ids_out, w_out,
+                                             nullptr, 0, stream, nullptr);
+    void* ws = nullptr;
+    hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+    // The array keeps the last call's contents: its shared region is cleared
+    // before this call uses it (a failed earlier call may have left it set).
+    const size_t fixed = small_fixed_bytes(desc->top_k, desc->expert.hidden, desc->expert.ff, desc->shared_ff,
+                                           desc->expert.qtype);
+    const size_t n16 = fixed / 16;
+    const unsigned blocks = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (uint4*)ws, n16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "zero-fill launch: %s", hipGetErrorString(e));
+    return layer_forward_checked(desc, expert_table, shared_blob, x, x_dtype, logits, T, y, ids_out, w_out, ws,
+                                 kScratchBytes, stream, nullptr);
 }
 
 int64_t moe_max_tokens(const moe_layer_desc* desc) {

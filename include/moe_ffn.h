@@ -201,6 +201,26 @@ moe_status moe_dequant_matrix(const moe_expert_desc* desc, const void* blob, int
 moe_status moe_validate_table(const void* const* expert_table, int32_t E, void* stream);
 
 /*
+ * moe_layer_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same checks, kernels and results (bitwise) as moe_layer_forward for T <= 8,
+ * but the workspace is a library-owned device array of 4 MiB per GPU (a
+ * file-scope __device__ array, held until the process ends), so the caller
+ * passes none.  Each call first clears the array's shared region with a fill
+ * kernel (no memset node, so a captured graph replays it correctly) and calls
+ * no hipMalloc, hipFree or allocating routine.
+ *   T > 8 (the matrix-core path, whose workspace is far larger) returns
+ *   MOE_ERR_UNSUPPORTED; a shape whose T = 8 workspace exceeds 4 MiB returns
+ *   MOE_ERR_WORKSPACE (the Strata and Gemma decode shapes need about 1.2 MB).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * race (they must be ordered, as every layer call on a device must be).  A
+ * failure shows as NaN outputs (the next call's clear resets the array).
+ */
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const void* const* expert_table,
+                                     const void* shared_blob, const void* x, int32_t x_dtype, const float* logits,
+                                     int32_t T, float* y, int32_t* ids_out, float* w_out, void* stream);
+
+/*
  * The largest T a layer call accepts for this descriptor (0 if it is
  * invalid): the matrix-core path addresses its activation planes [2][T][H] and
  * its SwiGLU planes [2][rows][max(FF, shared_ff)] (rows = T*k, plus T with a
