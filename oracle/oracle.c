@@ -21,10 +21,18 @@
  *             projections -> activation/gating -> weighted reduction) and
  *             section 7.1 (the layer output is the router-weighted sum of the
  *             selected experts' outputs).
- *   [kairos]  kairos-engine README, "The MoE forward" (top-k over the router
- *             logits; the shared expert is summed with the routed experts,
- *             not sequenced) and "The memory problem, and the expert arena"
- *             (4-bit expert file; ~12.85 GB of experts).
+ *   [kairos]  kairos-engine README, "The MoE forward" (normalise, router GEMM
+ *             to logits, top-k; the router reads its input through its own
+ *             weightless norm and a per-input-dim scale; the down projection's
+ *             scale is per expert; the shared expert is summed with the routed
+ *             experts, not sequenced), "The memory problem, and the expert
+ *             arena" (4-bit expert file; ~12.85 GB of experts) and "Decode,
+ *             2026-09-28/29: the hybrid, and the host thread" (the model's
+ *             GELU is the tanh form).
+ *   [Krasis]  section 7.5 "Preserving the native execution shape": a fixed
+ *             top-k shape in which an omitted route is a slot with a dummy
+ *             expert and a zero router weight, for which no expert work is
+ *             done.
  *
  * Readings where the pages leave a step open (each is also a descriptor
  * field or documented choice of the library):
@@ -43,7 +51,15 @@
  *     (-0 == +0; a NaN logit ranks below every number).  Weights are the
  *     softmax over the k selected logits (renormalize = 1) or the full softmax
  *     over all E logits taken at the selected experts (renormalize = 0).
- *   - Activation: SwiGLU, a = silu(gate x) * (up x), silu(v) = v / (1 + e^-v).
+ *   - Activation: SwiGLU, a = silu(gate x) * (up x), silu(v) = v / (1 + e^-v);
+ *     or GeGLU with the tanh form of GELU, a = gelu(gate x) * (up x),
+ *     gelu(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
+ *   - Per-expert down scale: expert e's output is s_e * (W_down a).
+ *   - Router: logits = W_r x' with bf16 W_r [E][H]; x' = x, or with the
+ *     weightless norm x / sqrt(mean(x^2) + eps), then times the per-input-dim
+ *     scale when one is given.
+ *   - Caller-supplied routing: the given ids and weights are used as they are;
+ *     a slot whose weight is 0 contributes nothing and its expert is not read.
  *   - Output: y = shared(x) + sum_j w_j expert_{id_j}(x), shared first, then
  *     slots in rank order.
  */
@@ -148,6 +164,15 @@ static void matvec(const omat* M, const double* v, double* out) {
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }
 
+/* GELU, tanh form: v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))). */
+static double gelu_tanh(double v) {
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * v * (1.0 + tanh(c * (v + 0.044715 * v * v * v)));
+}
+
+/* The gate's activation: 0 = SiLU (SwiGLU), 1 = tanh GELU (GeGLU). */
+static double gate_act(double g, int act) { return act == 1 ? gelu_tanh(g) : silu(g); }
+
 /* Activations as exact doubles: x_dtype 0 = fp32, 1 = bf16 raw bits. */
 static void load_x(const void* x, int x_dtype, int64_t n, double* out) {
     if (x_dtype == 1) {
@@ -159,16 +184,45 @@ static void load_x(const void* x, int x_dtype, int64_t n, double* out) {
     }
 }
 
-/* One expert's SwiGLU FFN on one token: y = W_down (silu(W_gate x) * (W_up x)). */
-static void ffn_token(const uint8_t* blob, int qtype, double z, int64_t H, int64_t FF, const double* x, double* y,
-                      double* g, double* u) {
+/* One expert's gated FFN on one token: y = W_down (act(W_gate x) * (W_up x)). */
+static void ffn_token_act(const uint8_t* blob, int qtype, double z, int64_t H, int64_t FF, int act, const double* x,
+                          double* y, double* g, double* u) {
     omat Mg = matrix_of(blob, qtype, z, H, FF, 0);
     omat Mu = matrix_of(blob, qtype, z, H, FF, 1);
     omat Md = matrix_of(blob, qtype, z, H, FF, 2);
     matvec(&Mg, x, g);
     matvec(&Mu, x, u);
-    for (int64_t f = 0; f < FF; ++f) g[f] = silu(g[f]) * u[f];
+    for (int64_t f = 0; f < FF; ++f) g[f] = gate_act(g[f], act) * u[f];
     matvec(&Md, g, y);
+}
+
+/* SwiGLU. */
+static void ffn_token(const uint8_t* blob, int qtype, double z, int64_t H, int64_t FF, const double* x, double* y,
+                      double* g, double* u) {
+    ffn_token_act(blob, qtype, z, H, FF, 0, x, y, g, u);
+}
+
+/* gelu_tanh of n values (exported for the pins). */
+void oracle_gelu_tanh(const double* v, int64_t n, double* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = gelu_tanh(v[i]);
+}
+
+/* y[T][H] = expert FFN with activation act (0 SwiGLU, 1 GeGLU-tanh) of each token. */
+int oracle_expert_ffn_act(const uint8_t* blob, int qtype, double z, int64_t H, int64_t FF, int act, const void* x,
+                          int x_dtype, int64_t T, double* y) {
+    if (codes_per_block(qtype) == 0 || H % codes_per_block(qtype) || FF % codes_per_block(qtype)) return 1;
+    if (act != 0 && act != 1) return 1;
+    double* xt = (double*)malloc(sizeof(double) * (size_t)H);
+    double* g = (double*)malloc(sizeof(double) * (size_t)FF);
+    double* u = (double*)malloc(sizeof(double) * (size_t)FF);
+    for (int64_t t = 0; t < T; ++t) {
+        load_x((const uint8_t*)x + (size_t)(t * H) * (x_dtype == 1 ? 2 : 4), x_dtype, H, xt);
+        ffn_token_act(blob, qtype, z, H, FF, act, xt, y + t * H, g, u);
+    }
+    free(xt);
+    free(g);
+    free(u);
+    return 0;
 }
 
 /* y[T][H] = expert FFN of each token; x is T x H (fp32 or bf16 bits). */
@@ -256,6 +310,84 @@ int oracle_layer_forward(const uint8_t* const* blobs, int32_t E, int32_t k, int3
         for (int j = 0; j < k; ++j) {
             ffn_token(blobs[ids[t * k + j]], qtype, z, H, FF, xt, ye, g, u);
             for (int64_t h = 0; h < H; ++h) yt[h] += w[t * k + j] * ye[h];
+        }
+    }
+    free(xt);
+    free(ye);
+    free(g);
+    free(u);
+    return 0;
+}
+
+/* Router: logits[t][e] = sum_h W_r[e][h] x'[t][h], W_r bf16 bits [E][H];
+ * x' = x, or with norm = 1 the weightless norm x / sqrt(mean_h x^2 + eps);
+ * then times in_scale[h] when in_scale is not NULL. */
+int oracle_router_logits(const uint16_t* wr, int32_t E, int64_t H, const void* x, int x_dtype, int64_t T, int norm,
+                         double eps, const float* in_scale, double* logits) {
+    if (E < 1 || H < 1) return 1;
+    double* xt = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int64_t t = 0; t < T; ++t) {
+        load_x((const uint8_t*)x + (size_t)(t * H) * (x_dtype == 1 ? 2 : 4), x_dtype, H, xt);
+        if (norm) {
+            double ss = 0.0;
+            for (int64_t h = 0; h < H; ++h) ss += xt[h] * xt[h];
+            const double r = 1.0 / sqrt(ss / (double)H + eps);
+            for (int64_t h = 0; h < H; ++h) xt[h] *= r;
+        }
+        if (in_scale)
+            for (int64_t h = 0; h < H; ++h) xt[h] *= (double)in_scale[h];
+        for (int32_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; ++h) acc += bf16_to_double(wr[(size_t)e * H + h]) * xt[h];
+            logits[t * E + e] = acc;
+        }
+    }
+    free(xt);
+    return 0;
+}
+
+/* One routed MoE FFN layer with the options of the extended call:
+ *   act        : 0 SwiGLU, 1 GeGLU-tanh (routed and shared experts alike)
+ *   down_scale : NULL, or [E]: routed expert e's output is down_scale[e] * (W_down a)
+ *   ids_in/w_in: NULL, or caller-supplied routing [T][k]; a slot whose weight is 0 is
+ *                skipped (its id is not read); a nonzero weight with an id outside
+ *                [0, E) is an error (returns 2).  Otherwise routing from logits.
+ *   ids, w     : the routing used (outputs). */
+int oracle_layer_forward_ex(const uint8_t* const* blobs, int32_t E, int32_t k, int32_t renormalize, int qtype,
+                            double z, int64_t H, int64_t FF, int act, const uint8_t* shared, int64_t shared_ff,
+                            const float* down_scale, const void* x, int x_dtype, const float* logits,
+                            const int32_t* ids_in, const float* w_in, int64_t T, double* y, int32_t* ids, double* w) {
+    int qk = codes_per_block(qtype);
+    if (qk == 0 || H % qk || FF % qk || (shared && shared_ff % qk) || (act != 0 && act != 1)) return 1;
+    if (ids_in) {
+        for (int64_t q = 0; q < T * k; ++q) {
+            if (w_in[q] != 0.0f && (ids_in[q] < 0 || ids_in[q] >= E)) return 2;
+            ids[q] = ids_in[q];
+            w[q] = (double)w_in[q];
+        }
+    } else if (oracle_route_topk(logits, T, E, k, renormalize, ids, w)) {
+        return 1;
+    }
+    int64_t ffmax = shared && shared_ff > FF ? shared_ff : FF;
+    double* xt = (double*)malloc(sizeof(double) * (size_t)H);
+    double* ye = (double*)malloc(sizeof(double) * (size_t)H);
+    double* g = (double*)malloc(sizeof(double) * (size_t)ffmax);
+    double* u = (double*)malloc(sizeof(double) * (size_t)ffmax);
+    for (int64_t t = 0; t < T; ++t) {
+        double* yt = y + t * H;
+        load_x((const uint8_t*)x + (size_t)(t * H) * (x_dtype == 1 ? 2 : 4), x_dtype, H, xt);
+        for (int64_t h = 0; h < H; ++h) yt[h] = 0.0;
+        if (shared) {
+            ffn_token_act(shared, qtype, z, H, shared_ff, act, xt, ye, g, u);
+            for (int64_t h = 0; h < H; ++h) yt[h] += ye[h];
+        }
+        for (int j = 0; j < k; ++j) {
+            const double wj = w[t * k + j];
+            if (ids_in && wj == 0.0) continue;   /* an omitted route: no expert work */
+            const int e = ids[t * k + j];
+            ffn_token_act(blobs[e], qtype, z, H, FF, act, xt, ye, g, u);
+            const double s = down_scale ? (double)down_scale[e] : 1.0;
+            for (int64_t h = 0; h < H; ++h) yt[h] += wj * (s * ye[h]);
         }
     }
     free(xt);

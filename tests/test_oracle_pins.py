@@ -387,3 +387,159 @@ def test_layer_shared_expert_is_added():
     zero[:] = 0
     y0, _, _ = oracle.layer_forward([b] * E, k, 2, z, H, FF, x, logits, shared=zero, shared_ff=3 * FF)
     np.testing.assert_array_equal(y0, yr)
+
+
+# --- Gemma-faithful options: GeGLU (tanh GELU), per-expert down scale ---------------------------
+
+def test_gelu_tanh_against_library_and_identities():
+    """kairos-engine README ("Decode, 2026-09-28/29"): the model's GELU is the tanh
+    form.  Pinned to torch's own tanh-approximate GELU in float64, to the
+    identity gelu(v) - gelu(-v) = v that the tanh form keeps exactly, and to its
+    distance from the erf GELU (a few 1e-4 at most)."""
+    import torch
+    from scipy.special import erf
+    v = np.concatenate([np.linspace(-12, 12, 4001), [0.0, -0.0, 1e-12, -1e-12, 30.0, -30.0, 1e4, -1e4]])
+    g = oracle.gelu_tanh(v)
+    ref = torch.nn.functional.gelu(torch.from_numpy(v), approximate="tanh").numpy()
+    np.testing.assert_allclose(g, ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(g - oracle.gelu_tanh(-v), v, rtol=1e-13, atol=1e-15)
+    assert g[v == 0.0].tolist() == [0.0, 0.0, 0.0]
+    exact = 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+    assert np.max(np.abs(g - exact)) < 5e-4
+
+
+def test_expert_ffn_geglu_equals_dense_product():
+    import torch
+    rng = np.random.default_rng(31)
+    for qtype, H, FF in [(1, 128, 64), (2, 96, 64)]:
+        blob, (Wg, Wu, Wd), z = random_expert(rng, qtype, H, FF, 0.1)
+        x = rng.normal(size=(3, H)).astype(np.float32)
+        xd = x.astype(np.float64)
+        g = xd @ Wg.T
+        a = torch.nn.functional.gelu(torch.from_numpy(g), approximate="tanh").numpy() * (xd @ Wu.T)
+        np.testing.assert_allclose(oracle.expert_ffn(blob, qtype, z, H, FF, x, act=1), a @ Wd.T, rtol=1e-10,
+                                   atol=1e-12)
+        # act 0 of the extended function is the SwiGLU FFN, bit for bit
+        np.testing.assert_array_equal(oracle.expert_ffn(blob, qtype, z, H, FF, x, act=0),
+                                      oracle.expert_ffn(blob, qtype, z, H, FF, x))
+
+
+def _small_layer_blobs(rng, E, qtype, H, FF, sigma):
+    blobs, dense = [], []
+    for _ in range(E):
+        b, d, z = random_expert(rng, qtype, H, FF, sigma)
+        blobs.append(b)
+        dense.append(d)
+    return blobs, dense, z
+
+
+def test_layer_down_scale_per_expert():
+    """kairos-engine README ("The MoE forward"): the down projection's scale is
+    per expert.  Pins: scale 1 everywhere is the plain layer bit for bit; scale 2
+    everywhere doubles y exactly; random scales equal sum_j w_j s_{e_j} y_{e_j}
+    over dense experts."""
+    rng = np.random.default_rng(41)
+    E, k, H, FF = 8, 3, 128, 64
+    blobs, dense, z = _small_layer_blobs(rng, E, 1, H, FF, 0.05)
+    x = rng.normal(size=(4, H)).astype(np.float32)
+    lg = rng.normal(size=(4, E)).astype(np.float32)
+    y0, ids, w = oracle.layer_forward(blobs, k, 1, z, H, FF, x, lg)
+    y1, _, _ = oracle.layer_forward_ex(blobs, k, 1, z, H, FF, x, lg, down_scale=np.ones(E))
+    np.testing.assert_array_equal(y1, y0)
+    y2, _, _ = oracle.layer_forward_ex(blobs, k, 1, z, H, FF, x, lg, down_scale=np.full(E, 2.0))
+    np.testing.assert_array_equal(y2, 2.0 * y0)
+    s = rng.uniform(0.2, 3.0, size=E).astype(np.float32)
+    ys, _, _ = oracle.layer_forward_ex(blobs, k, 1, z, H, FF, x, lg, down_scale=s, act=1)
+    import torch
+    xd = x.astype(np.float64)
+    ref = np.zeros((4, H))
+    for t in range(4):
+        for j in range(k):
+            Wg, Wu, Wd = dense[ids[t, j]]
+            a = torch.nn.functional.gelu(torch.from_numpy(Wg @ xd[t]), approximate="tanh").numpy() * (Wu @ xd[t])
+            ref[t] += w[t, j] * float(s[ids[t, j]]) * (Wd @ a)
+    np.testing.assert_allclose(ys, ref, rtol=1e-10, atol=1e-12)
+
+
+# --- fixed top-k shape: caller-supplied routing, zero-weight slots skipped ------------------------
+
+def test_routed_zero_weight_slot_is_skipped():
+    """Krasis white paper 7.5: an omitted route keeps its slot with a dummy
+    expert and a zero weight, and no expert work is done for it.  A dummy
+    blob with NaN scales behind zero-weight slots (and an id outside [0, E))
+    leaves y finite and equal to the dense sum over the remaining slots; all
+    weights zero give y = 0 exactly; a nonzero weight on an id outside [0, E)
+    is rejected."""
+    rng = np.random.default_rng(43)
+    E, k, H, FF = 6, 4, 128, 64
+    blobs, dense, z = _small_layer_blobs(rng, E, 1, H, FF, 0.05)
+    poison = blobs[5].copy()
+    nb = FF * (H // 64)
+    poison[nb * 16:nb * 18] = np.frombuffer(np.full(nb, 0x7E00, dtype='<u2').tobytes(), dtype=np.uint8)   # NaN scales
+    blobs[5] = poison
+    x = rng.normal(size=(3, H)).astype(np.float32)
+    ids = np.array([[2, 5, 0, 5], [1, 3, 9, 4], [5, 5, 5, 5]], dtype=np.int32)
+    w = np.array([[0.5, 0.0, 0.25, 0.0], [0.4, 0.3, 0.0, 0.3], [0, 0, 0, 0]], dtype=np.float32)
+    y, ids_o, w_o = oracle.layer_forward_ex(blobs, k, 1, z, H, FF, x, ids_in=ids, w_in=w)
+    assert np.all(np.isfinite(y))
+    np.testing.assert_array_equal(ids_o, ids)
+    xd = x.astype(np.float64)
+    ref = np.zeros((3, H))
+    for t in range(3):
+        for j in range(k):
+            if w[t, j] != 0:
+                Wg, Wu, Wd = dense[ids[t, j]]
+                ref[t] += float(w[t, j]) * (Wd @ ((Wg @ xd[t]) / (1 + np.exp(-(Wg @ xd[t]))) * (Wu @ xd[t])))
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
+    assert np.all(y[2] == 0.0)
+    with pytest.raises(ValueError):
+        oracle.layer_forward_ex(blobs, k, 1, z, H, FF, x, ids_in=np.where(ids == 9, 7, ids),
+                                w_in=np.where(ids == 9, 0.2, w).astype(np.float32))
+
+
+def test_routed_equals_logit_routing_with_the_same_weights():
+    """Routing supplied as the oracle's own top-k ids and weights (rounded to
+    fp32) gives the logit-routed layer up to that rounding."""
+    rng = np.random.default_rng(47)
+    E, k, H, FF = 16, 4, 96, 64
+    blobs, _, z = _small_layer_blobs(rng, E, 2, H, FF, 0.02)
+    x = rng.normal(size=(5, H)).astype(np.float32)
+    lg = rng.normal(size=(5, E)).astype(np.float32)
+    y0, ids, w = oracle.layer_forward(blobs, k, 2, z, H, FF, x, lg)
+    y1, _, _ = oracle.layer_forward_ex(blobs, k, 2, z, H, FF, x, ids_in=ids, w_in=w.astype(np.float32))
+    np.testing.assert_allclose(y1, y0, rtol=1e-6, atol=1e-6 * np.abs(y0).max())
+
+
+# --- router GEMV front end -----------------------------------------------------------------------
+
+def test_router_logits_equal_dense_product_and_norm_properties():
+    """kairos-engine README ("The MoE forward"): the router GEMM gives the logits,
+    reading its input through its own weightless norm and a per-input-dim scale.
+    Pins: without the norm the logits equal a dense float64 product with the
+    bf16 weights; with identity weights the logits are x' itself, which with the
+    norm (eps 0) has unit mean square, is proportional to x and is invariant to
+    scaling x by 4 (exact in binary floating point); the per-input-dim scale
+    multiplies x' element by element."""
+    import synth
+    rng = np.random.default_rng(53)
+    E, H, T = 24, 160, 3
+    wr = np.array([synth.bf16_bits(v) for v in rng.normal(0, 0.05, size=E * H)], dtype=np.uint16).reshape(E, H)
+    xb = np.array([synth.bf16_bits(v) for v in rng.normal(size=T * H)], dtype=np.uint16).reshape(T, H)
+    W = synth.bf16_to_f32(wr).astype(np.float64)
+    X = synth.bf16_to_f32(xb).astype(np.float64)
+    np.testing.assert_allclose(oracle.router_logits(wr, xb), X @ W.T, rtol=1e-12, atol=1e-14)
+    xf = rng.normal(size=(T, H)).astype(np.float32)
+    np.testing.assert_allclose(oracle.router_logits(wr, xf), xf.astype(np.float64) @ W.T, rtol=1e-12, atol=1e-14)
+    one = synth.bf16_bits(1.0)
+    ident = np.zeros((H, H), dtype=np.uint16)
+    ident[np.arange(H), np.arange(H)] = one
+    xn = oracle.router_logits(ident, xf, norm=True, eps=0.0)
+    np.testing.assert_allclose(np.mean(xn ** 2, axis=1), 1.0, rtol=1e-14)
+    ratio = xn / xf.astype(np.float64)
+    np.testing.assert_allclose(ratio, ratio[:, :1] * np.ones((1, H)), rtol=1e-14)
+    np.testing.assert_array_equal(oracle.router_logits(ident, 4 * xf, norm=True, eps=0.0), xn)
+    sc = rng.uniform(0.5, 2.0, size=H).astype(np.float32)
+    np.testing.assert_allclose(oracle.router_logits(ident, xf, norm=True, eps=0.0, in_scale=sc),
+                               xn * sc.astype(np.float64), rtol=1e-15)
+    # eps only ever lowers |x'|
+    assert np.all(np.abs(oracle.router_logits(ident, xf, norm=True, eps=1e-2)) <= np.abs(xn))
