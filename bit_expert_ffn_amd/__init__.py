@@ -21,7 +21,7 @@ QK = {Q2_64: 64, Q4_32: 32}
 
 # Functions the header declares (the CPU test checks that each is exported).
 EXPORTS = ["moe_expert_blob_bytes", "moe_expert_workspace_bytes", "moe_layer_workspace_bytes", "moe_route_topk",
-           "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_timed", "moe_dequant_matrix", "moe_validate_table",
+           "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_ex", "moe_router_logits", "moe_layer_forward_timed", "moe_dequant_matrix", "moe_validate_table",
            "moe_layer_forward_noalloc", "moe_max_tokens", "moe_workspace_check", "moe_debug_set_wait_limit", "moe_status_str", "moe_last_error"]
 
 
@@ -39,6 +39,20 @@ class ExpertDesc(ctypes.Structure):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("expert", ExpertDesc), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("renormalize", ctypes.c_int32), ("shared_ff", ctypes.c_int32)]
+
+
+class Router(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("in_scale", ctypes.c_void_p), ("norm", ctypes.c_int32),
+                ("eps", ctypes.c_float)]
+
+
+class LayerOpts(ctypes.Structure):
+    _fields_ = [("router", ctypes.POINTER(Router)), ("logits_out", ctypes.c_void_p), ("down_scale", ctypes.c_void_p),
+                ("ids_in", ctypes.c_void_p), ("w_in", ctypes.c_void_p)]
+
+
+ACT_SWIGLU = 0
+ACT_GEGLU_TANH = 1
 
 
 _lib = None
@@ -64,6 +78,11 @@ def lib():
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, sz,
                                         vp]
+        L.moe_layer_forward_ex.restype = ctypes.c_int
+        L.moe_layer_forward_ex.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerOpts), vp, vp, vp, i32, vp,
+                                           i32, vp, vp, vp, vp, sz, vp]
+        L.moe_router_logits.restype = ctypes.c_int
+        L.moe_router_logits.argtypes = [ctypes.POINTER(Router), i32, i32, vp, i32, i32, vp, vp]
         L.moe_layer_forward_timed.restype = ctypes.c_int
         L.moe_layer_forward_timed.argtypes = [ctypes.POINTER(LayerDesc), vp, vp, vp, i32, vp, i32, vp, vp, vp, vp,
                                               sz, vp, vp, i32, ctypes.POINTER(i32)]
@@ -96,12 +115,23 @@ def _check(status):
         raise MoeError(status, lib().moe_last_error().decode())
 
 
-def expert_desc(hidden, ff, qtype, zero_point):
-    return ExpertDesc(hidden, ff, qtype, float(zero_point), 0)
+def expert_desc(hidden, ff, qtype, zero_point, act=ACT_SWIGLU):
+    return ExpertDesc(hidden, ff, qtype, float(zero_point), act)
 
 
-def layer_desc(hidden, ff, qtype, zero_point, n_experts, top_k, renormalize=True, shared_ff=0):
-    return LayerDesc(expert_desc(hidden, ff, qtype, zero_point), n_experts, top_k, int(bool(renormalize)), shared_ff)
+def layer_desc(hidden, ff, qtype, zero_point, n_experts, top_k, renormalize=True, shared_ff=0, act=ACT_SWIGLU):
+    return LayerDesc(expert_desc(hidden, ff, qtype, zero_point, act), n_experts, top_k, int(bool(renormalize)),
+                     shared_ff)
+
+
+def router(weight, in_scale=None, norm=False, eps=1e-6):
+    """weight: bf16 CUDA tensor [E][H]; in_scale: fp32 CUDA tensor [H] or None.
+    The returned struct holds references to both tensors, so their memory
+    stays allocated while it is in use."""
+    _need_cuda(weight, in_scale)
+    rt = Router(weight.data_ptr(), in_scale.data_ptr() if in_scale is not None else None, int(bool(norm)), float(eps))
+    rt._tensors = (weight, in_scale)
+    return rt
 
 
 def expert_blob_bytes(desc):
@@ -191,6 +221,37 @@ def layer_forward(desc, table, x, logits, shared=None, y=None, ids=None, weights
     _check(lib().moe_layer_forward(ctypes.byref(desc), _ptr(table), _ptr(shared), _ptr(x), _xdtype(x),
                                    _ptr(logits), T, _ptr(y), _ptr(ids), _ptr(weights), _ptr(ws), ws.numel(),
                                    _stream(stream)))
+    return y
+
+
+def router_logits(rt, E, x, logits=None, stream=None):
+    """rt: a Router (see router()); x [T][H]; returns logits [T][E] fp32."""
+    _need_cuda(x, logits)
+    T, H = x.shape
+    with _on(stream):
+        if logits is None:
+            logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().moe_router_logits(ctypes.byref(rt), E, H, _ptr(x), _xdtype(x), T, _ptr(logits), _stream(stream)))
+    return logits
+
+
+def layer_forward_ex(desc, table, x, logits=None, shared=None, rt=None, logits_out=None, down_scale=None,
+                     ids_in=None, w_in=None, y=None, ids=None, weights=None, ws=None, stream=None):
+    """The layer with options: rt (a Router: logits computed inside the call),
+    down_scale [E], or caller-supplied routing ids_in / w_in [T][k]."""
+    _need_cuda(table, x, logits, shared, logits_out, down_scale, ids_in, w_in, y, ids, weights, ws)
+    T = x.shape[0]
+    with _on(stream):
+        if y is None:
+            y = torch.empty((T, desc.expert.hidden), dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = workspace(layer_workspace_bytes(desc, T), x.device)
+    opts = LayerOpts(ctypes.pointer(rt) if rt is not None else None, logits_out.data_ptr() if logits_out is not None
+                     else None, down_scale.data_ptr() if down_scale is not None else None,
+                     ids_in.data_ptr() if ids_in is not None else None, w_in.data_ptr() if w_in is not None else None)
+    _check(lib().moe_layer_forward_ex(ctypes.byref(desc), ctypes.byref(opts), _ptr(table), _ptr(shared), _ptr(x),
+                                      _xdtype(x), _ptr(logits), T, _ptr(y), _ptr(ids), _ptr(weights), _ptr(ws),
+                                      ws.numel(), _stream(stream)))
     return y
 
 

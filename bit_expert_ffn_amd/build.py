@@ -5,7 +5,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
-SOURCES = ["moe_api.hip", "moe_route.hip", "moe_gemv.hip", "moe_window.hip", "moe_prefill.hip"]
+SOURCES = ["moe_api.hip", "moe_route.hip", "moe_router.hip", "moe_gemv.hip", "moe_window.hip", "moe_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -54,7 +54,7 @@ struct Bump {
     }
 };
 
-SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype) {
+SmallLayout small_layout(int T, int k, int E, int H, int FF, int FFs, int qtype) {
     SmallLayout L{};
     Bump b;
     const size_t n = (size_t)T * k;
@@ -66,11 +66,14 @@ SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype) {
     L.d = b.take((size_t)(kSmallT * k + kSmallT) * H * 4);
     L.ids = b.take(n * 4);
     L.w = b.take(n * 4);
+    L.logits = b.take((size_t)T * E * 4);
     L.total = b.off;
     return L;
 }
 
-size_t small_fixed_bytes(int k, int H, int FF, int FFs, int qtype) { return small_layout(0, k, H, FF, FFs, qtype).ids; }
+size_t small_fixed_bytes(int k, int H, int FF, int FFs, int qtype) {
+    return small_layout(0, k, 1, H, FF, FFs, qtype).ids;
+}
 
 // Workspace of moe_layer_forward_noalloc: a file-scope device array, one copy
 // per GPU, held until the process ends.  Host code never passes its name to a
@@ -117,7 +120,8 @@ static moe_status check_expert(const moe_expert_desc* d, const char* what) {
     if (d->hidden % qk || d->ff % qk)
         return fail(MOE_ERR_INVALID_ARG, "%s: hidden (%d) and ff (%d) must be multiples of %d", what, d->hidden,
                     d->ff, qk);
-    if (d->act != MOE_ACT_SWIGLU) return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d not supported", what, d->act);
+    if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_GEGLU_TANH)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d not supported", what, d->act);
     if (!isfinite(d->zero_point)) return fail(MOE_ERR_INVALID_ARG, "%s: zero_point is not finite", what);
     if (fabsf(d->zero_point) > 64.f || d->zero_point * 2.f != floorf(d->zero_point * 2.f))
         return fail(MOE_ERR_UNSUPPORTED, "%s: zero_point %g is not a multiple of 0.5 in [-64, 64]", what,
@@ -170,14 +174,15 @@ size_t moe_expert_blob_bytes(const moe_expert_desc* d) {
 size_t moe_layer_workspace_bytes(const moe_layer_desc* d, int32_t T) {
     if (check_layer(d) != MOE_OK || T < 0) return 0;
     if (T <= kSmallT)
-        return small_layout(T, d->top_k, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype).total;
+        return small_layout(T, d->top_k, d->n_experts, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype)
+            .total;
     return large_layout(T, d->top_k, d->n_experts, d->expert.hidden, d->expert.ff, d->shared_ff, d->expert.qtype)
         .total;
 }
 
 size_t moe_expert_workspace_bytes(const moe_expert_desc* d, int32_t T) {
     if (check_expert(d, "expert") != MOE_OK || T < 0) return 0;
-    if (T <= kSmallT) return small_layout(T, 1, d->hidden, d->ff, 0, d->qtype).total;
+    if (T <= kSmallT) return small_layout(T, 1, 1, d->hidden, d->ff, 0, d->qtype).total;
     return large_layout(T, 1, 1, d->hidden, d->ff, 0, d->qtype).total;
 }
 
@@ -199,11 +204,34 @@ moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k, 
 
 static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_desc& ed, int FFs,
                             const void* const* table, const void* single, const void* shared, const void* x,
-                            int x_dtype, const float* logits, float* y, int32_t* ids_out, float* w_out, void* ws,
-                            size_t ws_bytes, hipStream_t s, bool identity, StageMarks* marks = nullptr) {
+                            int x_dtype, const float* logits, const moe_layer_opts* opts, float* y, int32_t* ids_out,
+                            float* w_out, void* ws, size_t ws_bytes, hipStream_t s, bool identity,
+                            StageMarks* marks = nullptr) {
     char* wsb = (char*)ws;
+    LayerOpts o;
+    o.act = ed.act;
+    const moe_router* router = nullptr;
+    float* logits_out = nullptr;
+    if (opts) {
+        o.down_scale = opts->down_scale;
+        o.ids_in = opts->ids_in;
+        o.w_in = opts->w_in;
+        router = opts->router;
+        logits_out = opts->logits_out;
+    }
+    // The router, when it runs inside the call, writes the logits the layer
+    // kernels read (into the caller's buffer or the workspace).
+    auto run_router = [&](size_t ws_logits) -> hipError_t {
+        if (!router) return hipSuccess;
+        float* lg = logits_out ? logits_out : (float*)(wsb + ws_logits);
+        stage_mark(marks, s);
+        hipError_t e = launch_router(router->weight, router->in_scale, router->norm, router->eps, E, ed.hidden, x,
+                                     x_dtype, T, lg, s);
+        logits = lg;
+        return e;
+    };
     if (T <= kSmallT) {
-        const SmallLayout L = small_layout(T, k, ed.hidden, ed.ff, FFs, ed.qtype);
+        const SmallLayout L = small_layout(T, k, E, ed.hidden, ed.ff, FFs, ed.qtype);
         if (ws_bytes < L.total)
             return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
         hipError_t e;
@@ -211,15 +239,19 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
             const GemvShape g = gemv_shape(ed.hidden, ed.ff, FFs, ed.qtype, ed.zero_point, T, k);
             if (g.lds_bytes > 128 * 1024)
                 return fail(MOE_ERR_UNSUPPORTED, "decode tile needs %zu bytes of LDS", g.lds_bytes);
-            e = launch_decode_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm, identity ? 1 : 0,
-                                    ids_out, w_out, L, wsb, y, s, marks);
+            e = run_router(L.logits);
+            if (e == hipSuccess)
+                e = launch_decode_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm,
+                                        identity ? 1 : 0, o, ids_out, w_out, L, wsb, y, s, marks);
         } else {
             const WindowShape g = window_shape(ed.hidden, ed.ff, FFs, ed.qtype, x_dtype, T, k);
             if (g.lds_bytes > 150 * 1024)
                 return fail(MOE_ERR_UNSUPPORTED, "verify window needs %zu bytes of LDS", g.lds_bytes);
-            e = launch_window_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm, identity ? 1 : 0,
-                                    ed.qtype, ed.zero_point, ed.hidden, ed.ff, FFs, ids_out, w_out, L, wsb, y, s,
-                                    marks);
+            e = run_router(L.logits);
+            if (e == hipSuccess)
+                e = launch_window_layer(g, table, single, shared, x, x_dtype, logits, T, E, k, renorm,
+                                        identity ? 1 : 0, o, ed.qtype, ed.zero_point, ed.hidden, ed.ff, FFs, ids_out,
+                                        w_out, L, wsb, y, s, marks);
         }
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "decode launch: %s", hipGetErrorString(e));
         return MOE_OK;
@@ -230,8 +262,10 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
                     "address at this shape", T, (long long)t_max);
     const LargeLayout L = large_layout(T, k, E, ed.hidden, ed.ff, FFs, ed.qtype);
     if (ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
-    hipError_t e = launch_prefill_layer(table, single, shared, ed.qtype, ed.zero_point, ed.hidden, ed.ff, FFs, x, x_dtype,
-                                        logits, T, E, k, renorm, identity ? 1 : 0, ids_out, w_out, L, wsb, y, s, marks);
+    hipError_t e = run_router(L.logits);
+    if (e == hipSuccess)
+        e = launch_prefill_layer(table, single, shared, ed.qtype, ed.zero_point, ed.hidden, ed.ff, FFs, x, x_dtype,
+                                 logits, T, E, k, renorm, identity ? 1 : 0, o, ids_out, w_out, L, wsb, y, s, marks);
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "prefill launch: %s", hipGetErrorString(e));
     return MOE_OK;
 }
@@ -251,14 +285,25 @@ moe_status moe_expert_ffn(const moe_expert_desc* desc, const void* blob, const v
         return fail(MOE_ERR_INVALID_ARG, "blob, x and y must be 16-byte aligned and ws 256-byte aligned");
     const size_t need = moe_expert_workspace_bytes(desc, T);
     if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
-    return run_layer(T, 1, 1, 1, *desc, 0, nullptr, blob, nullptr, x, x_dtype, nullptr, y, nullptr, nullptr, ws,
-                     ws_bytes, (hipStream_t)stream, true);
+    return run_layer(T, 1, 1, 1, *desc, 0, nullptr, blob, nullptr, x, x_dtype, nullptr, nullptr, y, nullptr, nullptr,
+                     ws, ws_bytes, (hipStream_t)stream, true);
+}
+
+static moe_status check_router(const moe_router* r, int H) {
+    if (!r->weight) return fail(MOE_ERR_INVALID_ARG, "router weight is NULL");
+    if (!aligned(r->weight, 16) || (r->in_scale && !aligned(r->in_scale, 16)))
+        return fail(MOE_ERR_INVALID_ARG, "router weight and in_scale must be 16-byte aligned");
+    if (r->norm != 0 && r->norm != 1) return fail(MOE_ERR_INVALID_ARG, "router norm must be 0 or 1");
+    if (!isfinite(r->eps) || r->eps < 0.f) return fail(MOE_ERR_INVALID_ARG, "router eps must be finite and >= 0");
+    if (H % 32) return fail(MOE_ERR_INVALID_ARG, "router: H must be a multiple of 32");
+    return MOE_OK;
 }
 
 static moe_status layer_forward_checked(const moe_layer_desc* desc, const void* const* expert_table,
                                         const void* shared_blob, const void* x, int32_t x_dtype, const float* logits,
                                         int32_t T, float* y, int32_t* ids_out, float* w_out, void* ws,
-                                        size_t ws_bytes, void* stream, StageMarks* marks) {
+                                        size_t ws_bytes, void* stream, StageMarks* marks,
+                                        const moe_layer_opts* opts = nullptr) {
     moe_status st = check_layer(desc);
     if (st != MOE_OK) return st;
     if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
@@ -270,16 +315,56 @@ static moe_status layer_forward_checked(const moe_layer_desc* desc, const void* 
         return fail(MOE_ERR_UNSUPPORTED, "T = %d above %lld, the largest the matrix-core path addresses at this shape",
                     T, (long long)prefill_max_tokens(desc->top_k, desc->expert.hidden, desc->expert.ff,
                                                      desc->shared_ff));
-    if (!expert_table || !x || !logits || !y || !ws) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
-    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(logits, 4) || !aligned(ws, 256) ||
+    const bool routed = opts && opts->ids_in;
+    const bool router = opts && opts->router;
+    if (opts) {
+        if (routed && router) return fail(MOE_ERR_INVALID_ARG, "ids_in and router are exclusive");
+        if (routed != (opts->w_in != nullptr)) return fail(MOE_ERR_INVALID_ARG, "ids_in and w_in come together");
+        if (router && logits) return fail(MOE_ERR_INVALID_ARG, "logits must be NULL when the router computes them");
+        if (!router && opts->logits_out) return fail(MOE_ERR_INVALID_ARG, "logits_out needs the router");
+        if ((opts->ids_in && !aligned(opts->ids_in, 4)) || (opts->w_in && !aligned(opts->w_in, 4)) ||
+            (opts->down_scale && !aligned(opts->down_scale, 4)) || (opts->logits_out && !aligned(opts->logits_out, 4)))
+            return fail(MOE_ERR_INVALID_ARG, "misaligned option pointer (4 B)");
+        if (router) {
+            moe_status rs = check_router(opts->router, desc->expert.hidden);
+            if (rs != MOE_OK) return rs;
+        }
+    }
+    if (!expert_table || !x || (!logits && !routed && !router) || !y || !ws)
+        return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(x, 16) || !aligned(y, 16) || (logits && !aligned(logits, 4)) || !aligned(ws, 256) ||
         !aligned(expert_table, 8) || (shared_blob && !aligned(shared_blob, 16)) || (ids_out && !aligned(ids_out, 4)) ||
         (w_out && !aligned(w_out, 4)))
         return fail(MOE_ERR_INVALID_ARG, "misaligned pointer (x, y, blobs: 16 B; ws: 256 B)");
     const size_t need = moe_layer_workspace_bytes(desc, T);
     if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
     return run_layer(T, desc->n_experts, desc->top_k, desc->renormalize, desc->expert, desc->shared_ff, expert_table,
-                     nullptr, shared_blob, x, x_dtype, logits, y, ids_out, w_out, ws, ws_bytes, (hipStream_t)stream,
-                     false, marks);
+                     nullptr, shared_blob, x, x_dtype, routed ? nullptr : logits, opts, y, ids_out, w_out, ws,
+                     ws_bytes, (hipStream_t)stream, false, marks);
+}
+
+moe_status moe_layer_forward_ex(const moe_layer_desc* desc, const moe_layer_opts* opts,
+                                const void* const* expert_table, const void* shared_blob, const void* x,
+                                int32_t x_dtype, const float* logits, int32_t T, float* y, int32_t* ids_out,
+                                float* w_out, void* ws, size_t ws_bytes, void* stream) {
+    return layer_forward_checked(desc, expert_table, shared_blob, x, x_dtype, logits, T, y, ids_out, w_out, ws,
+                                 ws_bytes, stream, nullptr, opts);
+}
+
+moe_status moe_router_logits(const moe_router* router, int32_t E, int32_t H, const void* x, int32_t x_dtype,
+                             int32_t T, float* logits, void* stream) {
+    if (!router) return fail(MOE_ERR_INVALID_ARG, "router is NULL");
+    if (E < 1 || H < 32 || T < 0) return fail(MOE_ERR_INVALID_ARG, "E >= 1, H >= 32 and T >= 0 required");
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "unknown x_dtype %d", x_dtype);
+    moe_status st = check_router(router, H);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!x || !logits) return fail(MOE_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(x, 16) || !aligned(logits, 4)) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    hipError_t e = launch_router(router->weight, router->in_scale, router->norm, router->eps, E, H, x, x_dtype, T,
+                                 logits, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "router launch: %s", hipGetErrorString(e));
+    return MOE_OK;
 }
 
 moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expert_table, const void* shared_blob,

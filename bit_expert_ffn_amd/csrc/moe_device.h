@@ -110,6 +110,17 @@ __device__ __forceinline__ bool bounded_wait(F ready, long polls, int* err) {
     return true;
 }
 
+// The gate's activation of a gated expert FFN: SiLU (SwiGLU), or the tanh
+// form of GELU (GeGLU; kairos-engine README, "Decode, 2026-09-28/29").  Both
+// are v / (1 + e^(-b)): b = v for SiLU, and since (1 + tanh u) / 2 =
+// 1 / (1 + e^(-2u)), b = 2 sqrt(2/pi) (v + 0.044715 v^3) for GELU.
+constexpr int kActSilu = 0;
+constexpr int kActGeluTanh = 1;
+__device__ __forceinline__ float gate_arg(float v, int act) {
+    return act == kActGeluTanh ? 1.5957691216057308f * (v + 0.044715f * (v * v * v)) : v;
+}
+__device__ __forceinline__ float act_gate(float v, int act) { return v / (1.f + expf(-gate_arg(v, act))); }
+
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }

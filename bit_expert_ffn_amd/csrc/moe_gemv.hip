@@ -49,6 +49,10 @@ struct DecodeParams {
     int T, E, k, renorm, identity;
     int H, FF, FFs;
     float z;
+    int act;                     // gate activation (kActSilu / kActGeluTanh)
+    const float* down_scale;     // [E] per routed expert, or null
+    const int* ids_in;           // [T][k] caller-supplied routing, or null
+    const float* w_in;           // [T][k]
     int* ids_out;                // [T][k] or null
     float* w_out;                // [T][k] or null
     uint32_t* a;                 // [T*k][FF] packed bf16 hi | lo << 16, agent-coherent
@@ -79,7 +83,7 @@ struct RouteLDS {
     float w[kMaxK];
     int pair_tok[kMaxK], pair_exp[kMaxK], slot_pair[kMaxK];
     int group_first[kMaxK], group_n[kMaxK], group_of_pair[kMaxK];
-    int slot_src[kMaxK];   // slot j -> group * NT + token-in-group of its pair
+    int slot_src[kMaxK];   // slot j -> group * NT + token-in-group of its pair; -1: a skipped slot
     uint64_t topk[kGemvThreads / 64][128];   // each wave's top-k scratch
     int n_groups;
     int fail;              // this workgroup's output is NaN: an earlier failure, or one of its waits gave up
@@ -91,12 +95,42 @@ __device__ __forceinline__ const uint8_t* expert_blob(const DecodeParams& p, int
 }
 
 // Routing of the token: its k slots are its pairs and groups, in rank order
-// (group numbering changes no arithmetic).
+// (group numbering changes no arithmetic).  With caller-supplied routing
+// (Krasis white paper 7.5: a fixed top-k shape in which an omitted route is
+// a zero-weight slot), the slots of nonzero weight become the groups, in slot
+// order; a zero-weight slot has no group and its expert is never read.  A
+// nonzero weight on an id outside [0, E) flags kErrBadId and fails the call.
 __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k;
     const int prior = tid == 0 ? load_error(p.err) : 0;   // issued ahead of the logits
-    if (wv == 0) {
+    if (wv == 0 && p.ids_in) {
+        const int id = lane < k ? p.ids_in[lane] : 0;
+        const float wt = lane < k ? p.w_in[lane] : 0.f;
+        const bool on = lane < k && wt != 0.f;
+        const bool bad = on && (id < 0 || id >= p.E);
+        if (bad) flag_error(p.err, kErrBadId);
+        const uint64_t live = __ballot(on && !bad);
+        const int pos = lanes_below(live);
+        if (lane < k) {
+            R.id[lane] = id;
+            R.w[lane] = wt;
+            R.slot_src[lane] = (on && !bad) ? pos : -1;
+        }
+        if (on && !bad) {
+            R.slot_pair[pos] = pos;
+            R.pair_tok[pos] = 0;
+            R.pair_exp[pos] = id;
+            R.group_first[pos] = pos;
+            R.group_n[pos] = 1;
+            R.group_of_pair[pos] = pos;
+        }
+        const bool any_bad = __ballot(bad) != 0;   // every lane votes
+        if (lane == 0) {
+            R.n_groups = __popcll(live);
+            R.fail = prior != 0 || any_bad;
+        }
+    } else if (wv == 0) {
         int id = 0;
         float wt = 1.f;
         if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, R.topk[0], &id, &wt);
@@ -238,7 +272,7 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         if (f >= rows || t >= ntok) continue;
         const float g = sum_columns4(lds + ((0 * Rr + rr) * NT + t) * ncp, ncol);
         const float u = sum_columns4(lds + ((1 * Rr + rr) * NT + t) * ncp, ncol);
-        const float a = g / (1.f + expf(-g)) * u;
+        const float a = act_gate(g, p.act) * u;
         __hip_atomic_store(out + (size_t)outrow[t] * rows + f, pack_a(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // Every store above has completed (the barrier waits for them), so a flag
@@ -290,6 +324,9 @@ __device__ __forceinline__ uint32_t stage_src_off(int q, int routed_words, uint3
     return wd < routed_words ? 4u * (uint32_t)wd : as_off + 4u * (uint32_t)(wd - routed_words);
 }
 
+// Copies this call's `a` words: routed_words (the routed groups' rows) then
+// the shared expert's row; p.stage_words sizes the largest call (every slot a
+// group), and with caller-supplied routing fewer slots may have groups.
 template <int QK>
 __device__ __forceinline__ void stage_a(const DecodeParams& p, __amdgpu_buffer_rsrc_t rsrc, const uint8_t* a_base,
                                         uint32_t as_off, int routed_words, uint8_t* dst, int* fail) {
@@ -299,7 +336,7 @@ __device__ __forceinline__ void stage_a(const DecodeParams& p, __amdgpu_buffer_r
     // The addresses below are computed here, not hoisted to the start of the
     // caller (where holding them would spill registers).
     asm volatile("" : "+v"(lane));
-    const int n_chunks = p.stage_words / 4;
+    const int n_chunks = (routed_words + (p.shared ? p.T * p.FFs : 0)) / 4;
     // Pass j of wave wv fills LDS chunks [64 (4 j + wv), +64): lane i the i-th.
     // Positions past the last chunk (inside the last pass) take a copy of it.
 #pragma unroll
@@ -351,6 +388,23 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
     const int nb_s = p.FFs / QK;
     const int ng = R.n_groups;
     const int n_units = ng * nb_r + p.shared_groups * nb_s;
+    // Combine weight of slot j = tid % JS (the lane that adds slot j's term
+    // below): its routing weight times its expert's down scale, if any.
+    const int JS = p.k <= 16 ? 16 : 32;
+    float cw = 0.f;
+    {
+        const int j = tid % JS;
+        if (j < p.k && R.slot_src[j] >= 0)
+            cw = R.w[j] * (p.down_scale ? p.down_scale[R.id[j]] : 1.f);
+    }
+    if (n_units == 0) {
+        // Every slot skipped and no shared expert: y = 0.  Still counted as
+        // loaded, which the janitor waits for.
+        if (tid == 0) atomic_add_detached(sync_loaded(p.sync, tile % kLoadFan, p.max_groups + p.shared_groups), 1);
+        for (int i = tid; i < p.T * nrows; i += kGemvThreads)
+            p.y[(size_t)(i / nrows) * p.H + h0 + i % nrows] = R.fail ? __uint_as_float(0x7FC00000u) : 0.f;
+        return;
+    }
     // Units (group, block column); with few units, S threads split a unit's rows.
     int S = kGemvThreads / n_units;
     S = S < 1 ? 1 : (S > nrows ? nrows : S);
@@ -516,11 +570,11 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
     } else {
         lds_barrier();
     }
-    // y[t][h0 + r] = shared(t)[r] + sum over the token's k slots of w * d,
+    // y[t][h0 + r] = shared(t)[r] + sum over the token's k slots of cw * d,
     // where d (of the slot's group, row and token) is its block-column
     // partials summed in column order.  Lane j of a group of JS lanes takes
-    // slot j; the slot terms are summed by a fixed tree over the group.
-    const int JS = p.k <= 16 ? 16 : 32;
+    // slot j (0 for a skipped slot); the slot terms are summed by a fixed tree
+    // over the group.
     const int n_out = p.T * nrows;
     for (int base = 0; base < n_out; base += kGemvThreads / JS) {
         const int it = base + tid / JS, j = tid % JS;
@@ -529,8 +583,10 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
         float v = 0.f;
         if (live && j < p.k) {
             const int gs = R.slot_src[t * p.k + j];   // group * NT + token in group
-            const int gg = gs / NT, tt = gs - (gs / NT) * NT;
-            v = R.w[t * p.k + j] * sum_columns(part + ((gg * p.dn_rows + r) * NT + tt) * nbp_r, nb_r);
+            if (gs >= 0) {
+                const int gg = gs / NT, tt = gs - (gs / NT) * NT;
+                v = cw * sum_columns(part + ((gg * p.dn_rows + r) * NT + tt) * nbp_r, nb_r);
+            }
         }
         v = row_sum_f32(v);
         if (JS == 32) v += __shfl_xor(v, 16);
@@ -720,8 +776,8 @@ static hipError_t launch_decode_t(const GemvShape& g, DecodeParams& p, hipStream
 
 hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, const void* single, const void* shared,
                                const void* x, int x_dtype, const float* logits, int T, int E, int k, int renorm,
-                               int identity, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
-                               hipStream_t s, StageMarks* marks) {
+                               int identity, const LayerOpts& o, int* ids_out, float* w_out, const SmallLayout& L,
+                               char* ws, float* y, hipStream_t s, StageMarks* marks) {
     DecodeParams p{};
     p.table = table;
     p.single = (const uint8_t*)single;
@@ -737,6 +793,10 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
     p.FF = g.FF;
     p.FFs = g.FFs;
     p.z = g.z;
+    p.act = o.act;
+    p.down_scale = o.down_scale;
+    p.ids_in = o.ids_in;
+    p.w_in = o.w_in;
     p.ids_out = ids_out;
     p.w_out = w_out;
     p.a = (uint32_t*)(ws + L.a);

@@ -60,6 +60,7 @@ struct SmallLayout {
     size_t as;               // [T][FFs] the shared expert's
     size_t d;                // [8k + 8][H] verify windows: down output per slot, then per token of the shared expert
     size_t ids, w;           // [T][k] routing when the caller passes no output
+    size_t logits;           // [T][E] router output when the router runs inside the call
     size_t total;
 };
 
@@ -72,8 +73,17 @@ struct LargeLayout {
     size_t xq, xe;           // [2][T][H] fp16 activation planes (hi, lo); [T] power-of-two exponents
     size_t a;                // [rows][FFmax] bf16 hi plane, then the lo plane
     size_t ypair;            // [rows][H] fp32 down projection per sorted row
+    size_t logits;           // [T][E] router output when the router runs inside the call
     size_t max_tiles;
     size_t total;
+};
+
+// Options of a layer call beyond its descriptor (moe_layer_forward_ex).
+struct LayerOpts {
+    int act = 0;                       // 0 SwiGLU, 1 GeGLU (tanh GELU)
+    const float* down_scale = nullptr; // [E] per routed expert, or none
+    const int* ids_in = nullptr;       // [T][k] caller-supplied routing, or none (route from logits)
+    const float* w_in = nullptr;       // [T][k]; a zero weight skips its slot
 };
 
 struct GemvShape {
@@ -102,7 +112,7 @@ struct WindowShape {
 WindowShape window_shape(int H, int FF, int FFs, int qtype, int x_dtype, int T, int k);
 size_t window_sync_bytes(int k, int n_chunks);
 
-SmallLayout small_layout(int T, int k, int H, int FF, int FFs, int qtype);
+SmallLayout small_layout(int T, int k, int E, int H, int FF, int FFs, int qtype);
 size_t small_fixed_bytes(int k, int H, int FF, int FFs, int qtype);   // sync + a + as + d: where every layout's own regions start
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype);
 GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k);
@@ -128,17 +138,22 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renor
                              hipStream_t s);
 hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, const void* single, const void* shared,
                                const void* x, int x_dtype, const float* logits, int T, int E, int k, int renorm,
-                               int identity, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
-                               hipStream_t s, StageMarks* marks = nullptr);
+                               int identity, const LayerOpts& o, int* ids_out, float* w_out, const SmallLayout& L,
+                               char* ws, float* y, hipStream_t s, StageMarks* marks = nullptr);
 hipError_t launch_window_layer(const WindowShape& g, const void* const* table, const void* single,
                                const void* shared, const void* x, int x_dtype, const float* logits, int T, int E,
-                               int k, int renorm, int identity, int qtype, float z, int H, int FF, int FFs,
-                               int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y, hipStream_t s,
-                               StageMarks* marks = nullptr);
+                               int k, int renorm, int identity, const LayerOpts& o, int qtype, float z, int H, int FF,
+                               int FFs, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
+                               hipStream_t s, StageMarks* marks = nullptr);
 hipError_t launch_prefill_layer(const void* const* table, const void* single, const void* shared, int qtype, float z,
                                 int H, int FF, int FFs, const void* x, int x_dtype, const float* logits, int T, int E,
-                                int k, int renorm, int identity, int* ids_out, float* w_out, const LargeLayout& L,
-                                char* ws, float* y, hipStream_t s, StageMarks* marks = nullptr);
+                                int k, int renorm, int identity, const LayerOpts& o, int* ids_out, float* w_out,
+                                const LargeLayout& L, char* ws, float* y, hipStream_t s, StageMarks* marks = nullptr);
+// Router logits [T][E] = W_r x' (bf16 W_r [E][H]; x' = x, optionally through
+// the weightless RMS norm and a per-input-dim scale): one launch (a GEMV for
+// T <= kSmallT, a tiled GEMM above).
+hipError_t launch_router(const void* wr, const float* in_scale, int norm, float eps, int E, int H, const void* x,
+                         int x_dtype, int T, float* logits, hipStream_t s);
 hipError_t launch_dequant(const void* blob, int qtype, float z, int rows, int cols, size_t plane_offset,
                           float* out, hipStream_t s);
 

@@ -82,6 +82,7 @@ LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype)
     L.xe = take((size_t)T * 4);
     L.a = take(P * ffmax * 2 * 2 + 256); // a_hi then a_lo planes, bf16 (+ slack as for xq)
     L.ypair = take(P * (size_t)H * 4);
+    L.logits = take((size_t)T * E * 4);
     L.max_tiles = max_tiles;
     L.total = off;
     return L;
@@ -95,6 +96,9 @@ struct PrefillParams {
     int T, E, k, H, FF, FFs, ffmax;
     float z;
     uint32_t zc16;            // fp16 pair (-(1024 + 2z), -(1024 + 2z))
+    int act;                  // gate activation (kActSilu / kActGeluTanh)
+    int routed;               // caller-supplied routing: zero-weight pairs are skipped
+    const float* down_scale;  // [E] per routed expert, or null
     const int* ids;
     const float* w;
     int* counts;
@@ -113,6 +117,16 @@ struct PrefillParams {
     int max_tiles;
 };
 
+// A (token, slot) pair takes part: always with routing from logits; with
+// caller-supplied routing (Krasis white paper 7.5: an omitted route is a
+// zero-weight slot) when its weight is nonzero and its id in [0, E) (an id
+// outside it was flagged by prefill_routed_kernel and fails the call).
+__device__ __forceinline__ bool pair_on(const PrefillParams& p, int q) {
+    if (!p.routed) return true;
+    const int e = p.ids[q];
+    return p.w[q] != 0.f && e >= 0 && e < p.E;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Bucketing: counts, offsets, tile list (one workgroup).
 // ---------------------------------------------------------------------------------------------
@@ -123,7 +137,8 @@ __global__ void __launch_bounds__(1024) prefill_count_kernel(PrefillParams p) {
     const int n = p.T * p.k;
     for (int e = tid; e < p.E; e += blockDim.x) hist[e] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += blockDim.x) atomicAdd(&hist[p.ids[i]], 1);   // counts: order-free
+    for (int i = tid; i < n; i += blockDim.x)   // counts: order-free
+        if (pair_on(p, i)) atomicAdd(&hist[p.ids[i]], 1);
     __syncthreads();
     if (tid == 0) {
         int off = 0, tb = 0;
@@ -170,7 +185,7 @@ __global__ void __launch_bounds__(256) prefill_place_kernel(PrefillParams p) {
         int pos = p.offsets[e];
         for (int c = 0; c < n; c += 64) {
             const int q = c + lane;
-            const bool match = q < n && p.ids[q] == e;
+            const bool match = q < n && p.ids[q] == e && pair_on(p, q);
             const uint64_t m = __ballot(match);
             if (match) {
                 const int r = pos + __popcll(m & ((1ull << lane) - 1));
@@ -182,6 +197,21 @@ __global__ void __launch_bounds__(256) prefill_place_kernel(PrefillParams p) {
     }
     if (p.shared)
         for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < p.T; t += gridDim.x * blockDim.x) p.perm[n + t] = t;
+}
+
+// Caller-supplied routing: copied to the routing buffers the later stages
+// read (and the caller's optional outputs); a nonzero weight on an id outside
+// [0, E) flags kErrBadId in the workspace's error word, so the combine writes
+// NaN.
+__global__ void prefill_routed_kernel(const int* ids_in, const float* w_in, int n, int E, int* ids, float* w,
+                                      int* err) {
+    const int q = blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n) return;
+    const int e = ids_in[q];
+    const float wt = w_in[q];
+    ids[q] = e;
+    w[q] = wt;
+    if (wt != 0.f && (e < 0 || e >= E)) flag_error(err, kErrBadId);
 }
 
 // Identity routing for one expert's FFN: every token, expert 0, weight 1.
@@ -555,8 +585,10 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
                     if (rr < nrows) {
                         const float g = __builtin_ldexpf(accg[r][k], ex[r][k]);
                         const float u = __builtin_ldexpf(accu[r][k], ex[r][k]);
-                        // silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (~1 ulp each)
-                        const float a = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * g)) * u;
+                        // act(g) = g / (1 + e^-b) (b = g for SiLU; see gate_arg) with the
+                        // hardware exp2 and reciprocal (~1 ulp each)
+                        const float a = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f *
+                                                                                               gate_arg(g, p.act))) * u;
                         const uint32_t ah = f32_to_bf16_rne(a);
                         const uint32_t al = f32_to_bf16_rne(a - __uint_as_float(ah << 16));
                         const size_t o = (size_t)(row0 + rr) * p.ffmax + fo;
@@ -752,7 +784,8 @@ __global__ void __launch_bounds__(256) prefill_combine_kernel(PrefillParams p) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.shared) acc = *reinterpret_cast<const float4*>(p.ypair + (size_t)(p.T * p.k + t) * p.H + h);
     for (int j = 0; j < p.k; ++j) {
-        const float wt = p.w[t * p.k + j];
+        if (!pair_on(p, t * p.k + j)) continue;
+        const float wt = p.w[t * p.k + j] * (p.down_scale ? p.down_scale[p.ids[t * p.k + j]] : 1.f);
         const float4 v = *reinterpret_cast<const float4*>(p.ypair + (size_t)p.inv[t * p.k + j] * p.H + h);
         acc.x = __builtin_fmaf(wt, v.x, acc.x);
         acc.y = __builtin_fmaf(wt, v.y, acc.y);
@@ -786,8 +819,8 @@ static void launch_gemms(const PrefillParams& p, int x_dtype, hipStream_t s, Sta
 
 hipError_t launch_prefill_layer(const void* const* table, const void* single, const void* shared, int qtype, float z,
                                 int H, int FF, int FFs, const void* x, int x_dtype, const float* logits, int T, int E,
-                                int k, int renorm, int identity, int* ids_out, float* w_out, const LargeLayout& L,
-                                char* ws, float* y, hipStream_t s, StageMarks* marks) {
+                                int k, int renorm, int identity, const LayerOpts& o, int* ids_out, float* w_out,
+                                const LargeLayout& L, char* ws, float* y, hipStream_t s, StageMarks* marks) {
     PrefillParams p{};
     p.table = table;
     p.single = (const uint8_t*)single;
@@ -806,6 +839,9 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     int* ids = ids_out ? ids_out : (int*)(ws + L.ids);
     float* w = w_out ? w_out : (float*)(ws + L.w);
     p.ids = ids;
+    p.act = o.act;
+    p.routed = o.ids_in != nullptr;
+    p.down_scale = o.down_scale;
     p.w = w;
     p.counts = (int*)(ws + L.counts);
     p.offsets = (int*)(ws + L.offsets);
@@ -826,6 +862,9 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     stage_mark(marks, s);
     if (identity)
         hipLaunchKernelGGL(prefill_identity_kernel, dim3((T + 255) / 256), dim3(256), 0, s, ids, w, T);
+    else if (o.ids_in)
+        hipLaunchKernelGGL(prefill_routed_kernel, dim3((T * k + 255) / 256), dim3(256), 0, s, o.ids_in, o.w_in, T * k,
+                           E, ids, w, (int*)ws + kErrWord);
     else
         (void)launch_route_topk(logits, T, E, k, renorm, ids, w, s);
     stage_mark(marks, s);

@@ -76,6 +76,10 @@ struct WindowParams {
     int T, E, k, renorm, identity;
     int H, FF, FFs;
     float z;
+    int act;                    // gate activation (kActSilu / kActGeluTanh)
+    const float* down_scale;    // [E] per routed expert, or null
+    const int* ids_in;          // [T][k] caller-supplied routing, or null
+    const float* w_in;          // [T][k]
     int* ids_out;               // [T][k] or null
     float* w_out;               // [T][k] or null
     uint32_t* a;                // [T*k][FF] by sorted pair (expert, token), packed bf16 hi | lo << 16
@@ -107,6 +111,8 @@ __device__ __forceinline__ int* win_combined(int* s, int k, int n_chunks, int c)
 struct WinLDS {
     int id[kWinPairs];
     float w[kWinPairs];
+    float cw[kWinPairs];            // combine weight: w times the expert's down scale; 0 for a skipped slot
+    int on[kWinPairs];              // the slot has a group (not skipped)
     alignas(16) int key[kWinPairs + 4];   // expert << 8 | slot, padded with INT_MAX
     int sorted[kWinPairs];          // sorted position -> slot
     int group_first[kWinPairs + 1]; // first sorted position of each group; [n_groups] = T * k
@@ -147,25 +153,44 @@ __device__ __forceinline__ void gu_tiling(const WindowParams& p, WinLDS& R, int 
 
 // Routing of the T tokens (wave w takes tokens w and w + 4), then the groups:
 // pairs sorted by (expert, token), each run of one expert cut into groups of
-// at most kWinGroup pairs.
+// at most kWinGroup pairs.  With caller-supplied routing (Krasis white paper
+// 7.5), zero-weight slots sort after every other pair and get no group, so
+// their experts are never read; a nonzero weight on an id outside [0, E)
+// flags kErrBadId and fails the call.
 // `scratch` is the dynamic LDS, free until the roles start (128 keys per wave).
 __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, uint64_t* scratch, int P_gu) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k, n = p.T * k;
     const int prior = tid == 0 ? load_error(p.err) : 0;   // issued ahead of the logits
+    bool bad_any = false;
     for (int t = wv; t < p.T; t += kGemvThreads / 64) {
         int id = 0;
         float wt = 1.f;
-        if (!p.identity) wave_topk(p.logits + (size_t)t * p.E, p.E, k, p.renorm, lane, scratch + 128 * wv, &id, &wt);
+        bool on = true;
+        if (p.ids_in) {
+            id = lane < k ? p.ids_in[t * k + lane] : 0;
+            wt = lane < k ? p.w_in[t * k + lane] : 0.f;
+            on = wt != 0.f;
+            const bool bad = lane < k && on && (id < 0 || id >= p.E);
+            if (bad) flag_error(p.err, kErrBadId);
+            bad_any |= __ballot(bad) != 0;
+            on = on && !bad;
+        } else if (!p.identity) {
+            wave_topk(p.logits + (size_t)t * p.E, p.E, k, p.renorm, lane, scratch + 128 * wv, &id, &wt);
+        }
         if (lane < k) {
             R.id[t * k + lane] = id;
             R.w[t * k + lane] = wt;
-            R.key[t * k + lane] = id << 8 | (t * k + lane);
+            R.cw[t * k + lane] = on ? wt * (p.down_scale ? p.down_scale[id] : 1.f) : 0.f;
+            R.on[t * k + lane] = on;
+            // skipped slots sort after every pair (ids are below 2^10)
+            R.key[t * k + lane] = on ? (id << 8 | (t * k + lane)) : (0x7F000000 | (t * k + lane));
         }
     }
     if (tid < 4) R.key[n + tid] = 0x7FFFFFFF;
     if (tid == 0) R.fail = prior != 0;
     __syncthreads();
+    if (bad_any && lane == 0) R.fail = 1;
     // Keys are distinct (a token selects an expert at most once), so each
     // pair's count of smaller keys is its sorted position.
     if (tid < n) {
@@ -179,15 +204,19 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
     }
     __syncthreads();
     if (wv == 0) {
+        // The pairs with a group: all of them, or those of nonzero weight
+        // (sorted first).
+        int na = 0;
+        for (int r0 = 0; r0 < n; r0 += 64) na += __popcll(__ballot(r0 + lane < n && R.on[r0 + lane]));
         // A group starts at every kWinGroup-th pair of a run of one expert.
         int base = 0, carry = 0;   // carry: the run start in effect at the end of the previous 64 pairs
-        for (int r0 = 0; r0 < n; r0 += 64) {
+        for (int r0 = 0; r0 < na; r0 += 64) {
             const int r = r0 + lane;
-            const bool run_start = r < n && (r == 0 || R.id[R.sorted[r - 1]] != R.id[R.sorted[r]]);
+            const bool run_start = r < na && (r == 0 || R.id[R.sorted[r - 1]] != R.id[R.sorted[r]]);
             const uint64_t m = __ballot(run_start);
             const uint64_t upto = m & (lane == 63 ? ~0ull : ((2ull << lane) - 1));
             const int rs = upto ? r0 + 63 - __clzll(upto) : carry;
-            const bool start = r < n && (r - rs) % kWinGroup == 0;
+            const bool start = r < na && (r - rs) % kWinGroup == 0;
             const uint64_t gm = __ballot(start);
             if (start) R.group_first[base + lanes_below(gm)] = r;
             base += __popcll(gm);
@@ -195,7 +224,7 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
         }
         if (lane == 0) {
             R.n_groups = base;
-            R.group_first[base] = n;
+            R.group_first[base] = na;
         }
         __builtin_amdgcn_wave_barrier();
         // Work order: the groups with kWinGroup tokens (the heaviest items)
@@ -355,7 +384,7 @@ __device__ __forceinline__ void gu_compute(const WindowParams& p, const WinLDS& 
             if (f >= it.rows || t >= nt) continue;
             const float gv = sum_columns4(lds + ((0 * Rr + rr) * 2 + t) * ncp, ncol);
             const float uv = sum_columns4(lds + ((1 * Rr + rr) * 2 + t) * ncp, ncol);
-            const float av = gv / (1.f + expf(-gv)) * uv;
+            const float av = act_gate(gv, p.act) * uv;
             const int orow = it.first + t0 + t;   // routed: sorted pair; shared: token
             __hip_atomic_store(it.out + (size_t)orow * it.rows + f, pack_a(av), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -494,17 +523,21 @@ __device__ __forceinline__ float pairwise_sum(const float* v) {
     else return pairwise_sum<N / 2>(v) + pairwise_sum<N / 2>(v + N / 2);
 }
 
-// Sum over slots [j0, j0 + 16) of w[t][j] * d[t * k + j] for 4 consecutive
-// rows h.. (0 past k), pairwise in slot order; all 16 loads in flight
-// together, then one check (a word still 0 is read again).
+// Sum over slots [j0, j0 + 16) of cw[t][j] * d[t * k + j] for 4 consecutive
+// rows h.. (0 past k and for a skipped slot, whose d is never written),
+// pairwise in slot order; all 16 loads in flight together, then one check (a
+// word still 0 is read again).
 __device__ __forceinline__ void slot_sums16(const WindowParams& p, const WinLDS& R, __amdgpu_buffer_rsrc_t rsrc, int t,
                                             int h, int j0, float (&out)[4]) {
     const int k = p.k;
     win_u32x4 raw[16];
+    bool on[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
+        on[j] = j0 + j < k && R.on[t * k + j0 + j];
         const int jj = j0 + j < k ? j0 + j : 0;   // past k: slot 0 again, unused
         raw[j] = load_coherent4(rsrc, 4u * (uint32_t)((t * k + jj) * p.H + h));
+        if (!on[j]) raw[j] = win_u32x4{1u, 1u, 1u, 1u};
     }
     uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
@@ -512,14 +545,14 @@ __device__ __forceinline__ void slot_sums16(const WindowParams& p, const WinLDS&
     if (m == 0u) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-            if (j0 + j < k && min4(raw[j]) == 0u)
+            if (on[j] && min4(raw[j]) == 0u)
                 raw[j] = reload_published4(p, rsrc, 4u * (uint32_t)((t * k + j0 + j) * p.H + h));
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         float v[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = j0 + j < k ? R.w[t * k + j0 + j] * __uint_as_float(raw[j][e]) : 0.f;
+        for (int j = 0; j < 16; ++j) v[j] = on[j] ? R.cw[t * k + j0 + j] * __uint_as_float(raw[j][e]) : 0.f;
         out[e] = pairwise_sum<16>(v);
     }
 }
@@ -1017,9 +1050,9 @@ static hipError_t window_grid(const WindowShape& g, int qtype, int x_dtype, int*
 
 hipError_t launch_window_layer(const WindowShape& g, const void* const* table, const void* single,
                                const void* shared, const void* x, int x_dtype, const float* logits, int T, int E,
-                               int k, int renorm, int identity, int qtype, float z, int H, int FF, int FFs,
-                               int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y, hipStream_t s,
-                               StageMarks* marks) {
+                               int k, int renorm, int identity, const LayerOpts& o, int qtype, float z, int H, int FF,
+                               int FFs, int* ids_out, float* w_out, const SmallLayout& L, char* ws, float* y,
+                               hipStream_t s, StageMarks* marks) {
     WindowParams p{};
     p.table = table;
     p.single = (const uint8_t*)single;
@@ -1035,6 +1068,10 @@ hipError_t launch_window_layer(const WindowShape& g, const void* const* table, c
     p.FF = FF;
     p.FFs = FFs;
     p.z = z;
+    p.act = o.act;
+    p.down_scale = o.down_scale;
+    p.ids_in = o.ids_in;
+    p.w_in = o.w_in;
     p.ids_out = ids_out;
     p.w_out = w_out;
     p.a = (uint32_t*)(ws + L.a);

@@ -85,8 +85,13 @@ typedef enum { MOE_Q2_64 = 1, MOE_Q4_32 = 2 } moe_qtype;
 /* Activation dtypes: fp32, or bfloat16 stored as raw 16-bit words. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
-/* Gated activation of an expert: SwiGLU, a = silu(gate x) * (up x). */
-typedef enum { MOE_ACT_SWIGLU = 0 } moe_act;
+/* Gated activation of an expert (routed and shared alike):
+ *   MOE_ACT_SWIGLU     a = silu(gate x) * (up x), silu(v) = v / (1 + e^-v);
+ *   MOE_ACT_GEGLU_TANH a = gelu(gate x) * (up x) with the tanh form
+ *                      gelu(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+ *                      (kairos-engine README, "Decode, 2026-09-28/29": the
+ *                      Gemma model's GELU is the tanh form). */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GEGLU_TANH = 1 } moe_act;
 
 typedef struct {
     int32_t hidden;      /* H: model width = input and output length */
@@ -170,6 +175,65 @@ moe_status moe_expert_ffn(const moe_expert_desc* desc, const void* blob, const v
 moe_status moe_layer_forward(const moe_layer_desc* desc, const void* const* expert_table, const void* shared_blob,
                              const void* x, int32_t x_dtype, const float* logits, int32_t T, float* y,
                              int32_t* ids_out, float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Router front end (kairos-engine README, "The MoE forward": normalise, run the
+ * router GEMM to get the logits, take the top-k; the router reads its input
+ * through its own weightless norm, and its scale is per input dimension):
+ *   logits[t][e] = sum_h W[e][h] x'[t][h],  x' = x, or x / sqrt(mean_h x^2 + eps)
+ *   when norm = 1, then times in_scale[h] when in_scale is not NULL.
+ * W is bf16 [E][H] (raw 16-bit words); products and sums in fp32.  For T <= 8
+ * a token's logits are bitwise independent of the other tokens.
+ */
+typedef struct {
+    const void* weight;      /* [E][H] bf16 router weights, device, 16-byte aligned */
+    const float* in_scale;   /* [H] fp32 per-input-dim scale, device, 16-byte aligned; or NULL */
+    int32_t norm;            /* 1: weightless RMS norm of x first; 0: none */
+    float eps;               /* the norm's epsilon (>= 0) */
+} moe_router;
+
+/*
+ * The router alone: logits [T][E] fp32 (device) from x [T][H] (x_dtype).
+ * H must be a multiple of 32.  No workspace.
+ */
+moe_status moe_router_logits(const moe_router* router, int32_t E, int32_t H, const void* x, int32_t x_dtype,
+                             int32_t T, float* logits, void* stream);
+
+/*
+ * Options of moe_layer_forward_ex; a NULL options pointer, or all fields NULL,
+ * is moe_layer_forward.
+ *   router     : the logits are computed from x by the router above, inside the
+ *                call (one more launch before the layer's); `logits` must then be
+ *                NULL.  They go to logits_out [T][E] if given, else to the
+ *                workspace.
+ *   down_scale : [E] fp32 per routed expert: expert e's output is
+ *                down_scale[e] * (W_down a) (kairos-engine README, "The MoE
+ *                forward": the down projection's scale is per expert).  The
+ *                shared expert is not scaled.  In the combine the weight and the
+ *                scale are multiplied first: (w_j * s_e) * (W_down a).
+ *   ids_in, w_in: [T][k] routing supplied by the caller instead of logits (a
+ *                fixed top-k shape: Krasis white paper 7.5, "Preserving the native
+ *                execution shape").  A slot whose weight is exactly 0 (+0 or -0)
+ *                is skipped: its expert is never read and its id may be anything
+ *                (a dummy).  A nonzero weight on an id outside [0, E) is an error:
+ *                the call's outputs are NaN and moe_workspace_check reports it
+ *                (cause bit 2).  Weights are used as given (not renormalised).
+ *                Exclusive with router; `logits` is ignored.
+ * The activation is the descriptor's `act`.  All pointers are device pointers,
+ * 4-byte aligned.
+ */
+typedef struct {
+    const moe_router* router;
+    float* logits_out;
+    const float* down_scale;
+    const int32_t* ids_in;
+    const float* w_in;
+} moe_layer_opts;
+
+moe_status moe_layer_forward_ex(const moe_layer_desc* desc, const moe_layer_opts* opts,
+                                const void* const* expert_table, const void* shared_blob, const void* x,
+                                int32_t x_dtype, const float* logits, int32_t T, float* y, int32_t* ids_out,
+                                float* w_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Measurement variant of moe_layer_forward: the same checks and the same work,

@@ -79,3 +79,22 @@ def max_err_over_rms(got, ref):
     ref = np.asarray(ref, dtype=np.float64)
     rms = np.sqrt(np.mean(ref * ref))
     return float(np.max(np.abs(got - ref)) / rms) if rms > 0 else float(np.max(np.abs(got - ref)))
+
+
+def bf16_bits_array(v):
+    """Round float values to bf16 (nearest-even) and return the raw 16-bit words."""
+    f = np.ascontiguousarray(v, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def router_error_bound(wr_bits, xp):
+    """A priori bound on the fp32 router logits' error against float64: with
+    n = H products summed in fp32 (each FMA rounds once, relative 2^-24), plus
+    the few roundings that form x' (norm factor, scale), the error of a logit is
+    at most (H + 16) * 2^-24 * sum_h |W[e][h] x'[t][h]| (the recursive-summation
+    bound gamma_n, Higham, Accuracy and Stability of Numerical Algorithms, 2002,
+    ch. 3).  xp: the exact x' (float64) [T][H]."""
+    W = (np.asarray(wr_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    H = W.shape[1]
+    return (H + 16) * 2.0 ** -24 * (np.abs(xp) @ np.abs(W).T)

@@ -153,3 +153,38 @@ def test_workspace_check_rejects_bad_arguments(L):
     assert L.moe_workspace_check(ctypes.byref(d), ctypes.c_void_p(FAKE), 256, None) == 3            # too small
     assert L.moe_workspace_check(None, ctypes.c_void_p(FAKE), 1 << 20, None) == 1
     L.moe_debug_set_wait_limit(-1)     # host-side state only
+
+
+def test_layer_options_and_router_reject_bad_arguments(L):
+    """Host checks of moe_layer_forward_ex's options and of moe_router_logits."""
+    p = ctypes.c_void_p(FAKE)
+    d = moe.layer_desc(2560, 640, 1, 1.5, 512, 10)
+    rt = moe.Router(FAKE, None, 1, 1e-6)
+
+    def ex(opts, logits=p, T=1, desc=d):
+        return L.moe_layer_forward_ex(ctypes.byref(desc), ctypes.byref(opts) if opts is not None else None, p, None,
+                                      p, 1, logits, T, p, None, None, p, 1 << 30, None)
+
+    O = moe.LayerOpts
+    assert ex(O(ctypes.pointer(rt), None, None, FAKE, FAKE), logits=None) == 1   # router and ids_in together
+    assert ex(O(None, None, None, FAKE, None)) == 1                               # ids_in without w_in
+    assert ex(O(ctypes.pointer(rt), None, None, None, None)) == 1                 # router with logits given
+    assert ex(O(None, FAKE, None, None, None)) == 1                               # logits_out without router
+    assert ex(None, logits=None) == 1                                             # nothing to route from
+    assert ex(O(None, None, FAKE + 2, None, None)) == 1                           # misaligned down_scale
+    bad = moe.Router(FAKE, None, 2, 1e-6)
+    assert ex(O(ctypes.pointer(bad), None, None, None, None), logits=None) == 1   # norm not 0/1
+    bad = moe.Router(FAKE, None, 1, -1.0)
+    assert ex(O(ctypes.pointer(bad), None, None, None, None), logits=None) == 1   # negative eps
+    gelu = moe.layer_desc(2560, 640, 1, 1.5, 512, 10, act=moe.ACT_GEGLU_TANH)
+    assert L.moe_layer_workspace_bytes(ctypes.byref(gelu), 1) > 0                 # GeGLU is a known activation
+    assert ex(O(None, None, None, FAKE, FAKE), T=0) == 0                          # nothing to do
+    f = L.moe_router_logits
+    assert f(ctypes.byref(rt), 512, 2560, p, 1, 0, p, None) == 0                  # T = 0
+    assert f(ctypes.byref(rt), 512, 2568, p, 1, 1, p, None) == 1                  # H not a multiple of 32
+    assert f(None, 512, 2560, p, 1, 1, p, None) == 1
+    assert f(ctypes.byref(moe.Router(FAKE + 8, None, 0, 0.0)), 512, 2560, p, 1, 1, p, None) == 1   # misaligned W
+    assert f(ctypes.byref(rt), 512, 2560, p, 7, 1, p, None) == 1                  # unknown x dtype
+    d3 = moe.layer_desc(2560, 640, 1, 1.5, 512, 10)
+    d3.expert.act = 2
+    assert ex(None, desc=d3) == 2                                                 # unknown activation
