@@ -160,6 +160,51 @@ def cpu_baseline(w, x_host, l_host, budget_s=12.0):
             "host": host_cores()}, ref
 
 
+def router_timing(args, w, arena, x_step, desc, ws, stream, n_layers, eager_layer_ms):
+    """The router front end's added time at this workload (the logits are
+    otherwise an input): synthetic bf16 router weights N(0, 0.02) per layer
+    (the Gemma-shaped workload also runs the weightless norm and a
+    per-input-dim scale); HIP events on the launch stream around (a) the router
+    alone and (b) the layer call with the router inside it, eagerly per layer,
+    three passes.  The eager layer without the router is `eager_layer_ms`."""
+    import torch
+
+    import bit_expert_ffn_amd as moe
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    wr = [(torch.randn((w.experts, w.hidden), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+          for _ in range(n_layers)]
+    gemma = w.shared_ff > 0
+    scale = torch.rand((w.hidden,), generator=gen, device="cuda") + 0.5 if gemma else None
+    rts = [moe.router(wr[l], scale, norm=gemma, eps=1e-6) for l in range(n_layers)]
+    lg = torch.empty((w.tokens, w.experts), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.tokens, w.hidden), dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_layers)]
+    t_router, t_layer = [], []
+    for rep in range(4):
+        for which in ("router", "layer"):
+            with torch.cuda.stream(stream):
+                for l in range(n_layers):
+                    evs[l][0].record(stream)
+                    if which == "router":
+                        moe.router_logits(rts[l], w.experts, x_step[l], logits=lg, stream=stream)
+                    else:
+                        moe.layer_forward_ex(desc, arena.tables[l], x_step[l], shared=arena.shared_blob(l), rt=rts[l],
+                                             y=y, ws=ws, stream=stream)
+                    evs[l][1].record(stream)
+            torch.cuda.synchronize()
+            if rep > 0:   # the first pass warms up
+                (t_router if which == "router" else t_layer).extend(a.elapsed_time(b) for a, b in evs)
+    r_us, l_us = float(np.mean(t_router)) * 1e3, float(np.mean(t_layer)) * 1e3
+    r_bytes = w.experts * w.hidden * 2 + w.tokens * w.hidden * (2 if w.x_dtype == "bf16" else 4) + \
+        w.tokens * w.experts * 4 + (w.hidden * 4 if gemma else 0)
+    return {"kernel": "router_gemv_kernel", "options": "weightless RMS norm + per-input-dim scale" if gemma
+            else "plain", "router_us": round(r_us, 3), "router_bytes": int(r_bytes),
+            "router_gbps": round(r_bytes / (r_us * 1e-6) / 1e9, 1),
+            "layer_with_router_us": round(l_us, 3), "layer_eager_us": round(eager_layer_ms * 1e3, 3),
+            "added_us_per_layer": round(l_us - eager_layer_ms * 1e3, 3),
+            "timing": "eager, HIP events per call on the launch stream, 3 passes x all layers"}
+
+
 def prefill_flops(w, n_slots, T):
     """Algorithmic flops of one layer's two grouped GEMM stages: gate and up are
     2 x (H x FF) multiply-adds per routed slot, down one more (plus the shared
@@ -543,6 +588,7 @@ def main():
         torch.cuda.synchronize()
         durs += [a.elapsed_time(b) for a, b in evs]
     eager_layer_ms = float(np.mean(durs))
+    router = router_timing(args, w, arena, xs[W], desc, ws, stream, n_ev, eager_layer_ms)
 
     result = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -560,6 +606,7 @@ def main():
                      "launch_us": round(layer_ms * 1e3, 3),
                      "bytes_per_launch": int(bytes_layer), "eager_launch_us": round(eager_layer_ms * 1e3, 3)},
         "wall_s": round(t_wall, 4),
+        "router": router,
         "repeats": args.repeats, "median_ms_per_step": round(ms_step, 5),
         "min_ms_per_step": round(min(reps_ms) / K, 5),
         "max_tokens_per_s": round(K * w.tokens / (min(reps_ms) / 1e3), 2),

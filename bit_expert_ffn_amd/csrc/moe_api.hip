@@ -245,7 +245,7 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
                                         identity ? 1 : 0, o, ids_out, w_out, L, wsb, y, s, marks);
         } else {
             const WindowShape g = window_shape(ed.hidden, ed.ff, FFs, ed.qtype, x_dtype, T, k);
-            if (g.lds_bytes > 150 * 1024)
+            if (g.lds_bytes > 148 * 1024)
                 return fail(MOE_ERR_UNSUPPORTED, "verify window needs %zu bytes of LDS", g.lds_bytes);
             e = run_router(L.logits);
             if (e == hipSuccess)

@@ -29,9 +29,11 @@ namespace moe {
 //
 // Failures.  A bounded wait that gives up ORs kErrTimeout into the
 // workspace's error word, and the down workgroup it belongs to writes NaN
-// into its output rows.  A call that finds the error word already set (a
-// failure that moe_workspace_check has not cleared) writes NaN into every
-// output row and does no other work.
+// into its output rows.  The down and janitor workgroups read the error word
+// before their first wait (not earlier: an agent-coherent load in flight
+// holds every barrier of its workgroup): if a failure that
+// moe_workspace_check has not cleared is there, they write NaN rows and do
+// nothing else, so no wait runs on stale shared state.
 // ---------------------------------------------------------------------------------------------
 constexpr size_t kDecodeLdsBudget = 112 * 1024;   // dynamic LDS of the fused decode kernel
 constexpr int kMaxRowsDn = 12;               // H rows per down workgroup
@@ -87,12 +89,8 @@ struct RouteLDS {
     uint64_t topk[kGemvThreads / 64][128];   // each wave's top-k scratch
     int n_groups;
     int fail;              // this workgroup's output is NaN: an earlier failure, or one of its waits gave up
+    int bad;               // a caller-supplied id outside [0, E) with a nonzero weight
 };
-
-// Expert e's blob from the device table (a global load of one pointer).
-__device__ __forceinline__ const uint8_t* expert_blob(const DecodeParams& p, int e) {
-    return (const uint8_t*)((const __attribute__((address_space(1))) uint64_t*)p.table)[e];
-}
 
 // Routing of the token: its k slots are its pairs and groups, in rank order
 // (group numbering changes no arithmetic).  With caller-supplied routing
@@ -103,7 +101,7 @@ __device__ __forceinline__ const uint8_t* expert_blob(const DecodeParams& p, int
 __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k;
-    const int prior = tid == 0 ? load_error(p.err) : 0;   // issued ahead of the logits
+    if (tid == 0) R.fail = 0;
     if (wv == 0 && p.ids_in) {
         const int id = lane < k ? p.ids_in[lane] : 0;
         const float wt = lane < k ? p.w_in[lane] : 0.f;
@@ -128,7 +126,7 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
         const bool any_bad = __ballot(bad) != 0;   // every lane votes
         if (lane == 0) {
             R.n_groups = __popcll(live);
-            R.fail = prior != 0 || any_bad;
+            R.bad = any_bad;
         }
     } else if (wv == 0) {
         int id = 0;
@@ -147,7 +145,7 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
         }
         if (lane == 0) {
             R.n_groups = k;
-            R.fail = prior != 0;
+            R.bad = 0;
         }
     }
     __syncthreads();
@@ -167,7 +165,7 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         grp = g;
         const int first = R.group_first[g];
         ntok = R.group_n[g];
-        blob = p.table ? expert_blob(p, R.pair_exp[first]) : p.single;
+        blob = p.table ? table_blob(p.table, R.pair_exp[first]) : p.single;
         rows = p.FF;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -401,8 +399,9 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
         // Every slot skipped and no shared expert: y = 0.  Still counted as
         // loaded, which the janitor waits for.
         if (tid == 0) atomic_add_detached(sync_loaded(p.sync, tile % kLoadFan, p.max_groups + p.shared_groups), 1);
+        const bool failed = load_error(p.err) != 0;   // an unchecked earlier failure
         for (int i = tid; i < p.T * nrows; i += kGemvThreads)
-            p.y[(size_t)(i / nrows) * p.H + h0 + i % nrows] = R.fail ? __uint_as_float(0x7FC00000u) : 0.f;
+            p.y[(size_t)(i / nrows) * p.H + h0 + i % nrows] = failed ? __uint_as_float(0x7FC00000u) : 0.f;
         return;
     }
     // Units (group, block column); with few units, S threads split a unit's rows.
@@ -449,7 +448,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
             nb = nb_r;
             const int first = R.group_first[g];
             ntok = R.group_n[g];
-            dcode = (p.table ? expert_blob(p, R.pair_exp[first]) : p.single) + gu_r;
+            dcode = (p.table ? table_blob(p.table, R.pair_exp[first]) : p.single) + gu_r;
         } else {
             const int us = u - ng * nb_r;
             g = us / nb_s;            // shared group
@@ -471,6 +470,14 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
             sc[i] = ldg_u16(dscale + blk * 2);
         }
         if (!waited) {
+            // The error word, loaded behind this unit's weights (whose arrival
+            // the first poll below waits for anyway): an unchecked earlier
+            // failure means NaN rows, and no wait on the stale state.
+            if (load_error(p.err) != 0) {
+                for (int i = tid; i < p.T * nrows; i += kGemvThreads)
+                    p.y[(size_t)(i / nrows) * p.H + h0 + i % nrows] = __uint_as_float(0x7FC00000u);
+                return;
+            }
             // Thread g of the first wave watches group g's ready flag (routed
             // groups, then shared groups) in this workgroup's replica; the wave
             // continues when all are raised.
@@ -610,6 +617,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
 template <int NT>
 __device__ void janitor_role(const DecodeParams& p, RouteLDS& R) {
     const int tid = threadIdx.x;
+    if (load_error(p.err) != 0) return;   // an unchecked earlier failure: the state stays as it is
     const int ng = R.n_groups, nsg = p.shared_groups, n_ctr = p.max_groups + p.shared_groups;
     // Every ready flag of every replica, and every replica's prefetch hint at
     // its full count (one per group).
@@ -671,9 +679,9 @@ __global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodePar
             if (p.w_out) p.w_out[q] = R.w[q];
         }
     }
-    if (R.fail) {
-        // The workspace holds an unchecked failure: its shared state may be
-        // stale, so nothing is computed; the down workgroups write NaN rows.
+    if (R.bad) {
+        // Invalid caller-supplied routing: nothing is computed; the down
+        // workgroups write NaN rows.
         if (wg >= p.n_gu && wg - p.n_gu < p.tiles_dn) {
             const int h0 = (wg - p.n_gu) * p.dn_rows, nrows = min(p.dn_rows, p.H - h0);
             for (int i = tid; i < p.T * nrows; i += kGemvThreads)

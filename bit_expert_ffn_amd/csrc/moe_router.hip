@@ -7,15 +7,18 @@
 // in fp32.
 //
 // T <= 8 (decode, verify windows): router_gemv_kernel, one wave per expert
-// row (4 per workgroup).  Each workgroup first computes the norm factor of
-// every token (one wave per token, a fixed-order sum).  Lane l reads the
-// 16-byte chunks l, l + 64, ... of the weight row (coalesced) and the same
-// chunks of each token's row; per token it accumulates in that order and a
-// fixed DPP tree sums the lanes.  A token's logits are therefore bitwise the
-// same whatever the other tokens of the window.
+// row (4 per workgroup), a workgroup per 4 experts and tile of tokens.  Each
+// lane issues the loads of all its 16-byte chunks of the weight row (chunks
+// l, l + 64, ...) at once, while the workgroup copies the tile's activation
+// rows (and the scale) into LDS; then, per token, the lane accumulates
+// w * (x * scale) over its chunks in order, and, for the norm, x * x; a fixed
+// DPP tree sums the lanes, and the norm factor 1 / sqrt(mean x^2 + eps)
+// multiplies the sum (a per-token scalar: W (x r s) = r W (x s)).  A token's
+// logits are therefore bitwise the same whatever the other tokens of the
+// window, and a call waits for one round trip to memory.
 // T > 8 (prefill): router_gemm_kernel computes 64 x 64 tiles of (tokens x
 // experts) from 32-wide slices of x' and W_r staged in LDS; each tile first
-// computes its tokens' norm factors (one wave per token, the same arithmetic).
+// computes its tokens' norm factors (one wave per token).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -55,76 +58,100 @@ __device__ __forceinline__ float row_rinv(const RouterParams& p, int t, int lane
 }
 
 // x'[t][h0 .. h0 + 7] from the activations (8 consecutive values).
-template <int XDT>
-__device__ __forceinline__ void x_chunk(const RouterParams& p, int t, int h0, float r, float (&v)[8]) {
-    const size_t base = (size_t)t * p.H + h0;
-    if constexpr (XDT == 1) {
-        const uint4 u = *reinterpret_cast<const uint4*>((const uint16_t*)p.x + base);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-    } else {
-        const float4 a = *reinterpret_cast<const float4*>((const float*)p.x + base);
-        const float4 b = *reinterpret_cast<const float4*>((const float*)p.x + base + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-    if (p.norm) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = v[i] * r;
-    }
-    if (p.in_scale) {
-        const float4 a = *reinterpret_cast<const float4*>(p.in_scale + h0);
-        const float4 b = *reinterpret_cast<const float4*>(p.in_scale + h0 + 4);
-        const float s[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = v[i] * s[i];
-    }
-}
+constexpr int kRtChunks = 8;                  // 16-byte weight chunks a lane holds at once
+constexpr size_t kRtLdsBudget = 64 * 1024;    // activation tile + scale in LDS
 
 template <int XDT>
-__global__ void __launch_bounds__(256) router_gemv_kernel(RouterParams p) {
-    __shared__ float rinv[kSmallT];
+__global__ void __launch_bounds__(256) router_gemv_kernel(RouterParams p, int tt) {
+    extern __shared__ __align__(16) uint8_t lds_raw[];
+    constexpr int ES = XDT == 1 ? 2 : 4;       // bytes per activation
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    if (p.norm)
-        for (int t = wv; t < p.T; t += 4) {
-            const float r = row_rinv<XDT>(p, t, lane);
-            if (lane == 0) rinv[t] = r;
-        }
-    __syncthreads();
     const int e = blockIdx.x * 4 + wv;
-    if (e >= p.E) return;
-    float acc[kSmallT];
+    const int t0 = blockIdx.y * tt, nt = min(tt, p.T - t0);
+    const int n_ch = p.H / 8;                  // 16-byte weight chunks of a row
+    const int ec = e < p.E ? e : p.E - 1;      // (a wave past E loads a real row and stores nothing)
+    const uint16_t* row = p.wr + (size_t)ec * p.H;
+    // The tile's activation rows and the scale, into LDS (16 bytes a thread
+    // and pass), while the first weight chunks are on their way.
+    uint4 wch[kRtChunks];
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t) acc[t] = 0.f;
-    const uint16_t* row = p.wr + (size_t)e * p.H;
-    for (int h0 = 8 * lane; h0 < p.H; h0 += 8 * 64) {
-        const uint4 u = *reinterpret_cast<const uint4*>(row + h0);
-        const uint32_t w2[4] = {u.x, u.y, u.z, u.w};
-        float w[8];
+    for (int i = 0; i < kRtChunks; ++i) {
+        const int c = lane + 64 * i;
+        wch[i] = *reinterpret_cast<const uint4*>(row + 8 * (c < n_ch ? c : 0));
+    }
+    const int x16 = nt * p.H * ES / 16;
+    const uint4* xsrc = reinterpret_cast<const uint4*>((const uint8_t*)p.x + (size_t)t0 * p.H * ES);
+    uint4* xl = reinterpret_cast<uint4*>(lds_raw);
+    for (int i = threadIdx.x; i < x16; i += 256) xl[i] = xsrc[i];
+    float* sl = reinterpret_cast<float*>(lds_raw + (size_t)tt * p.H * ES);
+    if (p.in_scale)
+        for (int i = threadIdx.x; i < p.H / 4; i += 256)
+            reinterpret_cast<float4*>(sl)[i] = reinterpret_cast<const float4*>(p.in_scale)[i];
+    __syncthreads();
+    float acc[kSmallT], ss[kSmallT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            w[2 * i] = __uint_as_float(w2[i] << 16);
-            w[2 * i + 1] = __uint_as_float(w2[i] & 0xFFFF0000u);
+    for (int t = 0; t < kSmallT; ++t) acc[t] = ss[t] = 0.f;
+    for (int c0 = 0; c0 < n_ch; c0 += 64 * kRtChunks) {
+        if (c0 > 0) {   // rows longer than 64 * kRtChunks chunks: the next set
+#pragma unroll
+            for (int i = 0; i < kRtChunks; ++i) {
+                const int c = c0 + lane + 64 * i;
+                wch[i] = *reinterpret_cast<const uint4*>(row + 8 * (c < n_ch ? c : 0));
+            }
         }
 #pragma unroll
-        for (int t = 0; t < kSmallT; ++t) {
-            if (t < p.T) {
-                float v[8];
-                x_chunk<XDT>(p, t, h0, p.norm ? rinv[t] : 1.f, v);
+        for (int i = 0; i < kRtChunks; ++i) {
+            const int c = c0 + lane + 64 * i;
+            if (c < n_ch) {
+                const uint32_t w2[4] = {wch[i].x, wch[i].y, wch[i].z, wch[i].w};
+                float w[8], sc[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[t] = __builtin_fmaf(w[i], v[i], acc[t]);
+                for (int j = 0; j < 4; ++j) {
+                    w[2 * j] = __uint_as_float(w2[j] << 16);
+                    w[2 * j + 1] = __uint_as_float(w2[j] & 0xFFFF0000u);
+                }
+                if (p.in_scale) {
+                    const float4 a = reinterpret_cast<const float4*>(sl)[2 * c];
+                    const float4 b = reinterpret_cast<const float4*>(sl)[2 * c + 1];
+                    sc[0] = a.x; sc[1] = a.y; sc[2] = a.z; sc[3] = a.w;
+                    sc[4] = b.x; sc[5] = b.y; sc[6] = b.z; sc[7] = b.w;
+                }
+#pragma unroll
+                for (int t = 0; t < kSmallT; ++t) {
+                    if (t < nt) {
+                        float v[8];
+                        if constexpr (XDT == 1) {
+                            const uint4 u = xl[(t * p.H) / 8 + c];
+                            const uint32_t x2[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                v[2 * j] = __uint_as_float(x2[j] << 16);
+                                v[2 * j + 1] = __uint_as_float(x2[j] & 0xFFFF0000u);
+                            }
+                        } else {
+                            const uint4 a = xl[(t * p.H) / 4 + 2 * c], b = xl[(t * p.H) / 4 + 2 * c + 1];
+                            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+                            v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+                            v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+                            v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            if (p.norm) ss[t] = __builtin_fmaf(v[j], v[j], ss[t]);
+                            const float xs = p.in_scale ? v[j] * sc[j] : v[j];
+                            acc[t] = __builtin_fmaf(w[j], xs, acc[t]);
+                        }
+                    }
+                }
             }
         }
     }
 #pragma unroll
     for (int t = 0; t < kSmallT; ++t) {
-        if (t < p.T) {
-            const float s = wave_sum_f32(acc[t]);
-            if (lane == 0) p.logits[(size_t)t * p.E + e] = s;
+        if (t < nt) {
+            float sum = wave_sum_f32(acc[t]);
+            if (p.norm) sum = sum * (1.f / sqrtf(wave_sum_f32(ss[t]) / (float)p.H + p.eps));
+            if (lane == 0 && e < p.E) p.logits[(size_t)(t0 + t) * p.E + e] = sum;
         }
     }
 }
@@ -207,9 +234,14 @@ hipError_t launch_router(const void* wr, const float* in_scale, int norm, float 
     p.eps = eps;
     const bool bf = x_dtype == 1;
     if (T <= kSmallT) {
-        const dim3 grid((E + 3) / 4);
-        if (bf) hipLaunchKernelGGL(router_gemv_kernel<1>, grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL(router_gemv_kernel<0>, grid, dim3(256), 0, s, p);
+        // As many tokens per tile as the LDS budget holds (one or more tiles).
+        const size_t es = bf ? 2 : 4, sc = in_scale ? (size_t)4 * H : 0;
+        int tt = T;
+        while (tt > 1 && (size_t)tt * H * es + sc > kRtLdsBudget) --tt;
+        const size_t lds = (size_t)tt * H * es + sc;
+        const dim3 grid((E + 3) / 4, (T + tt - 1) / tt);
+        if (bf) hipLaunchKernelGGL(router_gemv_kernel<1>, grid, dim3(256), lds, s, p, tt);
+        else hipLaunchKernelGGL(router_gemv_kernel<0>, grid, dim3(256), lds, s, p, tt);
         return hipGetLastError();
     }
     const dim3 grid((T + kRtTileT - 1) / kRtTileT, (E + kRtTileE - 1) / kRtTileE);

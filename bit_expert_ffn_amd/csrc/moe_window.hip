@@ -46,9 +46,12 @@
 //
 // Failures.  A bounded wait that gives up ORs kErrTimeout into the
 // workspace's error word, and from then on every value its workgroup
-// publishes (d words, output rows) is NaN, so the failure reaches y.  A call
-// that finds the error word already set (a failure that moe_workspace_check
-// has not cleared) writes NaN into every output row and does no other work.
+// publishes (d words, output rows) is NaN, so the failure reaches y.  Every
+// workgroup reads the error word when its gate/up items are done, before its
+// first wait (not earlier: an agent-coherent load in flight holds every
+// barrier of its workgroup): if a failure that moe_workspace_check has not
+// cleared is there, the workgroup writes NaN rows and does nothing else, so
+// no wait runs on stale shared state.
 #include <map>
 #include <mutex>
 #include <utility>
@@ -121,6 +124,8 @@ struct WinLDS {
     int gu_passes, tiles_gu, tiles_gu_s;   // this call's gate/up tiling (gu_tiling)
     int flag_reset;
     int fail;               // publish NaN: an earlier failure, or one of this workgroup's waits gave up
+    int prior;              // 1: an unchecked failure of an earlier call; -1: not looked at yet
+    int bad;                // a caller-supplied id outside [0, E) with a nonzero weight
 };
 
 constexpr uint32_t kNaNBits = 0x7FC00000u;   // never 0, so a published NaN reads as written
@@ -161,7 +166,6 @@ __device__ __forceinline__ void gu_tiling(const WindowParams& p, WinLDS& R, int 
 __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, uint64_t* scratch, int P_gu) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k, n = p.T * k;
-    const int prior = tid == 0 ? load_error(p.err) : 0;   // issued ahead of the logits
     bool bad_any = false;
     for (int t = wv; t < p.T; t += kGemvThreads / 64) {
         int id = 0;
@@ -181,16 +185,23 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
         if (lane < k) {
             R.id[t * k + lane] = id;
             R.w[t * k + lane] = wt;
-            R.cw[t * k + lane] = on ? wt * (p.down_scale ? p.down_scale[id] : 1.f) : 0.f;
+            float cw = wt;
+            if (p.down_scale && on) cw = wt * p.down_scale[id];
+            if (!on) cw = 0.f;
+            R.cw[t * k + lane] = cw;
             R.on[t * k + lane] = on;
             // skipped slots sort after every pair (ids are below 2^10)
             R.key[t * k + lane] = on ? (id << 8 | (t * k + lane)) : (0x7F000000 | (t * k + lane));
         }
     }
     if (tid < 4) R.key[n + tid] = 0x7FFFFFFF;
-    if (tid == 0) R.fail = prior != 0;
+    if (tid == 0) {
+        R.fail = 0;
+        R.prior = -1;
+        R.bad = 0;
+    }
     __syncthreads();
-    if (bad_any && lane == 0) R.fail = 1;
+    if (bad_any && lane == 0) R.bad = 1;
     // Keys are distinct (a token selects an expert at most once), so each
     // pair's count of smaller keys is its sorted position.
     if (tid < n) {
@@ -206,8 +217,11 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
     if (wv == 0) {
         // The pairs with a group: all of them, or those of nonzero weight
         // (sorted first).
-        int na = 0;
-        for (int r0 = 0; r0 < n; r0 += 64) na += __popcll(__ballot(r0 + lane < n && R.on[r0 + lane]));
+        int na = n;
+        if (p.ids_in) {
+            na = 0;
+            for (int r0 = 0; r0 < n; r0 += 64) na += __popcll(__ballot(r0 + lane < n && R.on[r0 + lane]));
+        }
         // A group starts at every kWinGroup-th pair of a run of one expert.
         int base = 0, carry = 0;   // carry: the run start in effect at the end of the previous 64 pairs
         for (int r0 = 0; r0 < na; r0 += 64) {
@@ -524,9 +538,10 @@ __device__ __forceinline__ float pairwise_sum(const float* v) {
 }
 
 // Sum over slots [j0, j0 + 16) of cw[t][j] * d[t * k + j] for 4 consecutive
-// rows h.. (0 past k and for a skipped slot, whose d is never written),
-// pairwise in slot order; all 16 loads in flight together, then one check (a
-// word still 0 is read again).
+// rows h.. (0 past k and, with caller-supplied routing, for a skipped slot,
+// whose d is never written), pairwise in slot order; all 16 loads in flight
+// together, then one check (a word still 0 is read again).
+template <bool ROUTED>
 __device__ __forceinline__ void slot_sums16(const WindowParams& p, const WinLDS& R, __amdgpu_buffer_rsrc_t rsrc, int t,
                                             int h, int j0, float (&out)[4]) {
     const int k = p.k;
@@ -534,10 +549,10 @@ __device__ __forceinline__ void slot_sums16(const WindowParams& p, const WinLDS&
     bool on[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        on[j] = j0 + j < k && R.on[t * k + j0 + j];
+        on[j] = j0 + j < k && (!ROUTED || R.on[t * k + j0 + j]);
         const int jj = j0 + j < k ? j0 + j : 0;   // past k: slot 0 again, unused
         raw[j] = load_coherent4(rsrc, 4u * (uint32_t)((t * k + jj) * p.H + h));
-        if (!on[j]) raw[j] = win_u32x4{1u, 1u, 1u, 1u};
+        if (ROUTED && !on[j]) raw[j] = win_u32x4{1u, 1u, 1u, 1u};
     }
     uint32_t m = 0xFFFFFFFFu;
 #pragma unroll
@@ -564,18 +579,20 @@ __device__ __forceinline__ void slot_sums16(const WindowParams& p, const WinLDS&
 // inside a window; the shared term is added last.  Each thread takes 4
 // consecutive rows of one token.  The d words read are cleared for the next
 // call.
+template <bool ROUTED>
 __device__ __forceinline__ void combine_rows(const WindowParams& p, const WinLDS& R, int h0, int n4) {
     const int k = p.k;
     const int nq = p.T * n4;
+    const bool failed = R.fail;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.d, 0, (kSmallT * k + kSmallT) * p.H * 4, kRsrcWord3);
     for (int qd = threadIdx.x; qd < nq; qd += kGemvThreads) {
         const int t = qd / n4, h = h0 + 4 * (qd - t * n4);
         float acc[4];
-        slot_sums16(p, R, rsrc, t, h, 0, acc);
+        slot_sums16<ROUTED>(p, R, rsrc, t, h, 0, acc);
         if (k > 16) {
             float hi[4];
-            slot_sums16(p, R, rsrc, t, h, 16, hi);
+            slot_sums16<ROUTED>(p, R, rsrc, t, h, 16, hi);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = acc[e] + hi[e];
         }
@@ -586,7 +603,7 @@ __device__ __forceinline__ void combine_rows(const WindowParams& p, const WinLDS
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(sv[e]) + acc[e];
         }
-        if (R.fail) acc[0] = acc[1] = acc[2] = acc[3] = __uint_as_float(kNaNBits);
+        if (failed) acc[0] = acc[1] = acc[2] = acc[3] = __uint_as_float(kNaNBits);
         *reinterpret_cast<float4*>(p.y + (size_t)t * p.H + h) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
         for (int j = 0; j < k; ++j) *reinterpret_cast<uint4*>(p.d + (size_t)(t * k + j) * p.H + h) = zero;
@@ -681,10 +698,20 @@ __device__ __forceinline__ void dn_load(const WindowParams& p, const DnItem& it,
     }
 }
 
-// Wait for the group's gate/up and take its `a` rows.
+// Thread 0, before the workgroup's first wait: whether the error word holds
+// an unchecked failure of an earlier call (R.prior).  The load is issued
+// after the item's weight loads, whose arrival the first poll waits for
+// anyway, so it costs no time.
+__device__ __forceinline__ bool prior_failure(const WindowParams& p, WinLDS& R) {
+    if (R.prior < 0) R.prior = load_error(p.err) != 0;
+    return R.prior != 0;
+}
+
+// Wait for the group's gate/up and take its `a` rows (nothing on an earlier
+// failure).
 template <int QK>
 __device__ __forceinline__ void dn_begin(const WindowParams& p, WinLDS& R, const DnItem& it, float* lds) {
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && !prior_failure(p, R)) {
         const int need = __builtin_amdgcn_readfirstlane(it.sh ? R.tiles_gu_s : R.tiles_gu);
         const int* cnt = win_gu_count(p.sync, it.g);
         if (!bounded_wait([&]() __attribute__((always_inline)) { return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need; },
@@ -692,6 +719,7 @@ __device__ __forceinline__ void dn_begin(const WindowParams& p, WinLDS& R, const
             R.fail = 1;
     }
     __syncthreads();
+    if (R.prior > 0) return;
     if (p.stage_words) {
         // Each slice (token i, block column b) once, arranged into dot pairs
         // of its hi and lo terms in LDS for every thread of column b.
@@ -773,12 +801,13 @@ __device__ __forceinline__ void dn_finish(const WindowParams& p, WinLDS& R, cons
             }
         }
         lds_barrier();
+        const bool failed = R.fail;
         for (int i = tid; i < it.nrows * 2; i += kGemvThreads) {
             const int r = i >> 1, t = i & 1;
             if (t >= nt) continue;
             const float v = sum_columns(part + (r * 2 + t) * nbp, l.nb);
             const int drow = it.sh ? kSmallT * p.k + it.first + t0 + t : R.sorted[it.first + t0 + t];
-            __hip_atomic_store(p.d + (size_t)drow * p.H + it.h0 + r, R.fail ? kNaNBits : nonzero_bits(v),
+            __hip_atomic_store(p.d + (size_t)drow * p.H + it.h0 + r, failed ? kNaNBits : nonzero_bits(v),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // The partials are reused by the next pair.  After the last pair the
@@ -841,6 +870,7 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
     while (true) {
         int next = item + p.n_wg;
         dn_begin<QK>(p, R, ia, lds);
+        if (R.prior > 0) return;
         if (item != first_item) dn_settle(p, R, ib, od_b);
         ib = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         ib.none = next >= n_items;
@@ -854,6 +884,7 @@ __device__ __forceinline__ void down_window(const WindowParams& p, WinLDS& R, fl
         item = next;
         next = item + p.n_wg;
         dn_begin<QK>(p, R, ib, lds);
+        if (R.prior > 0) return;
         dn_settle(p, R, ia, od_a);
         ia = dn_item<QK>(p, R, next < n_items ? next : item, n_routed);
         ia.none = next >= n_items;
@@ -883,13 +914,15 @@ __device__ __forceinline__ void combine_window(const WindowParams& p, WinLDS& R)
         const int c = sl / hp, part = sl - c * hp;
         const int c0 = c * p.chunk_rows, nr4 = (min(c0 + p.chunk_rows, p.H) - c0) / 4;
         const int q0 = part * nr4 / hp, q1 = (part + 1) * nr4 / hp;
-        if (threadIdx.x == 0) {
+        if (threadIdx.x == 0 && !prior_failure(p, R)) {
             const int* cnt = win_chunk(p.sync, p.k, c);
             if (!bounded_wait(
                     [&]() __attribute__((always_inline)) { return __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need_chunk; },
                     p.polls, p.err))
                 R.fail = 1;
         }
+        __syncthreads();
+        if (R.prior > 0) return;
         // Count this part as one that has seen the chunk complete (no part
         // looks at the chunk's counter after that); the count returns while
         // the rows are combined.
@@ -898,7 +931,8 @@ __device__ __forceinline__ void combine_window(const WindowParams& p, WinLDS& R)
             old = __hip_atomic_fetch_add(win_combined(p.sync, p.k, p.n_chunks, c), 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        combine_rows(p, R, c0 + 4 * q0, q1 - q0);
+        if (p.ids_in) combine_rows<true>(p, R, c0 + 4 * q0, q1 - q0);
+        else combine_rows<false>(p, R, c0 + 4 * q0, q1 - q0);
         if (threadIdx.x == 0) {
             if (old == hp - 1) {
                 __hip_atomic_store(win_chunk(p.sync, p.k, c), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -920,16 +954,21 @@ __global__ void __launch_bounds__(kGemvThreads, 2) window_layer_kernel(WindowPar
             if (p.w_out) p.w_out[q] = R.w[q];
         }
     }
-    if (R.fail) {
-        // The workspace holds an unchecked failure: its shared state may be
-        // stale, so nothing is computed; every output row is NaN.
+    if (!R.bad) {
+        gateup_window<QT, NTERM>(p, R, lds);
+        down_window<QT>(p, R, lds);
+        if (R.prior <= 0) combine_window(p, R);
+        // A workgroup without a down item or combine part looks too, so that
+        // on an earlier failure every workgroup writes its share of NaN rows.
+        if (threadIdx.x == 0) prior_failure(p, R);
+        __syncthreads();
+    }
+    if (R.bad || R.prior > 0) {
+        // Invalid caller-supplied routing, or an unchecked earlier failure
+        // (stale shared state: no wait ran on it): every output row is NaN.
         for (int q = blockIdx.x * kGemvThreads + threadIdx.x; q < p.T * p.H; q += p.n_wg * kGemvThreads)
             p.y[q] = __uint_as_float(kNaNBits);
-        return;
     }
-    gateup_window<QT, NTERM>(p, R, lds);
-    down_window<QT>(p, R, lds);
-    combine_window(p, R);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1020,7 +1059,7 @@ static hipError_t window_capacity(size_t lds_bytes, int* out) {
     auto it = cache.find({dev, lds_bytes});
     if (it == cache.end()) {
         e = hipFuncSetAttribute((const void*)window_layer_kernel<QT, NTERM>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                150 * 1024);
+                                148 * 1024);
         if (e != hipSuccess) return e;
         int n_cu = 0, per_cu = 0;
         e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);

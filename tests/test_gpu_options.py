@@ -206,6 +206,19 @@ def test_router_logits_within_fp32_bound(T, xd, norm, scaled):
     assert np.all(np.abs(got - ref) <= bound)
 
 
+@pytest.mark.parametrize("T,xd", [(8, "f32"), (5, "bf16"), (1, "f32")])
+def test_router_logits_wide_rows_and_token_tiles(T, xd):
+    """H = 7168: each lane's weight row takes two sets of chunks, and fp32 rows
+    of 8 tokens exceed the LDS budget, so tokens are split over tiles."""
+    E, H = 96, 7168
+    wr, sc, x = _router_inputs(E, H, T, seed=300 + T, xd=xd)
+    rt = moe.router(_x_tensor(wr.view(np.uint16)).view(torch.bfloat16), torch.from_numpy(sc).to(DEV), norm=True,
+                    eps=1e-6)
+    got = moe.router_logits(rt, E, _x_tensor(x)).cpu().numpy().astype(np.float64)
+    ref = oracle.router_logits(wr, x, norm=True, eps=1e-6, in_scale=sc)
+    assert np.all(np.abs(got - ref) <= router_error_bound(wr, _xprime(x, True, sc, 1e-6)))
+
+
 def test_router_logits_batch_invariant():
     E, H = 512, 2560
     wr, sc, x = _router_inputs(E, H, 8, seed=77)
