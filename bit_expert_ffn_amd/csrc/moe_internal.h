@@ -70,6 +70,7 @@ struct LargeLayout {
     size_t counts, offsets;  // per expert
     size_t tiles, ntiles;    // row tiles: (expert, first sorted row, rows)
     size_t perm, inv;        // sorted row -> token; (token, slot) -> sorted row
+    size_t bcount;           // [blocks of pairs][E] counts of the placement sort
     size_t xq, xe;           // [2][T][H] fp16 activation planes (hi, lo); [T] power-of-two exponents
     size_t a;                // [rows][FFmax] bf16 hi plane, then the lo plane
     size_t ypair;            // [rows][H] fp32 down projection per sorted row

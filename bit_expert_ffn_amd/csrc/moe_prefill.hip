@@ -4,16 +4,17 @@
 // 5.3; kairos-engine README "The MoE forward": the batch is bucketed by expert
 // and each expert runs one GEMM over every token that chose it; "Prefill and
 // decode are different machines": prefill dequantises and feeds the tensor
-// cores).  Steps, each one kernel on the caller's stream:
-//   1. route    : top-k per token (the decode path's wave top-k).
+// cores).  Stages on the caller's stream:
+//   1. route    : top-k per token (the decode path's wave top-k), or the
+//                 caller-supplied routing copied and checked.
 //   2. count    : per-expert counts, offsets and a list of row tiles (<= 128
 //                 (token, slot) rows of one expert each).
-//   3. place    : one wave per expert scans the pairs in (token, slot) order and
-//                 writes the sorted position of each (a stable counting sort);
-//                 the same launch converts the activations (step 3b).
+//   3. place    : the sorted position of every pair, a stable counting sort in
+//                 two launches over blocks of pairs (block counts, then
+//                 positions); then the activations are converted (3b).
 //   3b. xprep   : each token's activations as fp16 times a power of two.
-//   4. gate/up  : per row tile and 128 features, G = X W_g^T and U = X W_u^T
-//                 on MFMA, then a = silu(G) * U, stored as bf16 hi + lo.
+//   4. gate/up  : per row tile and 256 features, G = X W_g^T and U = X W_u^T
+//                 on MFMA, then a = act(G) * U, stored as bf16 hi + lo.
 //   5. down     : per row tile and 256 outputs, Y = a W_d^T on MFMA.
 //   6. combine  : y[t] = shared(t) + sum_j w[t][j] * Y[pair(t, j)], fixed order.
 //
@@ -56,6 +57,7 @@ constexpr int kGuThreads = 512;            // gate/up workgroup: 8 waves
 constexpr int kGuFeatures = 256;           // features per gate/up workgroup (32 per wave)
 constexpr int kDnThreads = 512;            // down workgroup: 8 waves
 constexpr int kDnCols = 512;               // outputs per down workgroup (64 per wave)
+constexpr int kPlaceBlock = 1024;          // (token, slot) pairs per placement block
 
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype) {
     LargeLayout L{};
@@ -78,6 +80,7 @@ LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype)
     L.ntiles = take(4);
     L.perm = take(P * 4);                // sorted row -> token
     L.inv = take(n * 4);                 // (token, slot) -> sorted row
+    L.bcount = take(((n + kPlaceBlock - 1) / kPlaceBlock) * (size_t)E * 4);   // per block of pairs, per expert
     L.xq = take((size_t)2 * T * H * 2 + 256);   // + slack: the last chunk of the last row reads past H
     L.xe = take((size_t)T * 4);
     L.a = take(P * ffmax * 2 * 2 + 256); // a_hi then a_lo planes, bf16 (+ slack as for xq)
@@ -107,6 +110,7 @@ struct PrefillParams {
     int* ntiles;
     int* perm;
     int* inv;
+    int* bcount;              // [blocks][E] pairs of each expert in each block of kPlaceBlock pairs
     uint16_t* xq;             // [2][T][H] fp16
     int* xe;                  // [T]
     uint16_t* a_hi;
@@ -176,27 +180,58 @@ __global__ void __launch_bounds__(1024) prefill_count_kernel(PrefillParams p) {
     }
 }
 
-// One wave per expert writes its pairs in (token, slot) order: a stable counting sort.
+// Stable counting sort of the (token, slot) pairs by expert, in two passes
+// over blocks of kPlaceBlock pairs (the pairs' order within an expert is
+// (token, slot) order).  Pass 1: each block's count of every expert.
+__global__ void __launch_bounds__(256) prefill_blockcount_kernel(PrefillParams p) {
+    __shared__ int h[kMaxE];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    const int n = p.T * p.k, q0 = b * kPlaceBlock, q1 = min(n, q0 + kPlaceBlock);
+    for (int e = tid; e < p.E; e += 256) h[e] = 0;
+    __syncthreads();
+    for (int q = q0 + tid; q < q1; q += 256)
+        if (pair_on(p, q)) atomicAdd(&h[p.ids[q]], 1);   // counts: order-free
+    __syncthreads();
+    for (int e = tid; e < p.E; e += 256) p.bcount[(size_t)b * p.E + e] = h[e];
+}
+
+// Pass 2: a pair's sorted position is its expert's offset, plus the pairs of
+// that expert in earlier blocks, plus those earlier in its own block (each
+// pair compares its expert with every earlier one of the block, read from
+// LDS: the same address for every lane of a wave at each step).
 __global__ void __launch_bounds__(256) prefill_place_kernel(PrefillParams p) {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int n = p.T * p.k;
-    if (e < p.E) {
-        int pos = p.offsets[e];
-        for (int c = 0; c < n; c += 64) {
-            const int q = c + lane;
-            const bool match = q < n && p.ids[q] == e && pair_on(p, q);
-            const uint64_t m = __ballot(match);
-            if (match) {
-                const int r = pos + __popcll(m & ((1ull << lane) - 1));
-                p.perm[r] = q / p.k;
-                p.inv[q] = r;
-            }
-            pos += __popcll(m);
+    __shared__ int base[kMaxE];
+    __shared__ __align__(16) int eid[kPlaceBlock];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    const int n = p.T * p.k, q0 = b * kPlaceBlock, len = min(kPlaceBlock, n - q0);
+    for (int e = tid; e < p.E; e += 256) {
+        int v = p.offsets[e];
+        for (int b0 = 0; b0 < b; b0 += 8) {   // eight block counts in flight at a time
+            int c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = b0 + u < b ? p.bcount[(size_t)(b0 + u) * p.E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v += c[u];
         }
+        base[e] = v;
     }
-    if (p.shared)
-        for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < p.T; t += gridDim.x * blockDim.x) p.perm[n + t] = t;
+    for (int i = tid; i < kPlaceBlock; i += 256) eid[i] = (i < len && pair_on(p, q0 + i)) ? p.ids[q0 + i] : -1;
+    __syncthreads();
+    for (int i = tid; i < len; i += 256) {
+        const int e = eid[i];
+        if (e < 0) continue;
+        int r = 0, j = 0;
+        for (; j + 4 <= i; j += 4) {
+            const int4 v = *reinterpret_cast<const int4*>(&eid[j]);
+            r += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+        }
+        for (; j < i; ++j) r += eid[j] == e;
+        const int pos = base[e] + r;
+        p.perm[pos] = (q0 + i) / p.k;
+        p.inv[q0 + i] = pos;
+    }
+    if (p.shared && b == 0)
+        for (int t = tid; t < p.T; t += 256) p.perm[n + t] = t;
 }
 
 // Caller-supplied routing: copied to the routing buffers the later stages
@@ -849,6 +884,7 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     p.ntiles = (int*)(ws + L.ntiles);
     p.perm = (int*)(ws + L.perm);
     p.inv = (int*)(ws + L.inv);
+    p.bcount = (int*)(ws + L.bcount);
     p.xq = (uint16_t*)(ws + L.xq);
     p.xe = (int*)(ws + L.xe);
     const size_t P = (size_t)T * k + (FFs ? (size_t)T : 0);
@@ -870,7 +906,11 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     stage_mark(marks, s);
     hipLaunchKernelGGL(prefill_count_kernel, dim3(1), dim3(1024), 0, s, p);
     stage_mark(marks, s);
-    hipLaunchKernelGGL(prefill_place_kernel, dim3((E + 3) / 4), dim3(256), 0, s, p);
+    {
+        const unsigned nb = (unsigned)((T * k + kPlaceBlock - 1) / kPlaceBlock);
+        hipLaunchKernelGGL(prefill_blockcount_kernel, dim3(nb), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(prefill_place_kernel, dim3(nb), dim3(256), 0, s, p);
+    }
     if (qtype == 2) {
         if (x_dtype == 1) hipLaunchKernelGGL((prefill_xprep_kernel<2, 1>), dim3(T), dim3(256), 0, s, p);
         else hipLaunchKernelGGL((prefill_xprep_kernel<2, 0>), dim3(T), dim3(256), 0, s, p);
