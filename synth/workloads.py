@@ -51,6 +51,12 @@ WORKLOADS = {
     "verify_t4": Workload("verify_t4", 48, 512, 2560, 640, 10, 1, 1.5, 0.05, 4, "bf16", 1.0),
     "verify_t8": Workload("verify_t8", 48, 512, 2560, 640, 10, 1, 1.5, 0.05, 8, "bf16", 1.0),
     "prefill": Workload("prefill", 4, 256, 7168, 2048, 8, 2, 7.5, 0.02, 4096, "bf16", 0.6),
+    # Measurement aids, not workloads of the pages: the Strata routing (512
+    # experts, top-10, Zipf s = 1.0) and layer structure with experts so small
+    # (H 256, FF 64) that their bytes and arithmetic are negligible, so a layer
+    # call's time is the fixed cost of its dependent steps.
+    "strata_floor": Workload("strata_floor", 48, 512, 256, 64, 10, 1, 1.5, 0.05, 1, "bf16", 1.0),
+    "verify_t8_floor": Workload("verify_t8_floor", 48, 512, 256, 64, 10, 1, 1.5, 0.05, 8, "bf16", 1.0),
 }
 
 
