@@ -330,18 +330,22 @@ __device__ __forceinline__ uint64_t topk_rounds(uint64_t (&key)[KPL], int k, int
     return sel;
 }
 
+// A row's logits as this lane holds them (l, l + 64, ...).  Every load is
+// unconditional (clamped address) so that all of them are in flight together;
+// out-of-range slots are masked afterwards, branch-free.
 template <int KPL>
-__device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int E, int k, int renorm, int lane,
-                                              uint64_t* scratch, int* out_id, float* out_w) {
-    uint64_t key[KPL];
-    float lv[KPL];
-    // Every load is unconditional (clamped address) so that all of them are in
-    // flight together; out-of-range slots are masked afterwards, branch-free.
+__device__ __forceinline__ void topk_load(const float* __restrict__ row, int E, int lane, float (&lv)[KPL]) {
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = lane + 64 * i;
         lv[i] = row[e < E ? e : E - 1];
     }
+}
+
+template <int KPL>
+__device__ __forceinline__ void topk_of_values(const float (&lv)[KPL], int E, int k, int renorm, int lane,
+                                               uint64_t* scratch, int* out_id, float* out_w) {
+    uint64_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const uint32_t e = (uint32_t)(lane + 64 * i);
@@ -374,6 +378,28 @@ __device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int
     *out_w = e_sel / denom;
 }
 
+template <int KPL>
+__device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int E, int k, int renorm, int lane,
+                                              uint64_t* scratch, int* out_id, float* out_w) {
+    float lv[KPL];
+    topk_load<KPL>(row, E, lane, lv);
+    topk_of_values<KPL>(lv, E, k, renorm, lane, scratch, out_id, out_w);
+}
+
+// Two rows by one wave, one after the other, with both rows' loads issued
+// first: the second row's logits arrive while the first is ranked.  With
+// `two` false only row0 is ranked (its loads are issued twice).
+template <int KPL>
+__device__ __forceinline__ void wave_topk2_kpl(const float* __restrict__ row0, const float* __restrict__ row1,
+                                               bool two, int E, int k, int renorm, int lane, uint64_t* scratch,
+                                               int (&out_id)[2], float (&out_w)[2]) {
+    float l0[KPL], l1[KPL];
+    topk_load<KPL>(row0, E, lane, l0);
+    topk_load<KPL>(two ? row1 : row0, E, lane, l1);
+    topk_of_values<KPL>(l0, E, k, renorm, lane, scratch, &out_id[0], &out_w[0]);
+    if (two) topk_of_values<KPL>(l1, E, k, renorm, lane, scratch, &out_id[1], &out_w[1]);
+}
+
 // `scratch`: 128 keys of LDS owned by the calling wave.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm, int lane,
                                           uint64_t* scratch, int* out_id, float* out_w) {
@@ -381,6 +407,15 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
     else if (E <= 256) wave_topk_kpl<4>(row, E, k, renorm, lane, scratch, out_id, out_w);
     else if (E <= 512) wave_topk_kpl<8>(row, E, k, renorm, lane, scratch, out_id, out_w);
     else wave_topk_kpl<16>(row, E, k, renorm, lane, scratch, out_id, out_w);
+}
+
+__device__ __forceinline__ void wave_topk2(const float* __restrict__ row0, const float* __restrict__ row1, bool two,
+                                           int E, int k, int renorm, int lane, uint64_t* scratch, int (&out_id)[2],
+                                           float (&out_w)[2]) {
+    if (E <= 128) wave_topk2_kpl<2>(row0, row1, two, E, k, renorm, lane, scratch, out_id, out_w);
+    else if (E <= 256) wave_topk2_kpl<4>(row0, row1, two, E, k, renorm, lane, scratch, out_id, out_w);
+    else if (E <= 512) wave_topk2_kpl<8>(row0, row1, two, E, k, renorm, lane, scratch, out_id, out_w);
+    else wave_topk2_kpl<16>(row0, row1, two, E, k, renorm, lane, scratch, out_id, out_w);
 }
 
 }  // namespace moe

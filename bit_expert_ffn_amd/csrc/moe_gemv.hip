@@ -263,8 +263,11 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         }
     }
     __syncthreads();
-    // One thread per (row, token): both row sums, SwiGLU, the store.
-    for (int i = tid; i < Rr * NT; i += kGemvThreads) {
+    // One thread per (row, token): both row sums, SwiGLU, the store; waves
+    // 1-3 take the rows when they suffice, so that the count below (wave 0)
+    // waits for no store of its own.
+    const int off = Rr * NT <= kGemvThreads - 64 ? 64 : 0;
+    for (int i = tid - off; i >= 0 && i < Rr * NT; i += kGemvThreads) {
         const int rr = i / NT, t = i - rr * NT;
         const int f = f0 + rr;
         if (f >= rows || t >= ntok) continue;
@@ -273,11 +276,11 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         const float a = act_gate(g, p.act) * u;
         __hip_atomic_store(out + (size_t)outrow[t] * rows + f, pack_a(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // Every store above has completed (the barrier waits for them), so a flag
-    // raised after this count is seen after the words.  Readers still check
-    // each word (see pack_a): a flag that ran ahead would cost a reload, not a
-    // wrong value.
-    __syncthreads();
+    // Every store above has been issued, not necessarily completed (the
+    // barrier does not wait for them): a flag raised after this count can be
+    // seen before a word has landed.  Readers check each word (see pack_a)
+    // and read again one still 0, so that costs a reload, not a wrong value.
+    lds_barrier();
     // Count this tile; the tile that completes its group raises the group's
     // ready flag in every replica (down workgroups each poll one replica).
     if (tid < 64) {

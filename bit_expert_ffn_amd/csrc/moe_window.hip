@@ -32,7 +32,7 @@
 // (If other work holds part of the GPU, the waits last until it leaves room.)
 // Each gate/up tile bumps its group's counter, and the down items of a group
 // start once its counter is complete (no wait for other groups).  Each down
-// item then bumps its chunk's counter once its d words are visible.  When a
+// item then bumps its chunk's counter once its d words are issued.  When a
 // chunk's count is complete, up to eight workgroups that are done with their
 // own items combine it, each a part of its rows: y[t][h] = shared +
 // sum_j w[t][j] d, the slots summed in rank order, so the output does not
@@ -167,6 +167,12 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k, n = p.T * k;
     bool bad_any = false;
+    // Wave w routes tokens w and w + 4 (T <= 8).
+    int rid[2] = {0, 0};
+    float rwt[2] = {1.f, 1.f};
+    if (!p.ids_in && !p.identity && wv < p.T)
+        wave_topk2(p.logits + (size_t)wv * p.E, p.logits + (size_t)(wv + 4) * p.E, wv + 4 < p.T, p.E, k, p.renorm,
+                   lane, scratch + 128 * wv, rid, rwt);
     for (int t = wv; t < p.T; t += kGemvThreads / 64) {
         int id = 0;
         float wt = 1.f;
@@ -180,7 +186,8 @@ __device__ __forceinline__ void route_window(const WindowParams& p, WinLDS& R, u
             bad_any |= __ballot(bad) != 0;
             on = on && !bad;
         } else if (!p.identity) {
-            wave_topk(p.logits + (size_t)t * p.E, p.E, k, p.renorm, lane, scratch + 128 * wv, &id, &wt);
+            id = t == wv ? rid[0] : rid[1];
+            wt = t == wv ? rwt[0] : rwt[1];
         }
         if (lane < k) {
             R.id[t * k + lane] = id;
@@ -810,16 +817,14 @@ __device__ __forceinline__ void dn_finish(const WindowParams& p, WinLDS& R, cons
             __hip_atomic_store(p.d + (size_t)drow * p.H + it.h0 + r, failed ? kNaNBits : nonzero_bits(v),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        // The partials are reused by the next pair.  After the last pair the
-        // barrier also waits for every d store of the workgroup, so the item
-        // is counted only once its words are visible: the combine that the
-        // count may start then finds them on its first read.
-        if (t0 + 2 < it.n_e) lds_barrier();
-        else __syncthreads();
+        // The partials are reused by the next pair.  The barrier does not
+        // wait for the d stores (nor for the next item's code loads issued
+        // before this item): the combine that the count below may start
+        // reads a word again while it is still 0.
+        lds_barrier();
     }
-    // Count the item in its chunk (its d words are visible: the barrier above
-    // waited for them) and, without staged rows, in its group; the group
-    // count is looked at in dn_settle.
+    // Count the item in its chunk (its d words are issued) and, without
+    // staged rows, in its group; the group count is looked at in dn_settle.
     if (tid == 0) {
         if (!p.stage_words)
             old_dn = __hip_atomic_fetch_add(win_dn_count(p.sync, it.g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
