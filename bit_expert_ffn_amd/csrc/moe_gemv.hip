@@ -151,7 +151,11 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     __syncthreads();
 }
 
-template <int QT, int NT, int NTERM>
+// PAIR: each lane takes two adjacent block columns of its row (used where that
+// puts more of the 256 lanes to work, e.g. 88 columns: 220 lanes against 176)
+// and adds their two sums itself, in the order the lane pairs of the default
+// mapping add them (even column first), so the partials are the same bits.
+template <int QT, int NT, int NTERM, bool PAIR>
 __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float* lds) {
     constexpr int QK = QTraits<QT>::QK;
     const int tid = threadIdx.x;
@@ -190,9 +194,12 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
     }
 
     const int nblk = p.H / QK;
-    const int P = kGemvThreads / nblk;
-    const bool active = tid < P * nblk;
-    const int rp = active ? tid / nblk : 0, b = active ? tid - (tid / nblk) * nblk : 0;
+    constexpr int BPL = PAIR ? 2 : 1;   // block columns per lane
+    const int cols = nblk / BPL;
+    const int P = kGemvThreads / cols;
+    const bool active = tid < P * cols;
+    const int rp = active ? tid / cols : 0, lc = active ? tid - (tid / cols) * cols : 0;
+    const int b = lc * BPL;             // the lane's (first) block column
     const int Rr = P * p.gu_passes;
     const int f0 = tile * Rr;
     const size_t plane = (size_t)rows * nblk;
@@ -204,30 +211,38 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
     // Loads of every pass first, from clamped rows (the last tile's overhang
     // re-reads its last row), so that all of them are in flight at once; the
     // pass count is uniform across the workgroup.
-    uint4 cg[kMaxPass], cu[kMaxPass];
-    uint16_t sg_[kMaxPass], su_[kMaxPass];
+    constexpr int MP = PAIR ? kMaxPassPair : kMaxPass;
+    uint4 cg[MP][BPL], cu[MP][BPL];
+    uint16_t sg_[MP][BPL], su_[MP][BPL];
 #pragma unroll
-    for (int m = 0; m < kMaxPass; ++m) {
+    for (int m = 0; m < MP; ++m) {
         if (m < p.gu_passes) {
             const int f = min(f0 + m * P + rp, rows - 1);
             const size_t blk = (size_t)f * nblk + b;
-            cg[m] = ldg_u4(gcode + blk * 16);
-            cu[m] = ldg_u4(ucode + blk * 16);
-            sg_[m] = ldg_u16(gscale + blk * 2);
-            su_[m] = ldg_u16(uscale + blk * 2);
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                cg[m][j] = ldg_u4(gcode + (blk + j) * 16);
+                cu[m][j] = ldg_u4(ucode + (blk + j) * 16);
+                sg_[m][j] = ldg_u16(gscale + (blk + j) * 2);
+                su_[m][j] = ldg_u16(uscale + (blk + j) * 2);
+            }
         }
     }
-    XSlice<QT, NTERM> xs[NT];
-    if (NT == 1 && p.x_off >= 0) {   // arranged while the routing ran
-        slice_from_lds<QT, NTERM>(xs[0], reinterpret_cast<const uint32_t*>(lds) + p.x_off +
-                                             b * SliceWords<QT, NTERM>::N);
-    } else {
+    XSlice<QT, NTERM> xs[BPL][NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if constexpr (NTERM == 1)
-                load_slice_bf16<QT, 1>(xs[t], (const uint16_t*)p.x + (size_t)toks[t] * p.H + b * QK, nullptr, p.z);
-            else
-                load_slice_f32<QT>(xs[t], (const float*)p.x + (size_t)toks[t] * p.H + b * QK, p.z);
+    for (int j = 0; j < BPL; ++j) {
+        if (NT == 1 && p.x_off >= 0) {   // arranged while the routing ran
+            slice_from_lds<QT, NTERM>(xs[j][0], reinterpret_cast<const uint32_t*>(lds) + p.x_off +
+                                                    (b + j) * SliceWords<QT, NTERM>::N);
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if constexpr (NTERM == 1)
+                    load_slice_bf16<QT, 1>(xs[j][t], (const uint16_t*)p.x + (size_t)toks[t] * p.H + (b + j) * QK,
+                                           nullptr, p.z);
+                else
+                    load_slice_f32<QT>(xs[j][t], (const float*)p.x + (size_t)toks[t] * p.H + (b + j) * QK, p.z);
+            }
         }
     }
     // Partials part[((mat * Rr + rr) * NT + t) * ncp + col]: a row's columns
@@ -239,13 +254,22 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
     const int ncp = (ncol + 3) & ~3;
     const int col = pairs ? b >> 1 : b;
 #pragma unroll
-    for (int m = 0; m < kMaxPass; ++m) {
+    for (int m = 0; m < MP; ++m) {
         const int f = f0 + m * P + rp;
         if (m < p.gu_passes && active && f < rows) {
             float og[NT], ou[NT];
-            block_dot<QT, NTERM, NT>(cg[m], scale_at_use(sg_[m]), xs, ntok, og);
-            block_dot<QT, NTERM, NT>(cu[m], scale_at_use(su_[m]), xs, ntok, ou);
-            if (pairs) {
+            block_dot<QT, NTERM, NT>(cg[m][0], scale_at_use(sg_[m][0]), xs[0], ntok, og);
+            block_dot<QT, NTERM, NT>(cu[m][0], scale_at_use(su_[m][0]), xs[0], ntok, ou);
+            if constexpr (PAIR) {
+                float og1[NT], ou1[NT];
+                block_dot<QT, NTERM, NT>(cg[m][BPL - 1], scale_at_use(sg_[m][BPL - 1]), xs[BPL - 1], ntok, og1);
+                block_dot<QT, NTERM, NT>(cu[m][BPL - 1], scale_at_use(su_[m][BPL - 1]), xs[BPL - 1], ntok, ou1);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    og[t] = og[t] + og1[t];
+                    ou[t] = ou[t] + ou1[t];
+                }
+            } else if (pairs) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     og[t] += dpp_xor1_f32(og[t]);
@@ -253,7 +277,7 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
                 }
             }
             const int rr = m * P + rp;
-            if (!pairs || (b & 1) == 0) {
+            if (PAIR || !pairs || (b & 1) == 0) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     lds[((0 * Rr + rr) * NT + t) * ncp + col] = og[t];
@@ -653,7 +677,7 @@ __device__ void janitor_role(const DecodeParams& p, RouteLDS& R) {
         __hip_atomic_store(p.as + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int QT, int NTERM>
+template <int QT, int NTERM, bool PAIR>
 __global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodeParams p) {
     constexpr int NT = 1;   // one token
     extern __shared__ __align__(16) float lds[];   // 16-byte aligned: float4 reads
@@ -692,7 +716,7 @@ __global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodePar
         }
         return;
     }
-    if (wg < p.n_gu) gateup_role<QT, NT, NTERM>(p, R, wg, lds);
+    if (wg < p.n_gu) gateup_role<QT, NT, NTERM, PAIR>(p, R, wg, lds);
     else if (wg - p.n_gu < p.tiles_dn) down_role<QT, NT>(p, R, wg - p.n_gu, lds);
     else janitor_role<NT>(p, R);
 }
@@ -710,7 +734,13 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     g.qtype = qtype;
     g.z = z;
     const int nblk_gu = H / qk;
-    const int P = kGemvThreads / nblk_gu;
+    // Lanes take one block column each, or two adjacent ones where that puts
+    // more lanes to work (the sums are the same bits either way).
+    const int P1 = kGemvThreads / nblk_gu;
+    const int P2 = nblk_gu % 2 == 0 ? kGemvThreads / (nblk_gu / 2) : 0;
+    g.gu_pair = P2 * (nblk_gu / 2) > P1 * nblk_gu ? 1 : 0;
+    const int P = g.gu_pair ? P2 : P1;
+    const int max_pass = g.gu_pair ? kMaxPassPair : kMaxPass;
     g.max_groups = T * k;
     // Enough passes per gate/up workgroup that at most about 256 of them (one
     // per CU) cover the routed experts' FF rows: each gate/up wave then has a
@@ -720,7 +750,7 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     {
         const long rows_all = (long)g.max_groups * FF;
         int passes = (int)((rows_all + (long)P * 256 - 1) / ((long)P * 256));
-        g.gu_passes = passes < 1 ? 1 : (passes > kMaxPass ? kMaxPass : passes);
+        g.gu_passes = passes < 1 ? 1 : (passes > max_pass ? max_pass : passes);
     }
     g.tile_rows_gu = P * g.gu_passes;
     g.tiles_gu = (FF + g.tile_rows_gu - 1) / g.tile_rows_gu;
@@ -764,7 +794,7 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     return g;
 }
 
-template <int QT, int NTERM>
+template <int QT, int NTERM, bool PAIR>
 static hipError_t launch_decode_t(const GemvShape& g, DecodeParams& p, hipStream_t s) {
     // Allow the dynamic LDS the largest shapes need, once per device.
     static std::mutex mu;
@@ -775,13 +805,13 @@ static hipError_t launch_decode_t(const GemvShape& g, DecodeParams& p, hipStream
     {
         std::lock_guard<std::mutex> lock(mu);
         if (!done.count(dev)) {
-            e = hipFuncSetAttribute((const void*)decode_layer_kernel<QT, NTERM>,
+            e = hipFuncSetAttribute((const void*)decode_layer_kernel<QT, NTERM, PAIR>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
             if (e != hipSuccess) return e;
             done.insert(dev);
         }
     }
-    hipLaunchKernelGGL((decode_layer_kernel<QT, NTERM>), dim3(g.grid), dim3(kGemvThreads), g.lds_bytes, s, p);
+    hipLaunchKernelGGL((decode_layer_kernel<QT, NTERM, PAIR>), dim3(g.grid), dim3(kGemvThreads), g.lds_bytes, s, p);
     return hipGetLastError();
 }
 
@@ -831,9 +861,11 @@ hipError_t launch_decode_layer(const GemvShape& g, const void* const* table, con
     hipError_t e;
     const bool bf = x_dtype == 1;
     if (g.qtype == 1)
-        e = bf ? launch_decode_t<1, 1>(g, p, s) : launch_decode_t<1, 2>(g, p, s);
+        e = bf ? launch_decode_t<1, 1, false>(g, p, s) : launch_decode_t<1, 2, false>(g, p, s);
+    else if (!g.gu_pair)
+        e = bf ? launch_decode_t<2, 1, false>(g, p, s) : launch_decode_t<2, 2, false>(g, p, s);
     else
-        e = bf ? launch_decode_t<2, 1>(g, p, s) : launch_decode_t<2, 2>(g, p, s);
+        e = bf ? launch_decode_t<2, 1, true>(g, p, s) : launch_decode_t<2, 2, true>(g, p, s);
     stage_mark(marks, s);
     return e;
 }

@@ -88,6 +88,7 @@ constexpr uint32_t kOnes = 0x3F803F80u;    // bf16 pair (1.0, 1.0)
 constexpr int kCpolSc1 = 16;               // cache policy bits of a buffer load: sc1 (agent coherence)
 constexpr int kRsrcWord3 = 0x00020000;     // buffer resource word 3: 32-bit data format, raw access
 constexpr int kMaxPass = 8;    // gate/up passes per tile (tile rows = P * passes)
+constexpr int kMaxPassPair = 5;   // the same with two block columns a lane (twice the codes a pass)
 
 template <int QT>
 struct QTraits;

@@ -91,6 +91,7 @@ struct GemvShape {
     int H, FF, FFs, qtype;
     float z;
     int gu_passes, tile_rows_gu, tiles_gu, tiles_gu_s;
+    int gu_pair;              // gate/up lanes take two adjacent block columns each
     int max_groups, shared_groups, n_gu;
     int tile_rows_dn, tiles_dn;
     int stage_words;          // `a` words each down workgroup stages in LDS (one token), else 0

@@ -286,6 +286,26 @@ def test_batch_invariance_and_determinism():
         assert torch.equal(yT, y8[:T])
 
 
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_batch_invariance_gemma_shape(x_dtype):
+    """The 4-bit shape with a shared expert, whose one-token gate/up lanes take
+    two adjacent block columns each (88 columns a row): token t's output is
+    still bitwise the same alone and inside a window of 8, and of 3."""
+    w = wl.WORKLOADS["gemma_decode"]
+    arena = wl.DeviceArena(w, device=DEV, layers=[1])
+    desc = moe.layer_desc(w.hidden, w.ff, w.qtype, w.zero_point, w.experts, w.top_k, shared_ff=w.shared_ff)
+    x, logits = wl.device_inputs(w, 1, 0, device=DEV, tokens=8)
+    if x_dtype == "f32":
+        x = x.float()
+    sh = arena.shared_blob(1)
+    y8 = moe.layer_forward(desc, arena.tables[1], x, logits, shared=sh)
+    for t in range(8):
+        y1 = moe.layer_forward(desc, arena.tables[1], x[t:t + 1].contiguous(), logits[t:t + 1].contiguous(), shared=sh)
+        assert torch.equal(y1[0], y8[t]), f"token {t} differs between T=1 and T=8"
+    y3 = moe.layer_forward(desc, arena.tables[1], x[:3].contiguous(), logits[:3].contiguous(), shared=sh)
+    assert torch.equal(y3, y8[:3])
+
+
 def test_identical_experts_ignore_routing():
     w = wl.WORKLOADS["strata_decode"]
     blob = torch.from_numpy(synth.expert_blob(0, 0, 0, w.qk, w.hidden, w.ff, w.sigma)).to(DEV)
