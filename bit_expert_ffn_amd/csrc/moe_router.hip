@@ -6,16 +6,16 @@
 // Every product of a bf16 weight and an fp32 x' is formed in fp32 and summed
 // in fp32.
 //
-// T <= 8 (decode, verify windows): router_gemv_kernel, one wave per expert
-// row (4 per workgroup), a workgroup per 4 experts and tile of tokens.  Each
-// lane issues the loads of all its 16-byte chunks of the weight row (chunks
-// l, l + 64, ...) at once, while the workgroup copies the tile's activation
-// rows (and the scale) into LDS; then, per token, the lane accumulates
+// T <= 8 (decode, verify windows): router_gemv_kernel, one workgroup per
+// expert row, its 256 threads splitting the row's 16-byte chunks; each thread
+// issues the loads of its chunks of the weight row and of the matching
+// activations (and scale) at once; then, per token, it accumulates
 // w * (x * scale) over its chunks in order, and, for the norm, x * x; a fixed
-// DPP tree sums the lanes, and the norm factor 1 / sqrt(mean x^2 + eps)
-// multiplies the sum (a per-token scalar: W (x r s) = r W (x s)).  A token's
-// logits are therefore bitwise the same whatever the other tokens of the
-// window, and a call waits for one round trip to memory.
+// DPP tree sums each wave, the four waves' sums are added in wave order, and
+// the norm factor 1 / sqrt(mean x^2 + eps) multiplies the sum (a per-token
+// scalar: W (x r s) = r W (x s)).  A token's logits are therefore bitwise the
+// same whatever the other tokens of the window, and a call waits for one
+// round trip to memory.
 // T > 8 (prefill): router_gemm_kernel computes 64 x 64 tiles of (tokens x
 // experts) from 32-wide slices of x' and W_r staged in LDS; each tile first
 // computes its tokens' norm factors (one wave per token).
@@ -57,102 +57,105 @@ __device__ __forceinline__ float row_rinv(const RouterParams& p, int t, int lane
     return 1.f / sqrtf(ss / (float)p.H + p.eps);
 }
 
-// x'[t][h0 .. h0 + 7] from the activations (8 consecutive values).
-constexpr int kRtChunks = 8;                  // 16-byte weight chunks a lane holds at once
-constexpr size_t kRtLdsBudget = 64 * 1024;    // activation tile + scale in LDS
+constexpr int kRtCPT = 2;   // 16-byte weight chunks (8 weights) a thread takes per round
 
+// One workgroup per expert row e; thread i of the 256 takes the row's 16-byte
+// chunks i, i + 256, ... (two per round), and every load of a round (the
+// weights, each token's 8 matching activations, the scale) is issued before
+// any product, straight from memory (the activations are read by every
+// workgroup, so from L2).  Per token, a thread accumulates w * (x * scale)
+// over its chunks in order (and x * x for the norm); a fixed DPP tree sums
+// each wave and the four waves' sums are added in wave order.
 template <int XDT>
-__global__ void __launch_bounds__(256) router_gemv_kernel(RouterParams p, int tt) {
-    extern __shared__ __align__(16) uint8_t lds_raw[];
-    constexpr int ES = XDT == 1 ? 2 : 4;       // bytes per activation
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int e = blockIdx.x * 4 + wv;
-    const int t0 = blockIdx.y * tt, nt = min(tt, p.T - t0);
-    const int n_ch = p.H / 8;                  // 16-byte weight chunks of a row
-    const int ec = e < p.E ? e : p.E - 1;      // (a wave past E loads a real row and stores nothing)
-    const uint16_t* row = p.wr + (size_t)ec * p.H;
-    // The tile's activation rows and the scale, into LDS (16 bytes a thread
-    // and pass), while the first weight chunks are on their way.
-    uint4 wch[kRtChunks];
-#pragma unroll
-    for (int i = 0; i < kRtChunks; ++i) {
-        const int c = lane + 64 * i;
-        wch[i] = *reinterpret_cast<const uint4*>(row + 8 * (c < n_ch ? c : 0));
-    }
-    const int x16 = nt * p.H * ES / 16;
-    const uint4* xsrc = reinterpret_cast<const uint4*>((const uint8_t*)p.x + (size_t)t0 * p.H * ES);
-    uint4* xl = reinterpret_cast<uint4*>(lds_raw);
-    for (int i = threadIdx.x; i < x16; i += 256) xl[i] = xsrc[i];
-    float* sl = reinterpret_cast<float*>(lds_raw + (size_t)tt * p.H * ES);
-    if (p.in_scale)
-        for (int i = threadIdx.x; i < p.H / 4; i += 256)
-            reinterpret_cast<float4*>(sl)[i] = reinterpret_cast<const float4*>(p.in_scale)[i];
-    __syncthreads();
+__global__ void __launch_bounds__(256) router_gemv_kernel(RouterParams p) {
+    constexpr int XW = XDT == 1 ? 1 : 2;       // 16-byte words of 8 activations
+    __shared__ float part[4][kSmallT][2];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int e = blockIdx.x;
+    const int T = p.T;
+    const int n_ch = p.H / 8;
+    const uint16_t* row = p.wr + (size_t)e * p.H;
+    const uint8_t* xb = (const uint8_t*)p.x;
     float acc[kSmallT], ss[kSmallT];
 #pragma unroll
     for (int t = 0; t < kSmallT; ++t) acc[t] = ss[t] = 0.f;
-    for (int c0 = 0; c0 < n_ch; c0 += 64 * kRtChunks) {
-        if (c0 > 0) {   // rows longer than 64 * kRtChunks chunks: the next set
+    for (int c0 = 0; c0 < n_ch; c0 += 256 * kRtCPT) {
+        uint4 wch[kRtCPT], xv[kRtCPT][kSmallT][XW];
+        float4 sv[kRtCPT][2];
 #pragma unroll
-            for (int i = 0; i < kRtChunks; ++i) {
-                const int c = c0 + lane + 64 * i;
-                wch[i] = *reinterpret_cast<const uint4*>(row + 8 * (c < n_ch ? c : 0));
+        for (int i = 0; i < kRtCPT; ++i) {
+            const int c = c0 + tid + 256 * i;
+            const int cc = c < n_ch ? c : n_ch - 1;   // clamped: every load unconditional
+            wch[i] = *reinterpret_cast<const uint4*>(row + 8 * cc);
+#pragma unroll
+            for (int t = 0; t < kSmallT; ++t)
+                if (t < T)
+#pragma unroll
+                    for (int q = 0; q < XW; ++q)
+                        xv[i][t][q] = *reinterpret_cast<const uint4*>(xb + ((size_t)t * p.H + 8 * cc) * (XDT == 1 ? 2 : 4) + 16 * q);
+            if (p.in_scale) {
+                sv[i][0] = reinterpret_cast<const float4*>(p.in_scale)[2 * cc];
+                sv[i][1] = reinterpret_cast<const float4*>(p.in_scale)[2 * cc + 1];
             }
         }
 #pragma unroll
-        for (int i = 0; i < kRtChunks; ++i) {
-            const int c = c0 + lane + 64 * i;
-            if (c < n_ch) {
-                const uint32_t w2[4] = {wch[i].x, wch[i].y, wch[i].z, wch[i].w};
-                float w[8], sc[8];
+        for (int i = 0; i < kRtCPT; ++i) {
+            if (c0 + tid + 256 * i >= n_ch) continue;
+            const uint32_t w2[4] = {wch[i].x, wch[i].y, wch[i].z, wch[i].w};
+            float w[8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    w[2 * j] = __uint_as_float(w2[j] << 16);
-                    w[2 * j + 1] = __uint_as_float(w2[j] & 0xFFFF0000u);
-                }
-                if (p.in_scale) {
-                    const float4 a = reinterpret_cast<const float4*>(sl)[2 * c];
-                    const float4 b = reinterpret_cast<const float4*>(sl)[2 * c + 1];
-                    sc[0] = a.x; sc[1] = a.y; sc[2] = a.z; sc[3] = a.w;
-                    sc[4] = b.x; sc[5] = b.y; sc[6] = b.z; sc[7] = b.w;
-                }
+            for (int j = 0; j < 4; ++j) {
+                w[2 * j] = __uint_as_float(w2[j] << 16);
+                w[2 * j + 1] = __uint_as_float(w2[j] & 0xFFFF0000u);
+            }
+            const float sc[8] = {sv[i][0].x, sv[i][0].y, sv[i][0].z, sv[i][0].w,
+                                 sv[i][1].x, sv[i][1].y, sv[i][1].z, sv[i][1].w};
 #pragma unroll
-                for (int t = 0; t < kSmallT; ++t) {
-                    if (t < nt) {
-                        float v[8];
-                        if constexpr (XDT == 1) {
-                            const uint4 u = xl[(t * p.H) / 8 + c];
-                            const uint32_t x2[4] = {u.x, u.y, u.z, u.w};
+            for (int t = 0; t < kSmallT; ++t) {
+                if (t >= T) continue;
+                float v[8];
+                if constexpr (XDT == 1) {
+                    const uint32_t x2[4] = {xv[i][t][0].x, xv[i][t][0].y, xv[i][t][0].z, xv[i][t][0].w};
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                v[2 * j] = __uint_as_float(x2[j] << 16);
-                                v[2 * j + 1] = __uint_as_float(x2[j] & 0xFFFF0000u);
-                            }
-                        } else {
-                            const uint4 a = xl[(t * p.H) / 4 + 2 * c], b = xl[(t * p.H) / 4 + 2 * c + 1];
-                            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
-                            v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-                            v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
-                            v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
-                        }
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            if (p.norm) ss[t] = __builtin_fmaf(v[j], v[j], ss[t]);
-                            const float xs = p.in_scale ? v[j] * sc[j] : v[j];
-                            acc[t] = __builtin_fmaf(w[j], xs, acc[t]);
-                        }
+                    for (int j = 0; j < 4; ++j) {
+                        v[2 * j] = __uint_as_float(x2[j] << 16);
+                        v[2 * j + 1] = __uint_as_float(x2[j] & 0xFFFF0000u);
                     }
+                } else {
+                    const uint4 a = xv[i][t][0], b = xv[i][t][XW - 1];
+                    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+                    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+                    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+                    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (p.norm) ss[t] = __builtin_fmaf(v[j], v[j], ss[t]);
+                    const float xs = p.in_scale ? v[j] * sc[j] : v[j];
+                    acc[t] = __builtin_fmaf(w[j], xs, acc[t]);
                 }
             }
         }
     }
 #pragma unroll
     for (int t = 0; t < kSmallT; ++t) {
-        if (t < nt) {
-            float sum = wave_sum_f32(acc[t]);
-            if (p.norm) sum = sum * (1.f / sqrtf(wave_sum_f32(ss[t]) / (float)p.H + p.eps));
-            if (lane == 0 && e < p.E) p.logits[(size_t)(t0 + t) * p.E + e] = sum;
+        if (t < T) {
+            const float a = wave_sum_f32(acc[t]);
+            const float q = p.norm ? wave_sum_f32(ss[t]) : 0.f;
+            if (lane == 0) {
+                part[wv][t][0] = a;
+                part[wv][t][1] = q;
+            }
         }
+    }
+    __syncthreads();
+    if (tid < T) {
+        float sum = (part[0][tid][0] + part[1][tid][0]) + (part[2][tid][0] + part[3][tid][0]);
+        if (p.norm) {
+            const float q = (part[0][tid][1] + part[1][tid][1]) + (part[2][tid][1] + part[3][tid][1]);
+            sum = sum * (1.f / sqrtf(q / (float)p.H + p.eps));
+        }
+        p.logits[(size_t)tid * p.E + e] = sum;
     }
 }
 
@@ -234,14 +237,8 @@ hipError_t launch_router(const void* wr, const float* in_scale, int norm, float 
     p.eps = eps;
     const bool bf = x_dtype == 1;
     if (T <= kSmallT) {
-        // As many tokens per tile as the LDS budget holds (one or more tiles).
-        const size_t es = bf ? 2 : 4, sc = in_scale ? (size_t)4 * H : 0;
-        int tt = T;
-        while (tt > 1 && (size_t)tt * H * es + sc > kRtLdsBudget) --tt;
-        const size_t lds = (size_t)tt * H * es + sc;
-        const dim3 grid((E + 3) / 4, (T + tt - 1) / tt);
-        if (bf) hipLaunchKernelGGL(router_gemv_kernel<1>, grid, dim3(256), lds, s, p, tt);
-        else hipLaunchKernelGGL(router_gemv_kernel<0>, grid, dim3(256), lds, s, p, tt);
+        if (bf) hipLaunchKernelGGL(router_gemv_kernel<1>, dim3(E), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL(router_gemv_kernel<0>, dim3(E), dim3(256), 0, s, p);
         return hipGetLastError();
     }
     const dim3 grid((T + kRtTileT - 1) / kRtTileT, (E + kRtTileE - 1) / kRtTileE);

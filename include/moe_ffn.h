@@ -239,11 +239,14 @@ moe_status moe_layer_forward_ex(const moe_layer_desc* desc, const moe_layer_opts
  * Measurement variant of moe_layer_forward: the same checks and the same work,
  * plus caller-created HIP events (hipEvent_t passed as void*, timing enabled)
  * recorded on `stream` at the boundaries of the kernels the call launches:
- * events[0] before the first kernel, events[i] after the i-th.  Boundaries
+ * events[0] before the first stage, events[i] after the i-th.  Boundaries
  * past n_events are not recorded.  *n_kernels (if not NULL) receives the
- * number of kernels launched: 1 on the decode/verify path (the fused layer
- * kernel); 6 on the prefill path (routing, expert histogram, slot placement,
- * gate/up + SwiGLU, down, combine).  Events are not owned by the library.
+ * number of stages: 1 on the decode/verify path (the fused layer kernel); 6 on
+ * the prefill path (routing, expert histogram, slot placement, gate/up +
+ * SwiGLU, down, combine).  Each stage is one kernel except slot placement,
+ * which is three launches (per-block counts, placement, and the activations'
+ * conversion to the matrix-core operand planes).  Events are not owned by the
+ * library.
  * A failing hipEventRecord returns MOE_ERR_DEVICE after the work is enqueued.
  */
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* const* expert_table,
