@@ -418,8 +418,8 @@ def bench_prefill(args, w):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50 decode, 10 prefill)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5 decode, 2 prefill)")
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 100 decode, 10 prefill)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10 decode, 2 prefill)")
     ap.add_argument("--workload", default="strata_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
@@ -470,8 +470,8 @@ def main():
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    K = args.steps if args.steps is not None else 50
-    W = args.warmup if args.warmup is not None else 5
+    K = args.steps if args.steps is not None else 100
+    W = args.warmup if args.warmup is not None else 10
     nsteps = K + W
 
     t0 = time.time()
