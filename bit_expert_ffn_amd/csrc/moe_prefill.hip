@@ -132,41 +132,102 @@ __device__ __forceinline__ bool pair_on(const PrefillParams& p, int q) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Bucketing: counts, offsets, tile list (one workgroup).
+// Bucketing: a stable counting sort of the (token, slot) pairs by expert, over
+// blocks of kPlaceBlock pairs (the pairs of one expert stay in (token, slot)
+// order).  Three launches: each block's count of every expert; the totals,
+// offsets and tile list, and each block's base per expert; each pair's
+// position.
 // ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) prefill_blockcount_kernel(PrefillParams p) {
+    __shared__ int h[kMaxE];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    const int n = p.T * p.k, q0 = b * kPlaceBlock, q1 = min(n, q0 + kPlaceBlock);
+    for (int e = tid; e < p.E; e += 256) h[e] = 0;
+    __syncthreads();
+    for (int q = q0 + tid; q < q1; q += 256)
+        if (pair_on(p, q)) atomicAdd(&h[p.ids[q]], 1);   // counts: order-free
+    __syncthreads();
+    for (int e = tid; e < p.E; e += 256) p.bcount[(size_t)b * p.E + e] = h[e];
+}
+
+// One workgroup: each expert's total over the blocks, the offsets (in expert
+// order) and the tile list; then each block's count of an expert is replaced
+// by that block's base for it, offset + the expert's pairs in earlier blocks.
 __global__ void __launch_bounds__(1024) prefill_count_kernel(PrefillParams p) {
+    static_assert(kMaxE <= 1024, "one thread per expert in the scan");
     __shared__ int hist[kMaxE + 1];
+    __shared__ int off_l[kMaxE + 1];
     __shared__ int tbase[kMaxE + 2];
     const int tid = threadIdx.x;
     const int n = p.T * p.k;
-    for (int e = tid; e < p.E; e += blockDim.x) hist[e] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += blockDim.x)   // counts: order-free
-        if (pair_on(p, i)) atomicAdd(&hist[p.ids[i]], 1);
-    __syncthreads();
-    if (tid == 0) {
-        int off = 0, tb = 0;
-        for (int e = 0; e < p.E; ++e) {
-            p.counts[e] = hist[e];
-            p.offsets[e] = off;
-            tbase[e] = tb;
-            off += hist[e];
-            tb += (hist[e] + kRowsPerTile - 1) / kRowsPerTile;
+    const int nb = (n + kPlaceBlock - 1) / kPlaceBlock;
+    int cnt = 0, nt_e = 0;   // thread e: expert e's pairs and row tiles
+    if (tid < p.E) {
+        for (int b0 = 0; b0 < nb; b0 += 8) {   // eight block counts in flight at a time
+            int c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = b0 + u < nb ? p.bcount[(size_t)(b0 + u) * p.E + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cnt += c[u];
         }
-        p.offsets[p.E] = off;
-        tbase[p.E] = tb;
-        int nt = tb;
-        if (p.shared) nt += (p.T + kRowsPerTile - 1) / kRowsPerTile;
-        *p.ntiles = nt;
+        nt_e = (cnt + kRowsPerTile - 1) / kRowsPerTile;
+        hist[tid] = cnt;
+        off_l[tid] = cnt;
+        tbase[tid] = nt_e;
+    }
+    __syncthreads();
+    // Inclusive scans of the pair and tile counts over the experts (integer
+    // sums: exact in any order), then the exclusive offsets.
+    for (int d = 1; d < p.E; d <<= 1) {
+        int a = 0, t = 0;
+        if (tid < p.E && tid >= d) {
+            a = off_l[tid - d];
+            t = tbase[tid - d];
+        }
+        __syncthreads();
+        if (tid < p.E && tid >= d) {
+            off_l[tid] += a;
+            tbase[tid] += t;
+        }
+        __syncthreads();
+    }
+    int incl = 0, tincl = 0;
+    if (tid < p.E) {
+        incl = off_l[tid];
+        tincl = tbase[tid];
+    }
+    __syncthreads();
+    if (tid < p.E) {
+        off_l[tid] = incl - cnt;
+        tbase[tid] = tincl - nt_e;
+        p.counts[tid] = cnt;
+        p.offsets[tid] = incl - cnt;
+        if (tid == p.E - 1) {
+            off_l[p.E] = incl;
+            tbase[p.E] = tincl;
+            p.offsets[p.E] = incl;
+            *p.ntiles = tincl + (p.shared ? (p.T + kRowsPerTile - 1) / kRowsPerTile : 0);
+        }
     }
     __syncthreads();
     for (int e = tid; e < p.E; e += blockDim.x) {
-        const int cnt = hist[e], o = p.offsets[e];
-        for (int i = 0; i * kRowsPerTile < cnt; ++i) {
+        const int ce = hist[e], o = off_l[e];
+        for (int i = 0; i * kRowsPerTile < ce; ++i) {
             int* t = p.tiles + 3 * (tbase[e] + i);
             t[0] = e;
             t[1] = o + i * kRowsPerTile;
-            t[2] = min(kRowsPerTile, cnt - i * kRowsPerTile);
+            t[2] = min(kRowsPerTile, ce - i * kRowsPerTile);
+        }
+        int run = o;
+        for (int b0 = 0; b0 < nb; b0 += 8) {
+            int c[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c[u] = b0 + u < nb ? p.bcount[(size_t)(b0 + u) * p.E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (b0 + u < nb) p.bcount[(size_t)(b0 + u) * p.E + e] = run;
+                run += c[u];
+            }
         }
     }
     if (p.shared) {
@@ -180,55 +241,48 @@ __global__ void __launch_bounds__(1024) prefill_count_kernel(PrefillParams p) {
     }
 }
 
-// Stable counting sort of the (token, slot) pairs by expert, in two passes
-// over blocks of kPlaceBlock pairs (the pairs' order within an expert is
-// (token, slot) order).  Pass 1: each block's count of every expert.
-__global__ void __launch_bounds__(256) prefill_blockcount_kernel(PrefillParams p) {
-    __shared__ int h[kMaxE];
-    const int tid = threadIdx.x, b = blockIdx.x;
-    const int n = p.T * p.k, q0 = b * kPlaceBlock, q1 = min(n, q0 + kPlaceBlock);
-    for (int e = tid; e < p.E; e += 256) h[e] = 0;
-    __syncthreads();
-    for (int q = q0 + tid; q < q1; q += 256)
-        if (pair_on(p, q)) atomicAdd(&h[p.ids[q]], 1);   // counts: order-free
-    __syncthreads();
-    for (int e = tid; e < p.E; e += 256) p.bcount[(size_t)b * p.E + e] = h[e];
-}
-
-// Pass 2: a pair's sorted position is its expert's offset, plus the pairs of
-// that expert in earlier blocks, plus those earlier in its own block (each
-// pair compares its expert with every earlier one of the block, read from
-// LDS: the same address for every lane of a wave at each step).
+// A pair's position: its block's base for its expert, plus the pairs of that
+// expert earlier in the block.  The block goes by in chunks of 256 pairs (one
+// a thread); within a wave, the lanes holding the same expert are found with
+// one ballot per bit of the expert id, and a lane's rank among them is the
+// count of those below it; a wave's count per expert goes to LDS, where the
+// later waves of the chunk, and then the running count of the block, take it.
 __global__ void __launch_bounds__(256) prefill_place_kernel(PrefillParams p) {
-    __shared__ int base[kMaxE];
-    __shared__ __align__(16) int eid[kPlaceBlock];
-    const int tid = threadIdx.x, b = blockIdx.x;
+    __shared__ int run[kMaxE];        // the block's base + its pairs in earlier chunks, per expert
+    __shared__ int wc[4][kMaxE];      // this chunk: each wave's pairs of each expert
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, b = blockIdx.x;
     const int n = p.T * p.k, q0 = b * kPlaceBlock, len = min(kPlaceBlock, n - q0);
     for (int e = tid; e < p.E; e += 256) {
-        int v = p.offsets[e];
-        for (int b0 = 0; b0 < b; b0 += 8) {   // eight block counts in flight at a time
-            int c[8];
+        run[e] = p.bcount[(size_t)b * p.E + e];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) c[u] = b0 + u < b ? p.bcount[(size_t)(b0 + u) * p.E + e] : 0;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v += c[u];
-        }
-        base[e] = v;
+        for (int w = 0; w < 4; ++w) wc[w][e] = 0;
     }
-    for (int i = tid; i < kPlaceBlock; i += 256) eid[i] = (i < len && pair_on(p, q0 + i)) ? p.ids[q0 + i] : -1;
+    const int nbits = p.E > 1 ? 32 - __clz(p.E - 1) : 0;
     __syncthreads();
-    for (int i = tid; i < len; i += 256) {
-        const int e = eid[i];
-        if (e < 0) continue;
-        int r = 0, j = 0;
-        for (; j + 4 <= i; j += 4) {
-            const int4 v = *reinterpret_cast<const int4*>(&eid[j]);
-            r += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+    for (int c0 = 0; c0 < len; c0 += 256) {
+        const int i = c0 + tid;
+        const int e = (i < len && pair_on(p, q0 + i)) ? p.ids[q0 + i] : -1;
+        uint64_t m = __ballot(e >= 0);   // every lane votes in each ballot
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool v = e >= 0 && ((e >> bit) & 1);
+            const uint64_t bb = __ballot(v);
+            m &= v ? bb : ~bb;
         }
-        for (; j < i; ++j) r += eid[j] == e;
-        const int pos = base[e] + r;
-        p.perm[pos] = (q0 + i) / p.k;
-        p.inv[q0 + i] = pos;
+        const int rw = lanes_below(m);   // for e >= 0: m holds the lanes whose expert is e
+        if (e >= 0 && rw == 0) wc[wv][e] = __popcll(m);
+        __syncthreads();
+        if (e >= 0) {
+            int pos = run[e] + rw;
+            for (int w = 0; w < wv; ++w) pos += wc[w][e];
+            p.perm[pos] = (q0 + i) / p.k;
+            p.inv[q0 + i] = pos;
+        }
+        __syncthreads();
+        if (e >= 0 && rw == 0) {
+            atomicAdd(&run[e], __popcll(m));   // integer sums: order-free
+            wc[wv][e] = 0;
+        }
+        __syncthreads();
     }
     if (p.shared && b == 0)
         for (int t = tid; t < p.T; t += 256) p.perm[n + t] = t;
@@ -264,23 +318,41 @@ __global__ void prefill_identity_kernel(int* ids, float* w, int T) {
 // values, position 2q + r holds value q + r*G/2: the order in which the
 // dequantised weight pairs come out of one code word.
 // ---------------------------------------------------------------------------------------------
+// The values of one 16-byte word of activations (8 bf16 or 4 fp32), widened.
 template <int XDT>
-__device__ __forceinline__ float load_x(const void* x, size_t i) {
-    if constexpr (XDT == 1) return __uint_as_float((uint32_t)((const uint16_t*)x)[i] << 16);
-    else return ((const float*)x)[i];
+__device__ __forceinline__ void word_values(const uint4 u, float* v) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (XDT == 1) {
+            v[2 * j] = __uint_as_float(w[j] << 16);
+            v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        } else {
+            v[j] = __uint_as_float(w[j]);
+        }
+    }
 }
 
 template <int QT, int XDT>
 __global__ void __launch_bounds__(256) prefill_xprep_kernel(PrefillParams p) {
     constexpr int G = QT == 1 ? 16 : 8;
+    constexpr int VPW = XDT == 1 ? 8 : 4;   // values per 16-byte word
+    constexpr int WPG = G / VPW;             // words per group
     __shared__ uint32_t red[4];
     const int t = blockIdx.x;
     const int H = p.H;
     const size_t base = (size_t)t * H;
+    // The row in 16-byte words (rows are 64-byte multiples, x is 16-byte aligned).
+    const uint4* xr = reinterpret_cast<const uint4*>((const uint8_t*)p.x + base * (XDT == 1 ? 2 : 4));
     uint32_t mx = 0;   // |x| bit patterns order like their values (NaN above every number)
-    for (int i = threadIdx.x; i < H; i += 256) {
-        const uint32_t b = __float_as_uint(load_x<XDT>(p.x, base + i)) & 0x7FFFFFFFu;
-        mx = b > mx ? b : mx;
+    for (int i = threadIdx.x; i < H / VPW; i += 256) {
+        float v[VPW];
+        word_values<XDT>(xr[i], v);
+#pragma unroll
+        for (int j = 0; j < VPW; ++j) {
+            const uint32_t b = __float_as_uint(v[j]) & 0x7FFFFFFFu;
+            mx = b > mx ? b : mx;
+        }
     }
     mx = wave_max_u32(mx);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
@@ -294,7 +366,9 @@ __global__ void __launch_bounds__(256) prefill_xprep_kernel(PrefillParams p) {
     for (int g = threadIdx.x; g < H / G; g += 256) {
         float v[G];
 #pragma unroll
-        for (int i = 0; i < G; ++i) v[i] = __builtin_ldexpf(load_x<XDT>(p.x, base + (size_t)g * G + i), -e);
+        for (int q = 0; q < WPG; ++q) word_values<XDT>(xr[(size_t)g * WPG + q], v + q * VPW);
+#pragma unroll
+        for (int i = 0; i < G; ++i) v[i] = __builtin_ldexpf(v[i], -e);
         _Float16 oh[G], ol[G];
 #pragma unroll
         for (int q = 0; q < G / 2; ++q) {
@@ -904,13 +978,11 @@ hipError_t launch_prefill_layer(const void* const* table, const void* single, co
     else
         (void)launch_route_topk(logits, T, E, k, renorm, ids, w, s);
     stage_mark(marks, s);
+    const unsigned n_pb = (unsigned)((T * k + kPlaceBlock - 1) / kPlaceBlock);
+    hipLaunchKernelGGL(prefill_blockcount_kernel, dim3(n_pb), dim3(256), 0, s, p);
     hipLaunchKernelGGL(prefill_count_kernel, dim3(1), dim3(1024), 0, s, p);
     stage_mark(marks, s);
-    {
-        const unsigned nb = (unsigned)((T * k + kPlaceBlock - 1) / kPlaceBlock);
-        hipLaunchKernelGGL(prefill_blockcount_kernel, dim3(nb), dim3(256), 0, s, p);
-        hipLaunchKernelGGL(prefill_place_kernel, dim3(nb), dim3(256), 0, s, p);
-    }
+    hipLaunchKernelGGL(prefill_place_kernel, dim3(n_pb), dim3(256), 0, s, p);
     if (qtype == 2) {
         if (x_dtype == 1) hipLaunchKernelGGL((prefill_xprep_kernel<2, 1>), dim3(T), dim3(256), 0, s, p);
         else hipLaunchKernelGGL((prefill_xprep_kernel<2, 0>), dim3(T), dim3(256), 0, s, p);

@@ -243,10 +243,11 @@ moe_status moe_layer_forward_ex(const moe_layer_desc* desc, const moe_layer_opts
  * past n_events are not recorded.  *n_kernels (if not NULL) receives the
  * number of stages: 1 on the decode/verify path (the fused layer kernel); 6 on
  * the prefill path (routing, expert histogram, slot placement, gate/up +
- * SwiGLU, down, combine).  Each stage is one kernel except slot placement,
- * which is three launches (per-block counts, placement, and the activations'
- * conversion to the matrix-core operand planes).  Events are not owned by the
- * library.
+ * SwiGLU, down, combine).  Each stage is one kernel except the expert
+ * histogram (two launches: per-block counts, then the totals, offsets, tile
+ * list and per-block bases) and slot placement (two: the placement, then the
+ * activations' conversion to the matrix-core operand planes).  Events are not
+ * owned by the library.
  * A failing hipEventRecord returns MOE_ERR_DEVICE after the work is enqueued.
  */
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const void* const* expert_table,
