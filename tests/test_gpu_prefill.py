@@ -64,6 +64,9 @@ def _small_layer(qtype, E, k, H, FF, T, xd, shared_ff, zipf, seed):
     (2, 16, 4, 256, 128, 257, "bf16", 192, 0.0),
     (1, 8, 2, 256, 128, 64, "f32", 0, 0.0),
     (2, 64, 8, 512, 256, 300, "bf16", 0, 1.2),
+    # 37 experts (6-bit ids, not a power of two), 2,350 pairs: three placement
+    # blocks, the last ragged, with skewed routing
+    (1, 37, 5, 256, 128, 470, "bf16", 0, 1.0),
 ])
 def test_layer_prefill_matches_oracle(qtype, E, k, H, FF, T, xd, shared_ff, zipf):
     y, y_ref = _small_layer(qtype, E, k, H, FF, T, xd, shared_ff, zipf, seed=T)
