@@ -18,6 +18,26 @@ static thread_local char g_err[512] = "";
 
 // Bound of every kernel wait (polls); negative = the default.
 static std::atomic<long> g_wait_polls{-1};
+
+// Compute units of the current device (the one-token kernel's down tiling
+// depends on it), cached per device.
+static hipError_t device_cus(int* out) {
+    static std::mutex mu;
+    static std::map<int, int> cus;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cus.find(dev);
+    if (it == cus.end()) {
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        it = cus.emplace(dev, n).first;
+    }
+    *out = it->second;
+    return hipSuccess;
+}
 long wait_polls() {
     const long v = g_wait_polls.load(std::memory_order_relaxed);
     return v < 0 ? kDefaultWaitPolls : v;
@@ -236,7 +256,10 @@ static moe_status run_layer(int T, int E, int k, int renorm, const moe_expert_de
             return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, L.total);
         hipError_t e;
         if (T == 1) {
-            const GemvShape g = gemv_shape(ed.hidden, ed.ff, FFs, ed.qtype, ed.zero_point, T, k);
+            int n_cu = 0;
+            e = device_cus(&n_cu);
+            if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "device query: %s", hipGetErrorString(e));
+            const GemvShape g = gemv_shape(ed.hidden, ed.ff, FFs, ed.qtype, ed.zero_point, T, k, n_cu);
             if (g.lds_bytes > 128 * 1024)
                 return fail(MOE_ERR_UNSUPPORTED, "decode tile needs %zu bytes of LDS", g.lds_bytes);
             e = run_router(L.logits);

@@ -1,4 +1,5 @@
 // Fused one-token decode layer (see moe_gemv_common.h for the GEMV scheme).
+#include <algorithm>
 #include <mutex>
 #include <set>
 
@@ -36,6 +37,7 @@ namespace moe {
 // nothing else, so no wait runs on stale shared state.
 // ---------------------------------------------------------------------------------------------
 constexpr size_t kDecodeLdsBudget = 112 * 1024;   // dynamic LDS of the fused decode kernel
+constexpr size_t kDecodeStaticLds = 6 * 1024;      // its static LDS (the routing state), rounded up
 constexpr int kMaxRowsDn = 12;               // H rows per down workgroup
 // Down rows one thread prefetches: as many as the registers hold without
 // spilling (2-bit blocks decode into more registers than 4-bit ones).
@@ -724,7 +726,7 @@ __global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodePar
 // ---------------------------------------------------------------------------------------------
 // Host side of the decode path.
 // ---------------------------------------------------------------------------------------------
-GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
+GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k, int n_cu) {
     GemvShape g{};
     const int qk = codes_per_block(qtype);
     const int NT = 1;   // one token (T == 1)
@@ -758,9 +760,20 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     const int per_expert = (T + NT - 1) / NT;
     g.shared_groups = FFs ? per_expert : 0;
     g.n_gu = g.max_groups * g.tiles_gu + g.shared_groups * g.tiles_gu_s;
-    // About 256 down workgroups of at most kMaxRowsDn rows, fewer rows if the
-    // partial sums of every (unit, row, token) would not fit in LDS.  The row
-    // count does not change any summation order.
+    // One token: the arranged activation slices follow the gate/up partials
+    // (sized for fp32 activations, the larger slice).
+    const int ncol_gu = nblk_gu % 2 == 0 ? nblk_gu / 2 : nblk_gu;   // lane pairs add their partials first
+    const size_t part_gu = (size_t)2 * g.tile_rows_gu * ((ncol_gu + 3) & ~3) * NT * 4;
+    g.x_off = T == 1 ? (int)(part_gu / 4) : -1;
+    const int sw = ((qk == 64 ? 64 : 32) + (qk == 64 ? 3 : 1) + 1 + 3) & ~3;
+    const size_t lds_gu = part_gu + (T == 1 ? (size_t)nblk_gu * sw * 4 : 0);
+    // Down workgroups own tiles of r output rows.  The row count changes no
+    // summation order; it sets the time of the busiest CU, which runs
+    // ceil(tiles / CUs) tiles of r rows each.  r is the value that makes that
+    // product smallest (the larger r on a tie) among those whose partial sums
+    // fit in LDS and with which every workgroup of the launch is resident at
+    // once (three a CU while LDS allows; a workgroup that waits to be
+    // dispatched lengthens the launch by a whole tile time).
     const int nb_r = FF / qk, nb_s = FFs / qk;
     const size_t units = (size_t)g.max_groups * nb_r + (size_t)g.shared_groups * nb_s;
     // partials padded to 4 columns per (group, row, token), plus one sum each
@@ -771,24 +784,34 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k) {
     // units, S = 256 / units threads share a unit's rows.
     int s_min = (int)(kGemvThreads / units);
     s_min = s_min < 1 ? 1 : s_min;
-    int rows = (H + 255) / 256;
-    rows = rows < 1 ? 1 : (rows > kMaxRowsDn ? kMaxRowsDn : rows);
-    if (rows > rows_per_thread(qtype) * s_min) rows = rows_per_thread(qtype) * s_min;
+    int rows_cap = rows_per_thread(qtype) * s_min;
+    rows_cap = rows_cap > kMaxRowsDn ? kMaxRowsDn : rows_cap;
     // One token: the `a` words are staged in LDS ahead of the partials.
     const long words = (long)g.max_groups * FF + FFs;
     g.stage_words = (T == 1 && words <= kStageMaxWords) ? (int)words : 0;
     const size_t stage = g.stage_words ? (size_t)stage_bytes(g.stage_words) : 0;
-    while (rows > 1 && per_row * rows + stage > kDecodeLdsBudget) --rows;
+    const int cus = n_cu > 0 ? n_cu : 256;
+    int rows = 0;
+    long best = 0;
+    for (int r = rows_cap; r >= 1; --r) {
+        const size_t lds = std::max(per_row * r + stage, lds_gu);
+        if (per_row * r + stage > kDecodeLdsBudget) continue;
+        const int tiles = (H + r - 1) / r;
+        const long per_cu = std::min<long>(3, (long)(160 * 1024) / (long)(lds + kDecodeStaticLds));
+        if ((long)g.n_gu + tiles + 1 > per_cu * cus) continue;
+        const long cost = (long)((tiles + cus - 1) / cus) * r;
+        if (rows == 0 || cost < best) {
+            rows = r;
+            best = cost;
+        }
+    }
+    if (rows == 0) {   // nothing fits every workgroup at once: the largest tile LDS allows
+        rows = rows_cap;
+        while (rows > 1 && per_row * rows + stage > kDecodeLdsBudget) --rows;
+    }
     g.tile_rows_dn = rows;
     g.tiles_dn = (H + rows - 1) / rows;
     const size_t lds_dn = per_row * rows + stage;
-    // One token: the arranged activation slices follow the gate/up partials
-    // (sized for fp32 activations, the larger slice).
-    const int ncol_gu = nblk_gu % 2 == 0 ? nblk_gu / 2 : nblk_gu;   // lane pairs add their partials first
-    const size_t part_gu = (size_t)2 * g.tile_rows_gu * ((ncol_gu + 3) & ~3) * NT * 4;
-    g.x_off = T == 1 ? (int)(part_gu / 4) : -1;
-    const int sw = ((qk == 64 ? 64 : 32) + (qk == 64 ? 3 : 1) + 1 + 3) & ~3;
-    const size_t lds_gu = part_gu + (T == 1 ? (size_t)nblk_gu * sw * 4 : 0);
     g.lds_bytes = lds_dn > lds_gu ? lds_dn : lds_gu;
     g.grid = g.n_gu + g.tiles_dn + 1;   // + the workgroup that resets the shared state
     return g;

@@ -117,7 +117,8 @@ size_t window_sync_bytes(int k, int n_chunks);
 SmallLayout small_layout(int T, int k, int E, int H, int FF, int FFs, int qtype);
 size_t small_fixed_bytes(int k, int H, int FF, int FFs, int qtype);   // sync + a + as + d: where every layout's own regions start
 LargeLayout large_layout(int T, int k, int E, int H, int FF, int FFs, int qtype);
-GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k);
+// n_cu: compute units of the device the call runs on (0: 256).
+GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k, int n_cu);
 
 // Caller-owned HIP events recorded on the launch stream at kernel boundaries
 // (measurement entry point): boundary 0 before the first kernel, boundary i
