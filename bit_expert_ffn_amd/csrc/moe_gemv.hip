@@ -743,16 +743,28 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k, i
     g.gu_pair = P2 * (nblk_gu / 2) > P1 * nblk_gu ? 1 : 0;
     const int P = g.gu_pair ? P2 : P1;
     const int max_pass = g.gu_pair ? kMaxPassPair : kMaxPass;
+    // Passes per gate/up workgroup (tile rows = P * passes): the count that
+    // makes the busiest CU's work, ceil(tiles / CUs) x passes, smallest (the
+    // larger count on a tie), with every gate/up workgroup resident at once.
+    // Strata decode: 220 tiles of 5 passes (one a CU); Gemma, with two block
+    // columns a lane: 394 tiles of 4 passes rather than 317 of 5.
+    const int cus = n_cu > 0 ? n_cu : 256;
     g.max_groups = T * k;
-    // Enough passes per gate/up workgroup that at most about 256 of them (one
-    // per CU) cover the routed experts' FF rows: each gate/up wave then has a
-    // SIMD to itself, where a second workgroup on a CU would double the
-    // slowest tile's compute (Strata decode: 220 tiles of 5 passes run 0.8%
-    // faster than 360 of 3).
     {
-        const long rows_all = (long)g.max_groups * FF;
-        int passes = (int)((rows_all + (long)P * 256 - 1) / ((long)P * 256));
-        g.gu_passes = passes < 1 ? 1 : (passes > max_pass ? max_pass : passes);
+        const int sg = FFs ? (T + NT - 1) / NT : 0;
+        g.gu_passes = 0;
+        long best = 0;
+        for (int pp = max_pass; pp >= 1; --pp) {
+            const int tr = P * pp;
+            const long tiles = (long)g.max_groups * ((FF + tr - 1) / tr) + (long)sg * (FFs ? (FFs + tr - 1) / tr : 0);
+            if (tiles + 1 > 3L * cus) continue;
+            const long cost = (tiles + cus - 1) / cus * pp;
+            if (g.gu_passes == 0 || cost < best) {
+                g.gu_passes = pp;
+                best = cost;
+            }
+        }
+        if (g.gu_passes == 0) g.gu_passes = max_pass;   // no count keeps them all resident: the fewest tiles
     }
     g.tile_rows_gu = P * g.gu_passes;
     g.tiles_gu = (FF + g.tile_rows_gu - 1) / g.tile_rows_gu;
@@ -790,7 +802,6 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k, i
     const long words = (long)g.max_groups * FF + FFs;
     g.stage_words = (T == 1 && words <= kStageMaxWords) ? (int)words : 0;
     const size_t stage = g.stage_words ? (size_t)stage_bytes(g.stage_words) : 0;
-    const int cus = n_cu > 0 ? n_cu : 256;
     int rows = 0;
     long best = 0;
     for (int r = rows_cap; r >= 1; --r) {
