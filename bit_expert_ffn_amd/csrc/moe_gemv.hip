@@ -260,12 +260,12 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         const int f = f0 + m * P + rp;
         if (m < p.gu_passes && active && f < rows) {
             float og[NT], ou[NT];
-            block_dot<QT, NTERM, NT>(cg[m][0], scale_at_use(sg_[m][0]), xs[0], ntok, og);
-            block_dot<QT, NTERM, NT>(cu[m][0], scale_at_use(su_[m][0]), xs[0], ntok, ou);
+            block_dot_pair<QT, NTERM, NT>(cg[m][0], scale_at_use(sg_[m][0]), cu[m][0], scale_at_use(su_[m][0]), xs[0],
+                                          ntok, og, ou);
             if constexpr (PAIR) {
                 float og1[NT], ou1[NT];
-                block_dot<QT, NTERM, NT>(cg[m][BPL - 1], scale_at_use(sg_[m][BPL - 1]), xs[BPL - 1], ntok, og1);
-                block_dot<QT, NTERM, NT>(cu[m][BPL - 1], scale_at_use(su_[m][BPL - 1]), xs[BPL - 1], ntok, ou1);
+                block_dot_pair<QT, NTERM, NT>(cg[m][BPL - 1], scale_at_use(sg_[m][BPL - 1]), cu[m][BPL - 1],
+                                              scale_at_use(su_[m][BPL - 1]), xs[BPL - 1], ntok, og1, ou1);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     og[t] = og[t] + og1[t];
@@ -743,22 +743,40 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k, i
     g.gu_pair = P2 * (nblk_gu / 2) > P1 * nblk_gu ? 1 : 0;
     const int P = g.gu_pair ? P2 : P1;
     const int max_pass = g.gu_pair ? kMaxPassPair : kMaxPass;
-    // Passes per gate/up workgroup (tile rows = P * passes): the count that
-    // makes the busiest CU's work, ceil(tiles / CUs) x passes, smallest (the
-    // larger count on a tie), with every gate/up workgroup resident at once.
-    // Strata decode: 220 tiles of 5 passes (one a CU); Gemma, with two block
-    // columns a lane: 394 tiles of 4 passes rather than 317 of 5.
+    // Passes per gate/up workgroup (tile rows = P * passes).  The busiest CU
+    // holds k = ceil(tiles / CUs) tiles, one wave each on every SIMD, and
+    // runs k x passes passes of block products; k waves a SIMD hide each
+    // other's dependency stalls, so a pass costs less with more of them.
+    // Cost k x passes x w(k), with w(1..3) = 57, 45, 42: the cycles per
+    // instruction of these products measured with one wave a SIMD (5.7), and
+    // a fit to the sweep of pass counts at both decode shapes.  Counts whose
+    // gate/up tiles, with the fewest down tiles (the most rows a down tile
+    // takes), would not all be resident at once (three a CU) are skipped: a
+    // down workgroup dispatched late starts its routing and prefetch late.
+    // The larger count wins a tie.  Strata decode: 540 tiles of 2 passes;
+    // Gemma, with two block columns a lane: 394 tiles of 4 passes.
     const int cus = n_cu > 0 ? n_cu : 256;
     g.max_groups = T * k;
+    const int nb_r = FF / qk, nb_s = FFs / qk;
+    const size_t units = (size_t)g.max_groups * nb_r + (size_t)(FFs ? (T + NT - 1) / NT : 0) * nb_s;
+    // A down thread prefetches at most rows_per_thread rows of its unit;
+    // with few units, S = 256 / units threads share a unit's rows.
+    int s_min = (int)(kGemvThreads / units);
+    s_min = s_min < 1 ? 1 : s_min;
+    int rows_cap = rows_per_thread(qtype) * s_min;
+    rows_cap = rows_cap > kMaxRowsDn ? kMaxRowsDn : rows_cap;
     {
         const int sg = FFs ? (T + NT - 1) / NT : 0;
+        const long fewest_dn = (H + rows_cap - 1) / rows_cap;
+        static const int w[4] = {0, 57, 45, 42};
         g.gu_passes = 0;
         long best = 0;
         for (int pp = max_pass; pp >= 1; --pp) {
             const int tr = P * pp;
             const long tiles = (long)g.max_groups * ((FF + tr - 1) / tr) + (long)sg * (FFs ? (FFs + tr - 1) / tr : 0);
-            if (tiles + 1 > 3L * cus) continue;
-            const long cost = (tiles + cus - 1) / cus * pp;
+            const long kk = (tiles + cus - 1) / cus;
+            if (kk > 3 || tiles + fewest_dn + 1 > 3L * cus) continue;
+            const long cost = kk * pp * w[kk];
             if (g.gu_passes == 0 || cost < best) {
                 g.gu_passes = pp;
                 best = cost;
@@ -786,18 +804,10 @@ GemvShape gemv_shape(int H, int FF, int FFs, int qtype, float z, int T, int k, i
     // fit in LDS and with which every workgroup of the launch is resident at
     // once (three a CU while LDS allows; a workgroup that waits to be
     // dispatched lengthens the launch by a whole tile time).
-    const int nb_r = FF / qk, nb_s = FFs / qk;
-    const size_t units = (size_t)g.max_groups * nb_r + (size_t)g.shared_groups * nb_s;
     // partials padded to 4 columns per (group, row, token), plus one sum each
     const size_t per_row =
         ((size_t)g.max_groups * ((nb_r + 3) & ~3) + (size_t)g.shared_groups * ((nb_s + 3) & ~3) + g.max_groups +
          g.shared_groups) * NT * 4;
-    // One thread prefetches at most rows_per_thread rows of its unit; with few
-    // units, S = 256 / units threads share a unit's rows.
-    int s_min = (int)(kGemvThreads / units);
-    s_min = s_min < 1 ? 1 : s_min;
-    int rows_cap = rows_per_thread(qtype) * s_min;
-    rows_cap = rows_cap > kMaxRowsDn ? kMaxRowsDn : rows_cap;
     // One token: the `a` words are staged in LDS ahead of the partials.
     const long words = (long)g.max_groups * FF + FFs;
     g.stage_words = (T == 1 && words <= kStageMaxWords) ? (int)words : 0;

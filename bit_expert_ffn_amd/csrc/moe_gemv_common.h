@@ -367,6 +367,89 @@ __device__ __forceinline__ void block_dot(const uint4 codes, float scale, const 
     }
 }
 
+// Two blocks against the same activation slices (gate and up of one row, or
+// two rows of one block column): the arithmetic of two block_dot calls, each
+// accumulation in the same order, with the two blocks' dot products
+// interleaved so that twice as many accumulation chains are in flight.
+template <int QT, int NTERM, int NT>
+__device__ __forceinline__ void block_dot_pair(const uint4 ca, float sa, const uint4 cb, float sb,
+                                               const XSlice<QT, NTERM> (&xs)[NT], int ntok, float (&oa)[NT],
+                                               float (&ob)[NT]) {
+    constexpr int NQ = QTraits<QT>::NQ;
+    float acc[2][NT][NQ];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) acc[0][t][q] = acc[1][t][q] = xs[t].neg_c[q];
+    const uint32_t dw[2][4] = {{ca.x, ca.y, ca.z, ca.w}, {cb.x, cb.y, cb.z, cb.w}};
+    const uint32_t mg = magic_vgpr();
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        if constexpr (QT == 1) {
+            uint32_t p[2][8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t D = dw[h][d], D6 = D >> 6, D12 = D >> 12;
+                p[h][0] = and_or(D, 0x00030003u, mg);
+                p[h][1] = and_or(D, 0x000C000Cu, mg);
+                p[h][2] = and_or(D, 0x00300030u, mg);
+                p[h][3] = and_or(D6, 0x00030003u, mg);
+                p[h][4] = and_or(D6, 0x000C000Cu, mg);
+                p[h][5] = and_or(D6, 0x00300030u, mg);
+                p[h][6] = and_or(D12, 0x00030003u, mg);
+                p[h][7] = and_or(D12, 0x000C000Cu, mg);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (NT == 1 || t < ntok) {
+#pragma unroll
+                    for (int tm = 0; tm < NTERM; ++tm)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+                                acc[h][t][q_of_pair(i)] = dot2(p[h][i], xs[t].pr[tm][8 * d + i], acc[h][t][q_of_pair(i)]);
+                }
+            }
+        } else {
+            uint32_t p[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t D = dw[h][d];
+                p[h][0] = and_or(D, 0x000F000Fu, mg);
+                p[h][1] = and_or(D >> 4, 0x000F000Fu, mg);
+                p[h][2] = and_or(D >> 8, 0x000F000Fu, mg);
+                p[h][3] = and_or(D >> 12, 0x000F000Fu, mg);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (NT == 1 || t < ntok) {
+#pragma unroll
+                    for (int tm = 0; tm < NTERM; ++tm)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+                                acc[h][t][0] = dot2(p[h][i], xs[t].pr[tm][4 * d + i], acc[h][t][0]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float cx[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if constexpr (QT == 1)
+                cx[h] = __builtin_fmaf(acc[h][t][2], 0.0625f, __builtin_fmaf(acc[h][t][1], 0.25f, acc[h][t][0]));
+            else
+                cx[h] = acc[h][t][0];
+        }
+        oa[t] = sa * (cx[0] - xs[t].zx);
+        ob[t] = sb * (cx[1] - xs[t].zx);
+    }
+}
+
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);   // exact, subnormals included
 }
