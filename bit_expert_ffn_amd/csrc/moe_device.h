@@ -208,9 +208,10 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // and every selected element is among those >= thr.  When at most 64 are, they
 // are gathered one per lane through `scratch` (128 keys of LDS owned by this
 // wave; slots 64.. take the writes of lanes with nothing to store), each counts
-// the larger keys among them, and the k of rank < k are written back at their
-// ranks.  Returns false (nothing selected) when more than 64 elements reach
-// thr; the outcome is uniform across the wave.
+// the larger keys among them (read from their lanes: lanes past the last
+// candidate hold 0, which is below every key), and the k of rank < k are
+// written back at their ranks.  Returns false (nothing selected) when more
+// than 64 elements reach thr; the outcome is uniform across the wave.
 template <int KPL>
 __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k, int lane, uint64_t* scratch,
                                                uint64_t* sel) {
@@ -243,20 +244,23 @@ __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k
     }
     if (n > 64) return false;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) scratch[hi[i] >= thr ? base[i] + lanes_below(mask[i]) : 64 + lane] = key[i];
+    for (int i = 0; i < KPL; ++i) {
+        // Position base[i] + (lanes below with a candidate in slot i), computed
+        // on every lane (no branch) and used where this lane has one.
+        const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask[i] >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask[i], (uint32_t)base[i]));
+        scratch[hi[i] >= thr ? pos : 64 + lane] = key[i];
+    }
     // LDS accesses of one wave complete in program order; the barrier keeps the
     // compiler from moving them across each other.
     __builtin_amdgcn_wave_barrier();
     const uint64_t mine = lane < n ? scratch[lane] : 0ull;
-    // Every lane reads the candidates from LDS, 8 at a time (the same address
-    // for all lanes: broadcast reads); positions n.. hold no candidate.
+    // Candidate u is read from lane u, four at a time: the reads past n (at
+    // most lane 63, as n <= 64) find 0 and count for nothing.
     int rank = 0;
-    for (int j = 0; j < n; j += 8) {
-        uint64_t c[8];
+    for (int u = 0; u < n; u += 4) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) c[u] = scratch[j + u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) rank += (j + u < n) && c[u] > mine;
+        for (int j = 0; j < 4; ++j) rank += readlane_u64(mine, u + j) > mine;
     }
     __builtin_amdgcn_wave_barrier();
     scratch[lane < n && rank < k ? rank : 64 + lane] = mine;
