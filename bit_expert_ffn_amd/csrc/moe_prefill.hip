@@ -414,6 +414,12 @@ __device__ __forceinline__ uint32_t ldg_u16(const uint8_t* base, uint32_t off) {
     return *(const __attribute__((address_space(1))) uint16_t*)(base + off);
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg_u128(const uint8_t* base, uint32_t off) {
+    const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)(base + off);
+    return uint4{v[0], v[1], v[2], v[3]};
+}
+
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // XCD-contiguous mapping of the 1-D grid onto n logical work items; -1 = no work.
@@ -567,26 +573,43 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
         boff[j] = (uint32_t)(m * plane * 18 + ((size_t)fr * nblk + (pc < BPC ? pc : 0)) * 16);
     }
     const uint8_t* xq = (const uint8_t*)p.xq;
-    auto issue = [&](int c, uint8_t* buf) {
-        const uint32_t k0 = (uint32_t)(c * KC);
-#pragma unroll
-        for (int j = 0; j < AJ; ++j)
-            if (wv + 8 * j < kAcopies) load_lds16(xq + 2 * (xoff[j] + k0), buf + 1024 * (wv + 8 * j));
+    // The copies of chunk c: weight codes (B) and activations (A), issued
+    // separately so that they spread over the previous chunk's blocks.
+    auto issue_b = [&](int c, uint8_t* buf) {
         const uint32_t kb = (uint32_t)(c * BPC * 16);
 #pragma unroll
         for (int j = 0; j < BP; ++j) load_lds16(blob + (boff[j] + kb), buf + kAbytes + (64 * wv * BP + 64 * j) * 16);
     };
-    // Scales of this lane's gate and up rows, one chunk ahead in registers.
+    auto issue_a = [&](int c, uint8_t* buf) {
+        const uint32_t k0 = (uint32_t)(c * KC);
+#pragma unroll
+        for (int j = 0; j < AJ; ++j)
+            if (wv + 8 * j < kAcopies) load_lds16(xq + 2 * (xoff[j] + k0), buf + 1024 * (wv + 8 * j));
+    };
+    // Scales of this lane's gate and up rows in registers, 8 blocks (16 bytes,
+    // CPL chunks) at a time: one 16-byte load per row when a row's scales are
+    // 16-byte aligned (nblk a multiple of 8; the chunk count is then a multiple
+    // of CPL), else 2-byte loads clamped to the row.
+    constexpr int CPL = 8 / BPC;
     const int fl = min(f0 + 32 * wv + col, FFe - 1);
     const uint32_t gsoff = (uint32_t)(plane * 16 + (size_t)fl * nblk * 2);
     const uint32_t usoff = gsoff + (uint32_t)(plane * 18);
-    uint32_t nsg[BPC], nsu[BPC];
-    auto load_s = [&](int c) {
+    const bool s16 = (nblk & 7) == 0;
+    uint4 svg, svu;
+    auto load_s8 = [&](int q) {
+        if (s16) {
+            svg = ldg_u128(blob, gsoff + 16u * (uint32_t)q);
+            svu = ldg_u128(blob, usoff + 16u * (uint32_t)q);
+        } else {
+            uint32_t hg[8], hu[8];
 #pragma unroll
-        for (int i = 0; i < BPC; ++i) {
-            const uint32_t blk = (uint32_t)min(c * BPC + i, nblk - 1);
-            nsg[i] = ldg_u16(blob, gsoff + 2 * blk);
-            nsu[i] = ldg_u16(blob, usoff + 2 * blk);
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t blk = (uint32_t)min(8 * q + j, nblk - 1);
+                hg[j] = ldg_u16(blob, gsoff + 2 * blk);
+                hu[j] = ldg_u16(blob, usoff + 2 * blk);
+            }
+            svg = uint4{hg[0] | hg[1] << 16, hg[2] | hg[3] << 16, hg[4] | hg[5] << 16, hg[6] | hg[7] << 16};
+            svu = uint4{hu[0] | hu[1] << 16, hu[2] | hu[3] << 16, hu[4] | hu[5] << 16, hu[6] | hu[7] << 16};
         }
     };
     // This lane's LDS read bases: A row col (+ 32 r rows), B rows of its features.
@@ -617,19 +640,31 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
         auto chunk = [&](int c, const uint8_t* buf, uint8_t* next) {
             wait_loads();
             __syncthreads();
+            // This chunk's block scales s / 2 (the weight operands are 2(c - z)),
+            // taken from the 8-block registers before the group's last chunk
+            // refills them.
+            const int cq = c % CPL;
             float fg[BPC], fu[BPC];
 #pragma unroll
             for (int i = 0; i < BPC; ++i) {
-                fg[i] = 0.5f * half_to_f32((uint16_t)nsg[i]);
-                fu[i] = 0.5f * half_to_f32((uint16_t)nsu[i]);
+                const int bi = cq * BPC + i, wsel = bi >> 1, sh = 16 * (bi & 1);
+                const uint32_t wg = wsel == 0 ? svg.x : wsel == 1 ? svg.y : wsel == 2 ? svg.z : svg.w;
+                const uint32_t wu = wsel == 0 ? svu.x : wsel == 1 ? svu.y : wsel == 2 ? svu.z : svu.w;
+                fg[i] = 0.5f * half_to_f32((uint16_t)(wg >> sh));
+                fu[i] = 0.5f * half_to_f32((uint16_t)(wu >> sh));
             }
-            if (c + 1 < nchunks) {
-                issue(c + 1, next);
-                load_s(c + 1);
-            }
+            if (cq == CPL - 1 && c + 1 < nchunks) load_s8((c + 1) / CPL);
+            // chunk c + 1's copies go out at the start of blocks 0 (codes) and 1
+            // (activations; block 0 too when a chunk holds one block); every chunk
+            // but a row's last has all its blocks
+            const bool more = c + 1 < nchunks;
+            // Each block's products summed from zero, then scaled by s / 2 once per
+            // output element, in fp32.
 #pragma unroll
             for (int i = 0; i < BPC; ++i) {
                 if (c * BPC + i >= nblk) break;
+                if (more && i == 0) issue_b(c + 1, next);
+                if (more && i == (BPC > 1 ? 1 : 0)) issue_a(c + 1, next);
                 const uint4 g4 = *reinterpret_cast<const uint4*>(buf + g_base + i * 16);
                 const uint4 u4 = *reinterpret_cast<const uint4*>(buf + u_base + i * 16);
                 const uint32_t gw[2] = {hh ? g4.z : g4.x, hh ? g4.w : g4.y};   // bytes 8 hh .. 8 hh + 7
@@ -663,8 +698,9 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
                 }
             }
         };
-        issue(0, buf0);
-        load_s(0);
+        issue_b(0, buf0);
+        issue_a(0, buf0);
+        load_s8(0);
         for (int c = 0; c < nchunks; c += 2) {
             chunk(c, buf0, buf1);
             if (c + 1 < nchunks) chunk(c + 1, buf1, buf0);
@@ -768,26 +804,40 @@ __global__ void __launch_bounds__(kDnThreads, 1) prefill_down_kernel(PrefillPara
         const int hr = min(hbase + 64 * wv + L / BP, H - 1), pc = L % BP;
         boff[j] = dco + (uint32_t)(((size_t)hr * nblk + (pc < BPC ? pc : 0)) * 16);
     }
-    auto issue = [&](int c, uint8_t* buf) {
-        const uint32_t k0 = (uint32_t)(c * KC * 2);
-#pragma unroll
-        for (int j = 0; j < AJ; ++j)
-            if (wv + 8 * j < kAcopies) load_lds16(abase + (aoff[j] + k0), buf + 1024 * (wv + 8 * j));
+    // The copies of chunk c, weight codes (B) and `a` (A), issued separately so
+    // that they spread over the previous chunk's blocks.
+    auto issue_b = [&](int c, uint8_t* buf) {
         const uint32_t kb = (uint32_t)(c * BPC * 16);
 #pragma unroll
         for (int j = 0; j < BP; ++j) load_lds16(blob + (boff[j] + kb), buf + kAbytes + (64 * wv * BP + 64 * j) * 16);
     };
+    auto issue_a = [&](int c, uint8_t* buf) {
+        const uint32_t k0 = (uint32_t)(c * KC * 2);
+#pragma unroll
+        for (int j = 0; j < AJ; ++j)
+            if (wv + 8 * j < kAcopies) load_lds16(abase + (aoff[j] + k0), buf + 1024 * (wv + 8 * j));
+    };
+    // Scales of this lane's two output rows in registers, 8 blocks (CPL chunks)
+    // at a time, as in the gate/up kernel.
+    constexpr int CPL = 8 / BPC;
     uint32_t soff[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n)
         soff[n] = dso + (uint32_t)((size_t)min(hbase + 64 * wv + 32 * n + col, H - 1) * nblk * 2);
-    uint32_t nsd[2][BPC];
-    auto load_s = [&](int c) {
+    const bool s16 = (nblk & 7) == 0;
+    uint4 sv[2];
+    auto load_s8 = [&](int q) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < 2; ++n) {
+            if (s16) {
+                sv[n] = ldg_u128(blob, soff[n] + 16u * (uint32_t)q);
+            } else {
+                uint32_t h[8];
 #pragma unroll
-            for (int i = 0; i < BPC; ++i)
-                nsd[n][i] = ldg_u16(blob, soff[n] + 2u * (uint32_t)min(c * BPC + i, nblk - 1));
+                for (int j = 0; j < 8; ++j) h[j] = ldg_u16(blob, soff[n] + 2u * (uint32_t)min(8 * q + j, nblk - 1));
+                sv[n] = uint4{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+            }
+        }
     };
     const uint32_t a_base = (uint32_t)(col * kApitch * 16 + (QK / 2) * hh * 2);
     const uint32_t b_base = (uint32_t)(kAbytes + (64 * wv + col) * BP * 16);
@@ -807,18 +857,23 @@ __global__ void __launch_bounds__(kDnThreads, 1) prefill_down_kernel(PrefillPara
         auto chunk = [&](int c, const uint8_t* buf, uint8_t* next) {
             wait_loads();
             __syncthreads();
+            const int cq = c % CPL;
             float fs[2][BPC];
 #pragma unroll
             for (int n = 0; n < 2; ++n)
 #pragma unroll
-                for (int i = 0; i < BPC; ++i) fs[n][i] = half_to_f32((uint16_t)nsd[n][i]);
-            if (c + 1 < nchunks) {
-                issue(c + 1, next);
-                load_s(c + 1);
-            }
+                for (int i = 0; i < BPC; ++i) {
+                    const int bi = cq * BPC + i, wsel = bi >> 1, sh = 16 * (bi & 1);
+                    const uint32_t w = wsel == 0 ? sv[n].x : wsel == 1 ? sv[n].y : wsel == 2 ? sv[n].z : sv[n].w;
+                    fs[n][i] = half_to_f32((uint16_t)(w >> sh));
+                }
+            if (cq == CPL - 1 && c + 1 < nchunks) load_s8((c + 1) / CPL);
+            const bool more = c + 1 < nchunks;
 #pragma unroll
             for (int i = 0; i < BPC; ++i) {
                 if (c * BPC + i >= nblk) break;
+                if (more && i == 0) issue_b(c + 1, next);
+                if (more && i == (BPC > 1 ? 1 : 0)) issue_a(c + 1, next);
                 bf16x8_t wb[2][SPB];
 #pragma unroll
                 for (int n = 0; n < 2; ++n) {
@@ -850,8 +905,9 @@ __global__ void __launch_bounds__(kDnThreads, 1) prefill_down_kernel(PrefillPara
                 }
             }
         };
-        issue(0, buf0);
-        load_s(0);
+        issue_b(0, buf0);
+        issue_a(0, buf0);
+        load_s8(0);
         for (int c = 0; c < nchunks; c += 2) {
             chunk(c, buf0, buf1);
             if (c + 1 < nchunks) chunk(c + 1, buf1, buf0);

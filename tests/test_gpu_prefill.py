@@ -37,6 +37,56 @@ def test_expert_ffn_prefill_matches_oracle(qtype, H, FF, T, xd):
     assert max_err_over_rms(y, ref) <= TOL
 
 
+def _scales(blob, qk, H, FF, m):
+    """Writable fp16 view [rows][nblk] of the scales plane of matrix m (0 gate,
+    1 up, 2 down) of an expert blob: each matrix is a codes plane [rows][nblk]
+    of 16 bytes followed by its scales."""
+    rows, cols = (FF, FF, H), (H, H, FF)
+    off = sum(rows[i] * (cols[i] // qk) * 18 for i in range(m))
+    nblk = cols[m] // qk
+    start = off + rows[m] * nblk * 16
+    return blob[start:start + rows[m] * nblk * 2].view(np.float16).reshape(rows[m], nblk)
+
+
+@pytest.mark.parametrize("qtype,z", [(2, 15.5), (2, 16.0), (2, -0.5), (2, -1.0), (1, 14.0), (1, -14.0)])
+def test_prefill_zero_point_range(qtype, z):
+    """bf16 activations with zero points away from the formats' centres (z a
+    multiple of 0.5 in [-64, 64]): the matrix-core weight operands 2(c - z) stay
+    exact fp16 integers at either end of the code range."""
+    qk = 64 if qtype == 1 else 32
+    H, FF, T = 512, 192, 70
+    blob = synth.expert_blob(11, 0, 1, qk, H, FF, 0.05 if qtype == 1 else 0.02)
+    x = synth.activations(11, 0, 1, T, H, "bf16")
+    d = moe.expert_desc(H, FF, qtype, z)
+    y = moe.expert_ffn(d, torch.from_numpy(blob).to(DEV), _x_tensor(x)).cpu().numpy()
+    ref = oracle.expert_ffn(blob, qtype, z, H, FF, x)
+    assert max_err_over_rms(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("qtype", [2, 1])
+def test_prefill_large_block_scales(qtype):
+    """Gate and up block scales times 2^17 (exact in fp16, up to 26,432): large
+    and small scales mixed along each row, with outputs far from unit size, keep
+    the oracle's relative accuracy through the per-block fp32 scaling."""
+    qk = 64 if qtype == 1 else 32
+    z = 1.5 if qtype == 1 else 7.5
+    H, FF, T = 512, 192, 40
+    blob = synth.expert_blob(12, 0, 2, qk, H, FF, 0.05 if qtype == 1 else 0.02)
+    for m in (0, 1):
+        sc = _scales(blob, qk, H, FF, m)
+        big = sc.astype(np.float64) * 2.0 ** 17
+        assert np.all(np.abs(big) <= 65504.0)
+        sc[...] = big.astype(np.float16)
+        frac = np.mean(np.abs(sc.astype(np.float64)) >= 1024.0)
+        assert 0.3 < frac < 1.0, frac   # large and small scales mixed
+    x = synth.activations(12, 0, 2, T, H, "bf16")
+    d = moe.expert_desc(H, FF, qtype, z)
+    y = moe.expert_ffn(d, torch.from_numpy(blob).to(DEV), _x_tensor(x)).cpu().numpy()
+    ref = oracle.expert_ffn(blob, qtype, z, H, FF, x)
+    assert np.all(np.isfinite(y))
+    assert max_err_over_rms(y, ref) <= TOL
+
+
 def _small_layer(qtype, E, k, H, FF, T, xd, shared_ff, zipf, seed):
     qk = 64 if qtype == 1 else 32
     z = 1.5 if qtype == 1 else 7.5
