@@ -573,18 +573,19 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
         boff[j] = (uint32_t)(m * plane * 18 + ((size_t)fr * nblk + (pc < BPC ? pc : 0)) * 16);
     }
     const uint8_t* xq = (const uint8_t*)p.xq;
-    // The copies of chunk c: weight codes (B) and activations (A), issued
-    // separately so that they spread over the previous chunk's blocks.
-    auto issue_b = [&](int c, uint8_t* buf) {
+    // Copies j0 .. j1 - 1 of chunk c's weight codes (B) and activations (A), so
+    // that they can spread over the previous chunk's blocks.
+    auto issue_b = [&](int c, uint8_t* buf, int j0, int j1) {
         const uint32_t kb = (uint32_t)(c * BPC * 16);
 #pragma unroll
-        for (int j = 0; j < BP; ++j) load_lds16(blob + (boff[j] + kb), buf + kAbytes + (64 * wv * BP + 64 * j) * 16);
+        for (int j = 0; j < BP; ++j)
+            if (j >= j0 && j < j1) load_lds16(blob + (boff[j] + kb), buf + kAbytes + (64 * wv * BP + 64 * j) * 16);
     };
-    auto issue_a = [&](int c, uint8_t* buf) {
+    auto issue_a = [&](int c, uint8_t* buf, int j0, int j1) {
         const uint32_t k0 = (uint32_t)(c * KC);
 #pragma unroll
         for (int j = 0; j < AJ; ++j)
-            if (wv + 8 * j < kAcopies) load_lds16(xq + 2 * (xoff[j] + k0), buf + 1024 * (wv + 8 * j));
+            if (j >= j0 && j < j1 && wv + 8 * j < kAcopies) load_lds16(xq + 2 * (xoff[j] + k0), buf + 1024 * (wv + 8 * j));
     };
     // Scales of this lane's gate and up rows in registers, 8 blocks (16 bytes,
     // CPL chunks) at a time: one 16-byte load per row when a row's scales are
@@ -654,17 +655,26 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
                 fu[i] = 0.5f * half_to_f32((uint16_t)(wu >> sh));
             }
             if (cq == CPL - 1 && c + 1 < nchunks) load_s8((c + 1) / CPL);
-            // chunk c + 1's copies go out at the start of blocks 0 (codes) and 1
-            // (activations; block 0 too when a chunk holds one block); every chunk
-            // but a row's last has all its blocks
+            // Chunk c + 1's copies go out two or three at a time at the starts of
+            // this chunk's blocks (codes first: they come from HBM), so that no
+            // wave stalls behind a burst of them; every chunk but a row's last
+            // has all its blocks.  (Copies issued between a block's LDS reads
+            // would make the compiler wait for them before those reads.)
             const bool more = c + 1 < nchunks;
             // Each block's products summed from zero, then scaled by s / 2 once per
             // output element, in fp32.
 #pragma unroll
             for (int i = 0; i < BPC; ++i) {
                 if (c * BPC + i >= nblk) break;
-                if (more && i == 0) issue_b(c + 1, next);
-                if (more && i == (BPC > 1 ? 1 : 0)) issue_a(c + 1, next);
+                if constexpr (BPC == 4) {
+                    if (more && i == 0) issue_b(c + 1, next, 0, 3);
+                    if (more && i == 1) issue_b(c + 1, next, 3, BP);
+                    if (more && i == 2) issue_a(c + 1, next, 0, 3);
+                    if (more && i == 3) issue_a(c + 1, next, 3, AJ);
+                } else {
+                    if (more && i == 0) issue_b(c + 1, next, 0, BP);
+                    if (more && i == (BPC > 1 ? 1 : 0)) issue_a(c + 1, next, 0, AJ);
+                }
                 const uint4 g4 = *reinterpret_cast<const uint4*>(buf + g_base + i * 16);
                 const uint4 u4 = *reinterpret_cast<const uint4*>(buf + u_base + i * 16);
                 const uint32_t gw[2] = {hh ? g4.z : g4.x, hh ? g4.w : g4.y};   // bytes 8 hh .. 8 hh + 7
@@ -698,8 +708,8 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
                 }
             }
         };
-        issue_b(0, buf0);
-        issue_a(0, buf0);
+        issue_b(0, buf0, 0, BP);
+        issue_a(0, buf0, 0, AJ);
         load_s8(0);
         for (int c = 0; c < nchunks; c += 2) {
             chunk(c, buf0, buf1);
