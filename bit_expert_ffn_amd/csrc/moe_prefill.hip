@@ -958,14 +958,33 @@ __global__ void __launch_bounds__(256) prefill_combine_kernel(PrefillParams p) {
     const int t = (int)(i * 4 / p.H), h = (int)(i * 4 - (size_t)t * p.H);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.shared) acc = *reinterpret_cast<const float4*>(p.ypair + (size_t)(p.T * p.k + t) * p.H + h);
-    for (int j = 0; j < p.k; ++j) {
-        if (!pair_on(p, t * p.k + j)) continue;
-        const float wt = p.w[t * p.k + j] * (p.down_scale ? p.down_scale[p.ids[t * p.k + j]] : 1.f);
-        const float4 v = *reinterpret_cast<const float4*>(p.ypair + (size_t)p.inv[t * p.k + j] * p.H + h);
-        acc.x = __builtin_fmaf(wt, v.x, acc.x);
-        acc.y = __builtin_fmaf(wt, v.y, acc.y);
-        acc.z = __builtin_fmaf(wt, v.z, acc.z);
-        acc.w = __builtin_fmaf(wt, v.w, acc.w);
+    // Eight slots at a time: their rows and weights, then all eight row loads,
+    // then the sums in slot order (a skipped slot loads nothing and adds
+    // nothing).
+    constexpr int G = 8;
+    for (int j0 = 0; j0 < p.k; j0 += G) {
+        bool on[G];
+        float wt[G];
+        int row[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const int q = t * p.k + j0 + u;
+            on[u] = j0 + u < p.k && pair_on(p, q);
+            wt[u] = on[u] ? p.w[q] * (p.down_scale ? p.down_scale[p.ids[q]] : 1.f) : 0.f;
+            row[u] = on[u] ? p.inv[q] : 0;
+        }
+        float4 v[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+            v[u] = on[u] ? *reinterpret_cast<const float4*>(p.ypair + (size_t)row[u] * p.H + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            if (!on[u]) continue;
+            acc.x = __builtin_fmaf(wt[u], v[u].x, acc.x);
+            acc.y = __builtin_fmaf(wt[u], v[u].y, acc.y);
+            acc.z = __builtin_fmaf(wt[u], v[u].z, acc.z);
+            acc.w = __builtin_fmaf(wt[u], v[u].w, acc.w);
+        }
     }
     *reinterpret_cast<float4*>(p.y + (size_t)t * p.H + h) = acc;
 }
