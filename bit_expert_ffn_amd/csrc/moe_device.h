@@ -346,9 +346,10 @@ __device__ __forceinline__ void topk_load(const float* __restrict__ row, int E, 
     }
 }
 
+// want_w false: only the ids (rank order); *out_w is left unset.
 template <int KPL>
 __device__ __forceinline__ void topk_of_values(const float (&lv)[KPL], int E, int k, int renorm, int lane,
-                                               uint64_t* scratch, int* out_id, float* out_w) {
+                                               uint64_t* scratch, int* out_id, float* out_w, bool want_w = true) {
     uint64_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
@@ -359,8 +360,12 @@ __device__ __forceinline__ void topk_of_values(const float (&lv)[KPL], int E, in
     uint64_t sel;
     if (!topk_threshold<KPL>(key, k, lane, scratch, &sel)) sel = topk_rounds<KPL>(key, k, lane);
     const uint32_t my_key = (uint32_t)(sel >> 32);
-    const uint32_t top_key = readlane_u32(my_key, 0);
     const int my_id = lane < k ? (int)(0xFFFFFFFFu - (uint32_t)sel) : -1;
+    if (!want_w) {
+        *out_id = my_id;
+        return;
+    }
+    const uint32_t top_key = readlane_u32(my_key, 0);
     const float top = from_order_bits(top_key);
     const float my_logit = from_order_bits(my_key);
     const bool all_neg_inf = (top == -INFINITY);
@@ -384,10 +389,10 @@ __device__ __forceinline__ void topk_of_values(const float (&lv)[KPL], int E, in
 
 template <int KPL>
 __device__ __forceinline__ void wave_topk_kpl(const float* __restrict__ row, int E, int k, int renorm, int lane,
-                                              uint64_t* scratch, int* out_id, float* out_w) {
+                                              uint64_t* scratch, int* out_id, float* out_w, bool want_w) {
     float lv[KPL];
     topk_load<KPL>(row, E, lane, lv);
-    topk_of_values<KPL>(lv, E, k, renorm, lane, scratch, out_id, out_w);
+    topk_of_values<KPL>(lv, E, k, renorm, lane, scratch, out_id, out_w, want_w);
 }
 
 // Two rows by one wave, one after the other, with both rows' loads issued
@@ -404,13 +409,14 @@ __device__ __forceinline__ void wave_topk2_kpl(const float* __restrict__ row0, c
     if (two) topk_of_values<KPL>(l1, E, k, renorm, lane, scratch, &out_id[1], &out_w[1]);
 }
 
-// `scratch`: 128 keys of LDS owned by the calling wave.
+// `scratch`: 128 keys of LDS owned by the calling wave.  want_w false: the ids
+// only (no softmax), for callers that never read the weights.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm, int lane,
-                                          uint64_t* scratch, int* out_id, float* out_w) {
-    if (E <= 128) wave_topk_kpl<2>(row, E, k, renorm, lane, scratch, out_id, out_w);
-    else if (E <= 256) wave_topk_kpl<4>(row, E, k, renorm, lane, scratch, out_id, out_w);
-    else if (E <= 512) wave_topk_kpl<8>(row, E, k, renorm, lane, scratch, out_id, out_w);
-    else wave_topk_kpl<16>(row, E, k, renorm, lane, scratch, out_id, out_w);
+                                          uint64_t* scratch, int* out_id, float* out_w, bool want_w = true) {
+    if (E <= 128) wave_topk_kpl<2>(row, E, k, renorm, lane, scratch, out_id, out_w, want_w);
+    else if (E <= 256) wave_topk_kpl<4>(row, E, k, renorm, lane, scratch, out_id, out_w, want_w);
+    else if (E <= 512) wave_topk_kpl<8>(row, E, k, renorm, lane, scratch, out_id, out_w, want_w);
+    else wave_topk_kpl<16>(row, E, k, renorm, lane, scratch, out_id, out_w, want_w);
 }
 
 __device__ __forceinline__ void wave_topk2(const float* __restrict__ row0, const float* __restrict__ row1, bool two,

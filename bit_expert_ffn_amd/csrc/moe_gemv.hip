@@ -100,7 +100,9 @@ struct RouteLDS {
 // a zero-weight slot), the slots of nonzero weight become the groups, in slot
 // order; a zero-weight slot has no group and its expert is never read.  A
 // nonzero weight on an id outside [0, E) flags kErrBadId and fails the call.
-__device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
+// want_w false: the slot weights are not computed (R.w is left unset), for a
+// workgroup that never reads them.
+__device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R, bool want_w) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int k = p.k;
     if (tid == 0) R.fail = 0;
@@ -133,7 +135,7 @@ __device__ void route_and_bucket(const DecodeParams& p, RouteLDS& R) {
     } else if (wv == 0) {
         int id = 0;
         float wt = 1.f;
-        if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, R.topk[0], &id, &wt);
+        if (!p.identity) wave_topk(p.logits, p.E, k, p.renorm, lane, R.topk[0], &id, &wt, want_w);
         if (lane < k) {
             R.id[lane] = id;
             R.w[lane] = wt;
@@ -701,7 +703,10 @@ __global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodePar
             slice_to_lds<QT, NTERM>(xsl, reinterpret_cast<uint32_t*>(lds) + p.x_off + b * SliceWords<QT, NTERM>::N);
         }
     }
-    route_and_bucket(p, R);
+    // Only the down workgroups (the combine) and workgroup 0 (w_out) read the
+    // weights: the gate/up workgroups skip the softmax, which is on the path to
+    // their weight loads.
+    route_and_bucket(p, R, wg >= p.n_gu || (wg == 0 && p.w_out));
     if (wg == 0) {
         for (int q = tid; q < p.T * p.k; q += kGemvThreads) {
             if (p.ids_out) p.ids_out[q] = R.id[q];
