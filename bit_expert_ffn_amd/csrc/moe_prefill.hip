@@ -615,7 +615,8 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
     };
     // This lane's LDS read bases: A row col (+ 32 r rows), B rows of its features.
     const uint32_t a_base = (uint32_t)(col * kApitch * 16 + (QK / 2) * hh * 2);
-    const uint32_t g_base = (uint32_t)(kAbytes + (32 * wv + col) * BP * 16);
+    // (B: this lane's half of each 16-byte block, bytes 8 hh .. 8 hh + 7)
+    const uint32_t g_base = (uint32_t)(kAbytes + (32 * wv + col) * BP * 16 + 8 * hh);
     const uint32_t u_base = g_base + (uint32_t)(kGuFeatures * BP * 16);
 
     // The chunk loop and epilogue, specialised on the number NR of 32-row MFMA
@@ -675,10 +676,10 @@ __global__ void __launch_bounds__(kGuThreads, 1) prefill_gateup_kernel(PrefillPa
                     if (more && i == 0) issue_b(c + 1, next, 0, BP);
                     if (more && i == (BPC > 1 ? 1 : 0)) issue_a(c + 1, next, 0, AJ);
                 }
-                const uint4 g4 = *reinterpret_cast<const uint4*>(buf + g_base + i * 16);
-                const uint4 u4 = *reinterpret_cast<const uint4*>(buf + u_base + i * 16);
-                const uint32_t gw[2] = {hh ? g4.z : g4.x, hh ? g4.w : g4.y};   // bytes 8 hh .. 8 hh + 7
-                const uint32_t uw[2] = {hh ? u4.z : u4.x, hh ? u4.w : u4.y};
+                const uint2 g2 = *reinterpret_cast<const uint2*>(buf + g_base + i * 16);
+                const uint2 u2 = *reinterpret_cast<const uint2*>(buf + u_base + i * 16);
+                const uint32_t gw[2] = {g2.x, g2.y};
+                const uint32_t uw[2] = {u2.x, u2.y};
                 f16x8_t wg[SPB], wu[SPB];
 #pragma unroll
                 for (int s = 0; s < SPB; ++s) {
@@ -850,7 +851,7 @@ __global__ void __launch_bounds__(kDnThreads, 1) prefill_down_kernel(PrefillPara
         }
     };
     const uint32_t a_base = (uint32_t)(col * kApitch * 16 + (QK / 2) * hh * 2);
-    const uint32_t b_base = (uint32_t)(kAbytes + (64 * wv + col) * BP * 16);
+    const uint32_t b_base = (uint32_t)(kAbytes + (64 * wv + col) * BP * 16 + 8 * hh);   // this lane's half-blocks
 
     auto run = [&](auto nr_c) {
         constexpr int NR = decltype(nr_c)::value;
@@ -887,8 +888,8 @@ __global__ void __launch_bounds__(kDnThreads, 1) prefill_down_kernel(PrefillPara
                 bf16x8_t wb[2][SPB];
 #pragma unroll
                 for (int n = 0; n < 2; ++n) {
-                    const uint4 d4 = *reinterpret_cast<const uint4*>(buf + b_base + (32 * n * BP + i) * 16);
-                    const uint32_t dw[2] = {hh ? d4.z : d4.x, hh ? d4.w : d4.y};
+                    const uint2 d2 = *reinterpret_cast<const uint2*>(buf + b_base + (32 * n * BP + i) * 16);
+                    const uint32_t dw[2] = {d2.x, d2.y};
 #pragma unroll
                     for (int s = 0; s < SPB; ++s) wb[n][s] = weights_bf16<QT>(dw[(QT == 2) ? s : (s >> 1)], s & 1, z);
                 }
