@@ -25,7 +25,11 @@ def _x_tensor(x):
 
 @pytest.mark.parametrize("qtype,H,FF,T,xd", [(2, 256, 128, 9, "bf16"), (2, 256, 192, 130, "bf16"), (1, 256, 128, 40, "bf16"),
                                              (2, 160, 96, 77, "f32"), (1, 192, 320, 300, "f32"),
-                                             (2, 2816, 704, 64, "bf16")])
+                                             (2, 2816, 704, 64, "bf16"),
+                                             # rows of a multiple of 8 blocks (scales in 16-byte loads), every
+                                             # format and activation plane count, gate/up and down
+                                             (1, 1024, 512, 70, "bf16"), (1, 512, 512, 33, "f32"),
+                                             (2, 512, 256, 50, "f32")])
 def test_expert_ffn_prefill_matches_oracle(qtype, H, FF, T, xd):
     qk = 64 if qtype == 1 else 32
     z = 1.5 if qtype == 1 else 7.5
