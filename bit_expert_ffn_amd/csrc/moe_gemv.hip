@@ -82,6 +82,16 @@ __device__ __forceinline__ int* sync_ready(int* s, int r, int g, int n_ctr) {
     return s + (lines + (size_t)r * kReadyStride) / 4 + g;
 }
 
+// floor(x / d) for 0 <= x < 2^20 and 1 <= d < 2^24, in single precision (the
+// decode shapes stay below both: at most 33 groups of 2^14 tiles).
+// (x + 0.5) / d lies at least 0.5 / d from every integer; the reciprocal (1 ulp)
+// and the rounded product leave a relative error below 2^-22, so the error
+// stays below (x + 0.5) / d * 2^-22 < 0.5 / d and the truncation is exact.
+// A few instructions where an integer division takes about twenty.
+__device__ __forceinline__ int small_div(int x, int d) {
+    return (int)(((float)x + 0.5f) * __builtin_amdgcn_rcpf((float)d));
+}
+
 struct RouteLDS {
     int id[kMaxK];
     float w[kMaxK];
@@ -167,7 +177,7 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
     int rows, tile, ntok, grp, toks[NT], outrow[NT];
     uint32_t* out;
     if (item < p.max_groups * p.tiles_gu) {
-        const int g = item / p.tiles_gu;
+        const int g = small_div(item, p.tiles_gu);
         tile = item - g * p.tiles_gu;
         if (g >= R.n_groups) return;
         grp = g;
@@ -183,7 +193,7 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
         out = p.a;
     } else {
         const int i2 = item - p.max_groups * p.tiles_gu;
-        const int sg = i2 / p.tiles_gu_s;
+        const int sg = small_div(i2, p.tiles_gu_s);
         tile = i2 - sg * p.tiles_gu_s;
         grp = p.max_groups + sg;
         blob = p.shared;
@@ -200,9 +210,10 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
     const int nblk = p.H / QK;
     constexpr int BPL = PAIR ? 2 : 1;   // block columns per lane
     const int cols = nblk / BPL;
-    const int P = kGemvThreads / cols;
+    const int P = small_div(kGemvThreads, cols);
     const bool active = tid < P * cols;
-    const int rp = active ? tid / cols : 0, lc = active ? tid - (tid / cols) * cols : 0;
+    const int rq = small_div(tid, cols);
+    const int rp = active ? rq : 0, lc = active ? tid - rq * cols : 0;
     const int b = lc * BPL;             // the lane's (first) block column
     const int Rr = P * p.gu_passes;
     const int f0 = tile * Rr;
