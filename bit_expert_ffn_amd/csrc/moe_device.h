@@ -11,18 +11,20 @@ namespace moe {
 
 // Routing order (Krasis white paper 5.3: the k highest-scoring experts; ties
 // toward the lower index).  A 32-bit key orders floats like `>` with
-// -0 == +0; NaN maps to 1, below every number (-inf maps to 0x007FFFFF), and 0
-// marks an empty or already-selected slot.
+// -0 == +0: a non-negative value sets its sign bit, a negative one takes its
+// two's complement (-0 and +0 both give 0x80000000, with no compare).  NaN
+// maps to 1, below every number (-inf maps to 0x00800000), and 0 marks an
+// empty or already-selected slot.
 __device__ __forceinline__ uint32_t order_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (f != f) return 1u;
-    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t neg = (uint32_t)((int32_t)u >> 31);
+    const uint32_t key = (u ^ (neg | 0x80000000u)) + (u >> 31);
+    return f != f ? 1u : key;
 }
 
 __device__ __forceinline__ float from_order_bits(uint32_t k) {
     if (k <= 1u) return __uint_as_float(0x7FC00000u);
-    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : 0u - k;
     return __uint_as_float(u);
 }
 
@@ -202,16 +204,18 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 }
 
 // Threshold selection.  P = the largest 16-bit value that at least k of the
-// 64 lane maxima reach in their top 16 bits (a search two bits at a time, with
-// three ballot counts per step); thr = P << 16.  The k lanes whose maxima reach
+// 64 lane maxima reach in their top 16 bits (a search one bit at a time: one
+// ballot count per step, the fewest instructions for a lone wave, which issues
+// about one every six cycles); thr = P << 16.  The k lanes whose maxima reach
 // thr hold k distinct elements >= thr, so the k-th largest element is >= thr
 // and every selected element is among those >= thr.  When at most 64 are, they
 // are gathered one per lane through `scratch` (128 keys of LDS owned by this
-// wave; slots 64.. take the writes of lanes with nothing to store), each counts
-// the larger keys among them (read from their lanes: lanes past the last
-// candidate hold 0, which is below every key), and the k of rank < k are
-// written back at their ranks.  Returns false (nothing selected) when more
-// than 64 elements reach thr; the outcome is uniform across the wave.
+// wave, 16-byte aligned; slots 64.. take the writes of lanes with nothing to
+// store, and slots past the last candidate are cleared first), each counts the
+// larger keys among them (16 at a time from broadcast LDS reads: the cleared
+// slots hold 0, below every key), and the k of rank < k are written back at
+// their ranks.  Returns false (nothing selected) when more than 64 elements
+// reach thr; the outcome is uniform across the wave.
 template <int KPL>
 __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k, int lane, uint64_t* scratch,
                                                uint64_t* sel) {
@@ -225,12 +229,9 @@ __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k
     const uint32_t l16 = lmax >> 16;
     uint32_t p = 0;
 #pragma unroll
-    for (int sh = 14; sh >= 0; sh -= 2) {
-        const uint32_t c1 = p | (1u << sh), c2 = p | (2u << sh), c3 = p | (3u << sh);
-        const int n1 = __popcll(__ballot(l16 >= c1));
-        const int n2 = __popcll(__ballot(l16 >= c2));
-        const int n3 = __popcll(__ballot(l16 >= c3));
-        p = n3 >= k ? c3 : (n2 >= k ? c2 : (n1 >= k ? c1 : p));
+    for (int sh = 15; sh >= 0; --sh) {
+        const uint32_t c = p | (1u << sh);
+        p = __popcll(__ballot(l16 >= c)) >= k ? c : p;
     }
     const uint32_t thr = p << 16;
     uint64_t mask[KPL];
@@ -243,6 +244,7 @@ __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k
         n += __popcll(mask[i]);
     }
     if (n > 64) return false;
+    scratch[lane] = 0ull;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         // Position base[i] + (lanes below with a candidate in slot i), computed
@@ -254,13 +256,16 @@ __device__ __forceinline__ bool topk_threshold(const uint64_t (&key)[KPL], int k
     // LDS accesses of one wave complete in program order; the barrier keeps the
     // compiler from moving them across each other.
     __builtin_amdgcn_wave_barrier();
-    const uint64_t mine = lane < n ? scratch[lane] : 0ull;
-    // Candidate u is read from lane u, four at a time: the reads past n (at
-    // most lane 63, as n <= 64) find 0 and count for nothing.
+    const uint64_t mine = scratch[lane];
+    // Slots u0 .. u0 + 15 < 64 (n <= 64), the same address in every lane.
     int rank = 0;
-    for (int u = 0; u < n; u += 4) {
+    for (int u0 = 0; u0 < n; u0 += 16) {
+        const ulonglong2* q = (const ulonglong2*)(scratch + u0);
+        ulonglong2 c[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rank += readlane_u64(mine, u + j) > mine;
+        for (int j = 0; j < 8; ++j) c[j] = q[j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rank += (int)(c[j].x > mine) + (int)(c[j].y > mine);
     }
     __builtin_amdgcn_wave_barrier();
     scratch[lane < n && rank < k ? rank : 64 + lane] = mine;

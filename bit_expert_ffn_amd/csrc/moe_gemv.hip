@@ -98,7 +98,7 @@ struct RouteLDS {
     int pair_tok[kMaxK], pair_exp[kMaxK], slot_pair[kMaxK];
     int group_first[kMaxK], group_n[kMaxK], group_of_pair[kMaxK];
     int slot_src[kMaxK];   // slot j -> group * NT + token-in-group of its pair; -1: a skipped slot
-    uint64_t topk[kGemvThreads / 64][128];   // each wave's top-k scratch
+    alignas(16) uint64_t topk[kGemvThreads / 64][128];   // each wave's top-k scratch
     int n_groups;
     int fail;              // this workgroup's output is NaN: an earlier failure, or one of its waits gave up
     int bad;               // a caller-supplied id outside [0, E) with a nonzero weight

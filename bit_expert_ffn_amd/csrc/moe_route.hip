@@ -16,7 +16,7 @@ namespace moe {
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                          int renorm, int* __restrict__ ids,
                                                          float* __restrict__ w) {
-    __shared__ uint64_t scratch[4][128];
+    __shared__ __align__(16) uint64_t scratch[4][128];
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
