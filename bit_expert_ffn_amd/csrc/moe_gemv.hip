@@ -717,6 +717,7 @@ __global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodePar
     // Only the down workgroups (the combine) and workgroup 0 (w_out) read the
     // weights: the gate/up workgroups skip the softmax, which is on the path to
     // their weight loads.
+    const int dn_tile = wg >= p.n_gu && wg - p.n_gu < p.tiles_dn ? wg - p.n_gu : -1;
     route_and_bucket(p, R, wg >= p.n_gu || (wg == 0 && p.w_out));
     if (wg == 0) {
         for (int q = tid; q < p.T * p.k; q += kGemvThreads) {
@@ -727,16 +728,16 @@ __global__ void __launch_bounds__(kGemvThreads, 3) decode_layer_kernel(DecodePar
     if (R.bad) {
         // Invalid caller-supplied routing: nothing is computed; the down
         // workgroups write NaN rows.
-        if (wg >= p.n_gu && wg - p.n_gu < p.tiles_dn) {
-            const int h0 = (wg - p.n_gu) * p.dn_rows, nrows = min(p.dn_rows, p.H - h0);
+        if (dn_tile >= 0) {
+            const int h0 = dn_tile * p.dn_rows, nrows = min(p.dn_rows, p.H - h0);
             for (int i = tid; i < p.T * nrows; i += kGemvThreads)
                 p.y[(size_t)(i / nrows) * p.H + h0 + i % nrows] = __uint_as_float(0x7FC00000u);
         }
         return;
     }
     if (wg < p.n_gu) gateup_role<QT, NT, NTERM, PAIR>(p, R, wg, lds);
-    else if (wg - p.n_gu < p.tiles_dn) down_role<QT, NT>(p, R, wg - p.n_gu, lds);
-    else janitor_role<NT>(p, R);
+    if (dn_tile >= 0) down_role<QT, NT>(p, R, dn_tile, lds);
+    else if (wg >= p.n_gu) janitor_role<NT>(p, R);
 }
 
 // ---------------------------------------------------------------------------------------------
