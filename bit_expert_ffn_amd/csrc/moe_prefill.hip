@@ -947,6 +947,8 @@ __global__ void __launch_bounds__(kDnThreads, 1) prefill_down_kernel(PrefillPara
 
 // y[t][h] = shared(t)[h] + sum_j w[t][j] * Y[pair(t, j)][h], in this order.
 // While the workspace's error word is set, every output is NaN.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __global__ void __launch_bounds__(256) prefill_combine_kernel(PrefillParams p) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t n4 = (size_t)p.T * p.H / 4;
@@ -977,7 +979,12 @@ __global__ void __launch_bounds__(256) prefill_combine_kernel(PrefillParams p) {
         float4 v[G];
 #pragma unroll
         for (int u = 0; u < G; ++u)
-            v[u] = on[u] ? *reinterpret_cast<const float4*>(p.ypair + (size_t)row[u] * p.H + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+            if (on[u]) {   // rows read once: non-temporal
+                const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.ypair + (size_t)row[u] * p.H + h));
+                v[u] = make_float4(q[0], q[1], q[2], q[3]);
+            } else {
+                v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
 #pragma unroll
         for (int u = 0; u < G; ++u) {
             if (!on[u]) continue;
@@ -987,7 +994,8 @@ __global__ void __launch_bounds__(256) prefill_combine_kernel(PrefillParams p) {
             acc.w = __builtin_fmaf(wt[u], v[u].w, acc.w);
         }
     }
-    *reinterpret_cast<float4*>(p.y + (size_t)t * p.H + h) = acc;
+    const f32x4 o = {acc.x, acc.y, acc.z, acc.w};
+    __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(p.y + (size_t)t * p.H + h));
 }
 
 // ---------------------------------------------------------------------------------------------
