@@ -236,8 +236,13 @@ __device__ void gateup_role(const DecodeParams& p, RouteLDS& R, int item, float*
             const size_t blk = (size_t)f * nblk + b;
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
-                cg[m][j] = ldg_u4(gcode + (blk + j) * 16);
-                cu[m][j] = ldg_u4(ucode + (blk + j) * 16);
+                if (out == p.as) {   // the shared expert: read every call
+                    cg[m][j] = ldg_u4(gcode + (blk + j) * 16);
+                    cu[m][j] = ldg_u4(ucode + (blk + j) * 16);
+                } else {
+                    cg[m][j] = ldg_u4_nt(gcode + (blk + j) * 16);
+                    cu[m][j] = ldg_u4_nt(ucode + (blk + j) * 16);
+                }
                 sg_[m][j] = ldg_u16(gscale + (blk + j) * 2);
                 su_[m][j] = ldg_u16(uscale + (blk + j) * 2);
             }
@@ -508,7 +513,7 @@ __device__ void down_role(const DecodeParams& p, RouteLDS& R, int tile, float* l
         for (int i = 0; i < RPT; ++i) {
             const int r = min(rs + i * S, nrows - 1);
             const size_t blk = (size_t)(h0 + r) * nb + b;
-            c[i] = ldg_u4(dcode + blk * 16);
+            c[i] = u >= ng * nb_r ? ldg_u4(dcode + blk * 16) : ldg_u4_nt(dcode + blk * 16);
             sc[i] = ldg_u16(dscale + blk * 2);
         }
         if (!waited) {

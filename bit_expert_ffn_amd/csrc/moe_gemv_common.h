@@ -72,6 +72,15 @@ __device__ __forceinline__ uint4 ldg_u4(const void* p) {
 __device__ __forceinline__ uint16_t ldg_u16(const void* p) {
     return *(const __attribute__((address_space(1))) uint16_t*)p;
 }
+// Weight codes of a routed expert: non-temporal.  Each is read once a call,
+// and a layer's next call selects other experts; the shared expert's codes,
+// read by every call, keep the ordinary loads (they can stay in the memory-
+// side cache from one call of the layer to the next).
+__device__ __forceinline__ uint4 ldg_u4_nt(const void* p) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_nontemporal_load((const __attribute__((address_space(1))) v4u*)p);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 
 
