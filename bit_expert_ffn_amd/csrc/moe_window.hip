@@ -330,8 +330,13 @@ __device__ __forceinline__ void gu_load(const GuItem& it, int nblk, int P, int g
     for (int m = 0; m < kWinMaxPass; ++m) {
         const int f = min(it.f0 + min(m, gp - 1) * P + rp, it.rows - 1);
         const size_t blk = it.none ? 0 : (size_t)f * nblk + b;
-        c.cg[m] = ldg_u4(gcode + blk * 16);
-        c.cu[m] = ldg_u4(ucode + blk * 16);
+        if (it.sh) {   // the shared expert: read by every call
+            c.cg[m] = ldg_u4(gcode + blk * 16);
+            c.cu[m] = ldg_u4(ucode + blk * 16);
+        } else {
+            c.cg[m] = ldg_u4_nt(gcode + blk * 16);
+            c.cu[m] = ldg_u4_nt(ucode + blk * 16);
+        }
         c.sg[m] = ldg_u16(gscale + blk * 2);
         c.su[m] = ldg_u16(uscale + blk * 2);
     }
@@ -700,7 +705,7 @@ __device__ __forceinline__ void dn_load(const WindowParams& p, const DnItem& it,
     for (int m = 0; m < kWinMaxPass; ++m) {
         const int r = min(l.rp + m * l.P, rlast);
         const size_t blk = it.none ? 0 : (size_t)(min(it.h0 + r, p.H - 1)) * l.nb + l.b;
-        c.c[m] = ldg_u4(it.dcode + blk * 16);
+        c.c[m] = it.sh ? ldg_u4(it.dcode + blk * 16) : ldg_u4_nt(it.dcode + blk * 16);
         c.sc[m] = ldg_u16(it.dscale + blk * 2);
     }
 }
